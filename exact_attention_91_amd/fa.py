@@ -1,0 +1,141 @@
+"""Thin ctypes binding over libfa.so (the C ABI declared in include/fa.h).
+
+Argument marshalling only: shape/dtype/device checks, output allocation with
+torch, and the call into `fa_fwd` / `fa_fwd_strided` on torch's current
+stream. Every step of the attention forward runs in the library's HIP kernels;
+there is no fallback. If libfa.so is missing, every call raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfa.so")
+_LIB = None
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+_I = ctypes.c_int
+_VP = ctypes.c_void_p
+_LL3 = ctypes.c_longlong * 3
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"libfa.so not found at {_LIB_PATH}: build it first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.fa_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP] + [_I] * 7 + [ctypes.c_float, _I, _VP]
+        lib.fa_fwd.restype = _I
+        lib.fa_fwd_strided.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 7 +
+                                       [ctypes.c_float, _I] + [_LL3] * 4 + [_VP])
+        lib.fa_fwd_strided.restype = _I
+        lib.fa_status_str.argtypes = [_I]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = _I
+        _LIB = lib
+    return _LIB
+
+
+def version() -> int:
+    return int(_lib().fa_version())
+
+
+def status_str(code: int) -> str:
+    return _lib().fa_status_str(int(code)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _check(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D, got {tuple(t.shape)}")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def _raise(rc: int, fn: str):
+    if rc != 0:
+        raise RuntimeError(f"{fn} failed: {status_str(rc)} (code {rc})")
+
+
+def fwd(q, k, v, causal: bool = False, scale=None):
+    """Attention forward on BNHD-contiguous tensors.
+
+    q: [B, T, H, D], k and v: [B, T, H_kv, D] (bf16 or fp32, contiguous).
+    Returns (o [B, T, H, D] in q's dtype, lse [B, H, T] float32), where lse is
+    the natural-log logsumexp of each row's scaled, masked scores.
+    """
+    _check(q, k, v)
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fwd needs contiguous [B,T,H,D] tensors; use fwd_strided for views")
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr(), B, H, H_kv, T, D, int(bool(causal)),
+                       float(scale), _dtype_code(q), stream)
+    _raise(rc, "fa_fwd")
+    return o, lse
+
+
+def fwd_strided(q, k, v, causal: bool = False, scale=None, out_layout: str = "bthd"):
+    """Attention forward on views with arbitrary (batch, token, head) strides.
+
+    Tensors are indexed logically as q[b, t, h, :] (pass e.g. x.transpose(1, 2)
+    of a [B, H, T, D] tensor); the last dim must have stride 1. `out_layout`
+    picks the memory order of o: "bthd" ([B,T,H,D]) or "bhtd" ([B,H,T,D]);
+    o is returned as a [B, T, H, D]-indexed view either way.
+    """
+    _check(q, k, v)
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out_layout == "bthd":
+        o = torch.empty((B, T, H, D), dtype=q.dtype, device=q.device)
+    elif out_layout == "bhtd":
+        o = torch.empty((B, H, T, D), dtype=q.dtype, device=q.device).transpose(1, 2)
+    else:
+        raise ValueError("out_layout must be 'bthd' or 'bhtd'")
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name} must have unit stride in its last dim")
+
+    def st(t):
+        return _LL3(t.stride(0), t.stride(1), t.stride(2))
+
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib().fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), B, H, H_kv, T, D, int(bool(causal)),
+                               float(scale), _dtype_code(q), st(q), st(k), st(v), st(o),
+                               stream)
+    _raise(rc, "fa_fwd_strided")
+    return o, lse

@@ -1,0 +1,162 @@
+"""float64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may use this module; the GPU product path never does and shares
+no code with it.
+
+Layout everywhere: q, o are [B, T, H, D]; k, v are [B, T, H_kv, D]; lse is
+[B, H, T]. Query head h reads kv head h // (H // H_kv).
+
+Functions
+---------
+attention(q, k, v, causal, scale)        two-pass softmax over the whole row
+                                         (C, OpenMP), the plain definition.
+attention_rows(..., rows)                the same for selected flat rows
+                                         (b*H + h)*T + i.
+attention_online(..., chunk)             the online-softmax recurrence over key
+                                         chunks (C), used to show it reaches the
+                                         two-pass result.
+brute_force(q, k, v, causal, scale)      pure Python, hand-expanded exponentials
+                                         summed with math.fsum, no max
+                                         subtraction; for T <= 8 only.
+
+Sources: the yelogs.com Flash Attention2-in-Triton article, sections
+"問題的根源：傳統注意力機制的痛點" (naive module), "核心思想：分塊計算與在線更新"
+(traditional and online softmax), "因果掩碼的高效實現" (causal predicate: query
+position >= key position), "Softmax 的在線計算" (recurrence), "核心 Kernel 實現"
+(stored statistic m + ln l), "多查詢注意力（MQA）" (shared kv head); and
+"Flash Attention Memory Optimization Explained", "What is Flash Attention?"
+(the four naive steps).
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build_oracle
+
+_LIB = None
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(build_oracle.LIB):
+            build_oracle.build()
+        lib = ctypes.CDLL(build_oracle.LIB)
+        common = [_DP, _DP, _DP]
+        shape = [ctypes.c_int] * 5 + [ctypes.c_int, ctypes.c_double]
+        lib.oracle_attn_f64.argtypes = common + [_DP, _DP] + shape
+        lib.oracle_attn_f64.restype = ctypes.c_int
+        lib.oracle_attn_rows_f64.argtypes = (
+            common + [ctypes.POINTER(ctypes.c_int64), ctypes.c_longlong, _DP, _DP] + shape)
+        lib.oracle_attn_rows_f64.restype = ctypes.c_int
+        lib.oracle_attn_online_f64.argtypes = common + [_DP, _DP] + shape + [ctypes.c_int]
+        lib.oracle_attn_online_f64.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_DP)
+
+
+def _shape(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, T, heads, D]")
+    B, T, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise ValueError(f"k/v shape {k.shape} does not match q {q.shape}")
+    H_kv = k.shape[2]
+    if H % H_kv:
+        raise ValueError("H must be a multiple of H_kv")
+    return B, H, H_kv, T, D
+
+
+def num_threads() -> int:
+    return int(_lib().oracle_num_threads())
+
+
+def attention(q, k, v, causal: bool, scale: float):
+    """Two-pass float64 attention. Returns (o [B,T,H,D], lse [B,H,T])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    o = np.empty((B, T, H, D), np.float64)
+    lse = np.empty((B, H, T), np.float64)
+    rc = _lib().oracle_attn_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                B, H, H_kv, T, D, int(bool(causal)), float(scale))
+    if rc:
+        raise RuntimeError(f"oracle_attn_f64 failed ({rc})")
+    return o, lse
+
+
+def attention_rows(q, k, v, causal: bool, scale: float, rows):
+    """Rows given as flat ids (b*H + h)*T + i. Returns (o [n, D], lse [n])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.shape[0]
+    o = np.empty((n, D), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = _lib().oracle_attn_rows_f64(
+        _ptr(q), _ptr(k), _ptr(v), rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        n, _ptr(o), _ptr(lse), B, H, H_kv, T, D, int(bool(causal)), float(scale))
+    if rc:
+        raise RuntimeError(f"oracle_attn_rows_f64 failed ({rc})")
+    return o, lse
+
+
+def attention_online(q, k, v, causal: bool, scale: float, chunk: int):
+    """Online-softmax recurrence over key chunks. Returns (o, lse)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    o = np.empty((B, T, H, D), np.float64)
+    lse = np.empty((B, H, T), np.float64)
+    rc = _lib().oracle_attn_online_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       B, H, H_kv, T, D, int(bool(causal)), float(scale),
+                                       int(chunk))
+    if rc:
+        raise RuntimeError(f"oracle_attn_online_f64 failed ({rc})")
+    return o, lse
+
+
+def brute_force(q, k, v, causal: bool, scale: float):
+    """Pure-Python attention for tiny inputs (T <= 8).
+
+    Every weight is written out as exp(score) / fsum(exp(scores)), with no max
+    subtraction, and L = ln(fsum(exp(scores))). Scores must stay moderate
+    (|score| < 700) for this to be valid.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    if T > 8:
+        raise ValueError("brute_force is for T <= 8")
+    o = np.zeros((B, T, H, D), np.float64)
+    lse = np.zeros((B, H, T), np.float64)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // H_kv)
+            for i in range(T):
+                keys = [j for j in range(T) if (not causal) or j <= i]
+                e = []
+                for j in range(T):
+                    if j not in keys:
+                        continue
+                    sc = scale * math.fsum(float(q[b, i, h, d]) * float(k[b, j, g, d])
+                                           for d in range(D))
+                    e.append((j, math.exp(sc)))
+                z = math.fsum(w for _, w in e)
+                for d in range(D):
+                    o[b, i, h, d] = math.fsum(w * float(v[b, j, g, d]) for j, w in e) / z
+                lse[b, h, i] = math.log(z)
+    return o, lse

@@ -1,0 +1,233 @@
+/*
+ * oracle_attn.c -- float64 CPU oracle for exact scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. The GPU product path
+ * never calls it and shares no code with it.
+ *
+ * What it computes (plain definition, no tiling, no fusion):
+ *   For every batch b, query head h, query row i, with kv head
+ *   g = h / (H / H_kv) and visible key set V_i = { j < T : !causal or j <= i },
+ *     s_ij = scale * sum_d q[b,i,h,d] * k[b,j,g,d]
+ *     m_i  = max_{j in V_i} s_ij
+ *     Z_i  = sum_{j in V_i} exp(s_ij - m_i)
+ *     O[b,i,h,:] = sum_{j in V_i} (exp(s_ij - m_i) / Z_i) * v[b,j,g,:]
+ *     L[b,h,i]   = m_i + ln Z_i
+ *
+ * Sources (pages, by title and section):
+ *  - yelogs.com Flash Attention2-in-Triton article, section
+ *    "問題的根源：傳統注意力機制的痛點" (the ScaledDotProductAttention module:
+ *    dot product, division by sqrt(d), masked_fill of masked positions, softmax,
+ *    weighted sum of V). Masked keys are excluded from the row, which gives the
+ *    same values as the module's -1e9 fill.
+ *  - same article, "核心思想：分塊計算與在線更新" (traditional_softmax:
+ *    subtract the row max, exponentiate, normalise) -- the two-pass form here.
+ *  - same article, "因果掩碼的高效實現" (query position >= key position is
+ *    visible, diagonal included).
+ *  - same article, "核心 Kernel 實現" epilogue (the stored per-row statistic is
+ *    the running max plus the natural log of the normaliser; eps taken as 0).
+ *  - same article, "多查詢注意力（MQA）" (one kv head shared by all query heads);
+ *    groups for 1 < H_kv < H are contiguous runs of H/H_kv query heads.
+ *  - "Flash Attention Memory Optimization Explained" (lzwjava.github.io),
+ *    "What is Flash Attention?": the four naive steps Q@K^T, scale and mask,
+ *    softmax, weighted sum with V.
+ *
+ * Memory layout (row-major):
+ *   q, o : [B, T, H,    D]     k, v : [B, T, H_kv, D]     lse : [B, H, T]
+ *
+ * oracle_attn_online_f64 follows the online-softmax recurrence of the same
+ * article ("Softmax 的在線計算": running max m, normaliser l rescaled by
+ * exp(m_old - m_new)), over key chunks of a caller-chosen size. It exists so a
+ * test can show the recurrence reaches the two-pass result.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math, no BLAS).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static size_t qidx(int b, int t, int h, int H, int T, int D) {
+    return (((size_t)b * T + t) * H + h) * (size_t)D;
+}
+
+/* One query row, two-pass softmax. s is caller scratch of length T. */
+static void attn_row(const double *q, const double *k, const double *v,
+                     double *o_row, double *lse_out,
+                     int H, int H_kv, int T, int D, int causal, double scale,
+                     int b, int h, int i, double *s) {
+    const int group = H / H_kv;
+    const int g = h / group;
+    const int nvis = causal ? i + 1 : T;
+    const double *qi = q + qidx(b, i, h, H, T, D);
+
+    /* pass 1: scores and their max */
+    double m = -INFINITY;
+    for (int j = 0; j < nvis; ++j) {
+        const double *kj = k + qidx(b, j, g, H_kv, T, D);
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    /* pass 2: exponentials and normaliser */
+    double z = 0.0;
+    for (int j = 0; j < nvis; ++j) {
+        s[j] = exp(s[j] - m);
+        z += s[j];
+    }
+    /* weighted sum of V with the normalised weights */
+    for (int d = 0; d < D; ++d) o_row[d] = 0.0;
+    for (int j = 0; j < nvis; ++j) {
+        const double w = s[j] / z;
+        const double *vj = v + qidx(b, j, g, H_kv, T, D);
+        for (int d = 0; d < D; ++d) o_row[d] += w * vj[d];
+    }
+    *lse_out = m + log(z);
+}
+
+static int bad_args(int B, int H, int H_kv, int T, int D) {
+    return B < 1 || H < 1 || H_kv < 1 || T < 1 || D < 1 || (H % H_kv) != 0;
+}
+
+/* Full attention. Returns 0 on success, -1 on bad shape, -2 on no memory. */
+int oracle_attn_f64(const double *q, const double *k, const double *v,
+                    double *o, double *lse,
+                    int B, int H, int H_kv, int T, int D, int causal, double scale) {
+    if (bad_args(B, H, H_kv, T, D)) return -1;
+    const long long nrows = (long long)B * H * T;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)T);
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long long r = 0; r < nrows; ++r) {
+                /* r enumerates (b, h, i) with i fastest */
+                const int i = (int)(r % T);
+                const int h = (int)((r / T) % H);
+                const int b = (int)(r / ((long long)T * H));
+                attn_row(q, k, v, o + qidx(b, i, h, H, T, D),
+                         lse + ((size_t)b * H + h) * T + i,
+                         H, H_kv, T, D, causal, scale, b, h, i, s);
+            }
+            free(s);
+        }
+    }
+    return fail ? -2 : 0;
+}
+
+/* Selected rows only. rows[r] = (b*H + h)*T + i. o_rows is [nrows, D],
+ * lse_rows is [nrows]. Returns -3 if a row index is out of range. */
+int oracle_attn_rows_f64(const double *q, const double *k, const double *v,
+                         const int64_t *rows, long long nrows,
+                         double *o_rows, double *lse_rows,
+                         int B, int H, int H_kv, int T, int D, int causal,
+                         double scale) {
+    if (bad_args(B, H, H_kv, T, D)) return -1;
+    const long long total = (long long)B * H * T;
+    for (long long r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= total) return -3;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)T);
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (long long r = 0; r < nrows; ++r) {
+                const long long id = rows[r];
+                const int i = (int)(id % T);
+                const int h = (int)((id / T) % H);
+                const int b = (int)(id / ((long long)T * H));
+                attn_row(q, k, v, o_rows + (size_t)r * D, lse_rows + r,
+                         H, H_kv, T, D, causal, scale, b, h, i, s);
+            }
+            free(s);
+        }
+    }
+    return fail ? -2 : 0;
+}
+
+/* Online-softmax recurrence over key chunks of `chunk` keys, per row:
+ *   m_new = max(m, max_j s_j) ; a = exp(m - m_new) ; p_j = exp(s_j - m_new)
+ *   l = a*l + sum_j p_j ; acc = a*acc + sum_j p_j v_j ; m = m_new
+ * then O = acc / l and L = m + ln l. Initial state m = -inf, l = 0, acc = 0. */
+int oracle_attn_online_f64(const double *q, const double *k, const double *v,
+                           double *o, double *lse,
+                           int B, int H, int H_kv, int T, int D, int causal,
+                           double scale, int chunk) {
+    if (bad_args(B, H, H_kv, T, D) || chunk < 1) return -1;
+    const int group = H / H_kv;
+    const long long nrows = (long long)B * H * T;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        double *p = (double *)malloc(sizeof(double) * (size_t)chunk);
+        if (!acc || !p) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long long r = 0; r < nrows; ++r) {
+                const int i = (int)(r % T);
+                const int h = (int)((r / T) % H);
+                const int b = (int)(r / ((long long)T * H));
+                const int g = h / group;
+                const int nvis = causal ? i + 1 : T;
+                const double *qi = q + qidx(b, i, h, H, T, D);
+                double m = -INFINITY, l = 0.0;
+                for (int d = 0; d < D; ++d) acc[d] = 0.0;
+                for (int j0 = 0; j0 < nvis; j0 += chunk) {
+                    const int n = (nvis - j0 < chunk) ? nvis - j0 : chunk;
+                    double cmax = -INFINITY;
+                    for (int t = 0; t < n; ++t) {
+                        const double *kj = k + qidx(b, j0 + t, g, H_kv, T, D);
+                        double dot = 0.0;
+                        for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+                        p[t] = scale * dot;
+                        if (p[t] > cmax) cmax = p[t];
+                    }
+                    const double m_new = (cmax > m) ? cmax : m;
+                    /* exp(-inf - finite) = 0: the empty initial state drops out */
+                    const double a = exp(m - m_new);
+                    double psum = 0.0;
+                    for (int t = 0; t < n; ++t) {
+                        p[t] = exp(p[t] - m_new);
+                        psum += p[t];
+                    }
+                    l = a * l + psum;
+                    for (int d = 0; d < D; ++d) acc[d] *= a;
+                    for (int t = 0; t < n; ++t) {
+                        const double *vj = v + qidx(b, j0 + t, g, H_kv, T, D);
+                        for (int d = 0; d < D; ++d) acc[d] += p[t] * vj[d];
+                    }
+                    m = m_new;
+                }
+                double *orow = o + qidx(b, i, h, H, T, D);
+                for (int d = 0; d < D; ++d) orow[d] = acc[d] / l;
+                lse[((size_t)b * H + h) * T + i] = m + log(l);
+            }
+        }
+        free(acc);
+        free(p);
+    }
+    return fail ? -2 : 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

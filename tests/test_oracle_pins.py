@@ -1,0 +1,249 @@
+"""Pins for the float64 oracle: truths fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: hand-worked
+values, closed forms, invariances of softmax attention, the online-softmax
+recurrence, or a pure-Python brute force. Together they fail on a dropped term,
+a wrong sign or index, a transposed operand, a wrong mask polarity, a wrong
+log base, a missing max subtraction or a wrong kv-head mapping.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from exact_attention_91_amd.inputs import generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _rand(B, H, H_kv, T, D, seed, sigma=1.0):
+    x = generate(B, H, H_kv, T, D, dtype="f32", seed=seed, qk_sigma=sigma)
+    return x.q64, x.k64, x.v64
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_hand_worked_golden(oracle, case):
+    """Hand-derived values (tests/golden/hand_worked.json)."""
+    B, H, H_kv, T, D = case["B"], case["H"], case["H_kv"], case["T"], case["D"]
+    q = np.array(case["q"], np.float64).reshape(B, T, H, D)
+    k = np.array(case["k"], np.float64).reshape(B, T, H_kv, D)
+    v = np.array(case["v"], np.float64).reshape(B, T, H_kv, D)
+    o, lse = oracle.attention(q, k, v, case["causal"], case["scale"])
+    np.testing.assert_allclose(o.ravel(), case["o"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse.ravel(), case["lse"], rtol=1e-15, atol=1e-12)
+    # the chunked recurrence and the pure-Python path reach the same values
+    o2, l2 = oracle.attention_online(q, k, v, case["causal"], case["scale"], 1)
+    np.testing.assert_allclose(o2.ravel(), case["o"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2.ravel(), case["lse"], rtol=1e-15, atol=1e-12)
+    if max(abs(x) for x in case["q"]) < 100:
+        o3, l3 = oracle.brute_force(q, k, v, case["causal"], case["scale"])
+        np.testing.assert_allclose(o3.ravel(), case["o"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l3.ravel(), case["lse"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_p1_rows_of_P_sum_to_one(oracle, causal):
+    """With V = identity (D = T, v_j = e_j) the output row IS the weight row
+    P_i: weights are non-negative, sum to 1, vanish on masked keys, and obey
+    P_ij = exp(s_ij - L_i) with s_ij = scale * q_i.k_j."""
+    B, H, T = 2, 3, 24
+    D = T
+    q, k, _ = _rand(B, H, H, T, D, seed=11)
+    v = np.zeros((B, T, H, D))
+    for j in range(T):
+        v[:, j, :, j] = 1.0
+    scale = 0.3
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    P = o.transpose(0, 2, 1, 3)                      # [B, H, T(query), T(key)]
+    assert np.all(P >= 0.0)
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-13 * T)
+    if causal:
+        assert np.all(np.triu(np.ones((T, T)), 1)[None, None] * P == 0.0)
+    s = scale * np.einsum("bihd,bjhd->bhij", q, k)
+    vis = np.tril(np.ones((T, T), bool)) if causal else np.ones((T, T), bool)
+    expect = np.where(vis[None, None], np.exp(s - lse[..., None]), 0.0)
+    np.testing.assert_allclose(P, expect, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("zero", ["q", "scale"])
+def test_p2_zero_scores_give_mean_of_v(oracle, causal, zero):
+    """Q = 0 (or scale = 0): every visible weight equal, so O_i is the mean of V
+    (non-causal) or the prefix mean (causal); L_i = ln T or ln(i+1)."""
+    B, H, H_kv, T, D = 2, 4, 2, 37, 16
+    q, k, v = _rand(B, H, H_kv, T, D, seed=12)
+    scale = 0.25
+    if zero == "q":
+        q = np.zeros_like(q)
+    else:
+        scale = 0.0
+    o, lse = oracle.attention(q, k, v, causal, scale)
+    vg = np.repeat(v, H // H_kv, axis=2)             # [B, T, H, D]
+    if causal:
+        counts = np.arange(1, T + 1, dtype=np.float64)
+        mean = np.cumsum(vg, axis=1) / counts[None, :, None, None]
+        expect_l = np.log(counts)[None, None, :].repeat(B, 0).repeat(H, 1)
+    else:
+        mean = np.broadcast_to(vg.mean(axis=1, keepdims=True), vg.shape)
+        expect_l = np.full((B, H, T), math.log(T))
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, expect_l, rtol=0, atol=1e-12)
+
+
+def test_p3_single_key(oracle):
+    """T = 1 (and causal row 0 for any T): O_0 = v_0, L_0 = scale * q_0.k_0."""
+    B, H, H_kv, D = 3, 2, 1, 32
+    q, k, v = _rand(B, H, H_kv, 1, D, seed=13)
+    o, lse = oracle.attention(q, k, v, False, 0.2)
+    np.testing.assert_allclose(o, np.repeat(v, H, axis=2), rtol=0, atol=1e-12)
+    expect = 0.2 * np.array([[sum(q[b, 0, h, d] * k[b, 0, 0, d] for d in range(D))
+                              for h in range(H)] for b in range(B)])
+    np.testing.assert_allclose(lse[:, :, 0], expect, rtol=0, atol=1e-12)
+    q, k, v = _rand(B, H, H_kv, 9, D, seed=14)
+    o, lse = oracle.attention(q, k, v, True, 0.2)
+    np.testing.assert_allclose(o[:, 0], np.repeat(v[:, 0], H, axis=1), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("magnitude", [1.0, 300.0])
+def test_p4_key_shift_adds_row_constant(oracle, causal, magnitude):
+    """k_j -> k_j + u for all j adds c_i = scale*q_i.u to every score of row i:
+    softmax is unchanged (O equal), L_i moves by exactly c_i. At magnitude 300
+    the scores reach ~1e3, where exp overflows without max subtraction."""
+    B, H, H_kv, T, D = 2, 2, 2, 40, 8
+    q, k, v = _rand(B, H, H_kv, T, D, seed=15)
+    scale = 0.5
+    rng = np.random.default_rng(7)
+    u = magnitude * rng.standard_normal((B, 1, H_kv, D))
+    o0, l0 = oracle.attention(q, k, v, causal, scale)
+    o1, l1 = oracle.attention(q, k + u, v, causal, scale)
+    shift = scale * np.einsum("bthd,bhd->bht", q, u[:, 0])
+    tol = 1e-10 * max(1.0, magnitude)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=tol)
+    np.testing.assert_allclose(l1, l0 + shift, rtol=0, atol=tol * 10)
+    assert np.all(np.isfinite(o1)) and np.all(np.isfinite(l1))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("chunk", [1, 2, 3, 7, 64, 70])
+def test_p5_online_recurrence_equals_two_pass(oracle, causal, chunk):
+    """The chunked online-softmax update (running max, normaliser rescaled by
+    exp(m_old - m_new)) reaches the two-pass result -- the yelogs article,
+    'Softmax 的在線計算', says the final result equals the batch computation."""
+    B, H, H_kv, T, D = 2, 3, 1, 70, 16
+    q, k, v = _rand(B, H, H_kv, T, D, seed=16, sigma=3.0)
+    o0, l0 = oracle.attention(q, k, v, causal, 0.25)
+    o1, l1 = oracle.attention_online(q, k, v, causal, 0.25, chunk)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 7, 8])
+@pytest.mark.parametrize("causal", [False, True])
+def test_p6_brute_force_small(oracle, T, causal):
+    """Pure-Python hand-expanded exponentials (no max subtraction, math.fsum)."""
+    B, H, H_kv, D = 2, 4, 2, 5
+    q, k, v = _rand(B, H, H_kv, T, D, seed=100 + T)
+    o0, l0 = oracle.attention(q, k, v, causal, 0.37)
+    o1, l1 = oracle.brute_force(q, k, v, causal, 0.37)
+    np.testing.assert_allclose(o0, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l0, l1, rtol=0, atol=1e-12)
+
+
+def test_p7_noncausal_key_permutation(oracle):
+    """Non-causal attention is a function of the set of (key, value) pairs:
+    permuting keys together with values changes nothing."""
+    B, H, H_kv, T, D = 2, 2, 1, 50, 8
+    q, k, v = _rand(B, H, H_kv, T, D, seed=17)
+    perm = np.random.default_rng(3).permutation(T)
+    o0, l0 = oracle.attention(q, k, v, False, 0.3)
+    o1, l1 = oracle.attention(q, k[:, perm], v[:, perm], False, 0.3)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l0, rtol=0, atol=1e-12)
+    # permuting keys alone (not values) must change the result
+    o2, _ = oracle.attention(q, k[:, perm], v, False, 0.3)
+    assert np.max(np.abs(o2 - o0)) > 1e-3
+
+
+def test_p8_causal_row_is_prefix_attention(oracle):
+    """Causal row i equals non-causal attention over the prefix K[:i+1], V[:i+1]."""
+    B, H, H_kv, T, D = 1, 2, 2, 33, 8
+    q, k, v = _rand(B, H, H_kv, T, D, seed=18)
+    oc, lc = oracle.attention(q, k, v, True, 0.4)
+    for i in (0, 1, 5, 16, 31, 32):
+        on, ln_ = oracle.attention(q[:, :i + 1], k[:, :i + 1], v[:, :i + 1], False, 0.4)
+        np.testing.assert_allclose(oc[:, i], on[:, i], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lc[:, :, i], ln_[:, :, i], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("H_kv", [1, 2, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_p9_shared_kv_heads_equal_expanded(oracle, H_kv, causal):
+    """Query head h reads kv head h // (H/H_kv); equal to giving every query
+    head its own copy (the yelogs article's MQA 'expand', generalised to
+    contiguous groups). Same arithmetic, so bitwise equal."""
+    B, H, T, D = 2, 6, 29, 16
+    q, k, v = _rand(B, H, H_kv, T, D, seed=19)
+    o0, l0 = oracle.attention(q, k, v, causal, 0.25)
+    ke = np.repeat(k, H // H_kv, axis=2)
+    ve = np.repeat(v, H // H_kv, axis=2)
+    o1, l1 = oracle.attention(q, ke, ve, causal, 0.25)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_p10_linear_in_v(oracle):
+    """O is linear in V for fixed Q, K; L does not depend on V."""
+    B, H, H_kv, T, D = 2, 2, 1, 45, 8
+    q, k, v = _rand(B, H, H_kv, T, D, seed=20)
+    _, _, v2 = _rand(B, H, H_kv, T, D, seed=21)
+    a, b = 0.7, -1.9
+    o1, l1 = oracle.attention(q, k, v, True, 0.3)
+    o2, l2 = oracle.attention(q, k, v2, True, 0.3)
+    o3, l3 = oracle.attention(q, k, a * v + b * v2, True, 0.3)
+    np.testing.assert_allclose(o3, a * o1 + b * o2, rtol=0, atol=1e-10)
+    assert np.array_equal(l1, l2) and np.array_equal(l1, l3)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_p11_identical_keys(oracle, causal):
+    """All keys equal: uniform weights over the visible keys,
+    O_i = mean of visible V, L_i = scale*q_i.k + ln |visible|."""
+    B, H, H_kv, T, D = 1, 3, 1, 21, 8
+    q, k, v = _rand(B, H, H_kv, T, D, seed=22)
+    k = np.broadcast_to(k[:, :1], k.shape).copy()
+    o, lse = oracle.attention(q, k, v, causal, 0.5)
+    counts = np.arange(1, T + 1) if causal else np.full(T, T)
+    vg = np.repeat(v, H, axis=2)
+    mean = (np.cumsum(vg, axis=1) / np.arange(1, T + 1)[None, :, None, None]
+            if causal else np.broadcast_to(vg.mean(1, keepdims=True), vg.shape))
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-12)
+    s = 0.5 * np.einsum("bthd,bd->bht", q, k[:, 0, 0])
+    np.testing.assert_allclose(lse, s + np.log(counts)[None, None], rtol=0, atol=1e-12)
+
+
+def test_rows_entry_matches_full(oracle):
+    """The selected-rows entry computes the same rows as the full entry."""
+    B, H, H_kv, T, D = 2, 3, 1, 50, 16
+    q, k, v = _rand(B, H, H_kv, T, D, seed=23)
+    o, lse = oracle.attention(q, k, v, True, 0.25)
+    rows = np.array([0, 1, 49, 50, 77, 149, 150, 299], np.int64)
+    orows, lrows = oracle.attention_rows(q, k, v, True, 0.25, rows)
+    b, rem = rows // (H * T), rows % (H * T)
+    h, i = rem // T, rem % T
+    assert np.array_equal(orows, o[b, i, h])
+    assert np.array_equal(lrows, lse[b, h, i])
+    with pytest.raises(RuntimeError):
+        oracle.attention_rows(q, k, v, True, 0.25, np.array([B * H * T], np.int64))
+
+
+def test_bad_shapes_rejected(oracle):
+    q, k, v = _rand(1, 3, 2, 4, 4, seed=24)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, False, 1.0)
