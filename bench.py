@@ -1,0 +1,189 @@
+"""Benchmark: attention forward TFLOP/s on one MI355X, through the C ABI.
+
+One step = one fa_fwd call over the whole workload (default: the GPT-2 124M
+attention layer, B=16 H=12 T=1024 D=64, BNHD, bf16, causal), inputs resident
+in HBM. W untimed warm-up steps, then K steps timed with HIP events on the
+stream the kernel is launched on, bracketed by device synchronisation.
+
+Counted FLOP per step: 4*B*H*T^2*D, halved when causal (the dense-contraction
+count; the masked upper triangle is not counted).
+
+Prints ONE JSON line. Extra keys: `roofline` (achieved vs MI355X dense bf16
+MFMA peak), `cpu_baseline` (the float64 oracle timed on this host, with the
+GPU output compared against it as a by-product), `cold` (per-call times with
+the 256 MB last-level cache flushed before each call).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MFMA peak (GPT-2 causal bf16 shape)"
+PEAK = {"bf16": 2500.0, "f32": 157.3}     # MI355X published dense MFMA, TFLOP/s
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_91_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_gpt2_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gpt2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle until this much wall time has passed")
+    ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run one device copy of this many MiB "
+                         "(a known-size kernel for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload_name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_hash() or t.get("workload") != workload_name:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention forward is sharded "
+              "by batch/head with no exchange, and multi-GPU runs are not part of "
+              "this build. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from exact_attention_91_amd import fa
+    from exact_attention_91_amd.inputs import WORKLOADS, generate_workload
+
+    w = WORKLOADS[a.workload]
+    causal = True if True in w.causal else False
+    torch.cuda.set_device(0)
+    x = generate_workload(w)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
+    lib = fa._lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    dcode = fa._dtype_code(q)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w.B, w.H, w.H_kv, w.T, w.D, int(causal), w.scale, dcode, sp)
+
+    def step():
+        rc = lib.fa_fwd(*args)
+        if rc:
+            raise RuntimeError(fa.status_str(rc))
+
+    if a.calib_copy_mib:
+        n = a.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    flops = w.flops(causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    cold = None
+    if not a.no_cold:
+        # 512 MiB fill between calls evicts the 256 MB MALL and the L2s.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(20):
+            flush.fill_(1)
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        del flush
+        cms = float(np.median(times))
+        cold = {"ms_median": cms, "tflops": flops / (cms * 1e-3) / 1e12,
+                "ms_p10": float(np.percentile(times, 10)),
+                "ms_p90": float(np.percentile(times, 90))}
+
+    peak = PEAK[w.dtype]
+    roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+            "frac": tflops / peak, "traffic": traffic_for(w.name),
+            "kernel": f"fa_fwd_{w.dtype}_kernel<D={w.D},causal={int(causal)}>"}
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        from oracle import oracle as orc
+        torch.cuda.synchronize()
+        o_gpu = o.to(torch.float64).cpu().numpy()
+        l_gpu = lse.to(torch.float64).cpu().numpy()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            o_ref, l_ref = orc.attention(x.q64, x.k64, x.v64, causal, w.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= a.cpu_seconds:
+                break
+        sec = el / reps
+        cpu = {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+               "kind": "oracle",
+               "sample": f"the full {w.name} workload (all {w.B * w.H * w.T} query rows), "
+                         f"{reps} repeat(s), {sec:.3f} s each",
+               "gpu_vs_oracle_max_abs_err": {"O": float(np.max(np.abs(o_gpu - o_ref))),
+                                             "L": float(np.max(np.abs(l_gpu - l_ref)))}}
+
+    out = {
+        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} H_kv={w.H_kv} T={w.T} D={w.D} "
+                               f"BNHD {w.dtype} causal={causal}",
+                   "B": w.B, "H": w.H, "H_kv": w.H_kv, "T": w.T, "D": w.D,
+                   "causal": causal, "layout": "BNHD", "parallelism": "single GPU"},
+        "flop_per_step": flops,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "cold": cold,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,618 @@
+// fa_fwd.hip -- exact, IO-aware, tiled attention forward for MI355X (gfx950),
+// and the C ABI declared in include/fa.h.
+//
+// Method (pages by title and section):
+//  * "Flash Attention Memory Optimization Explained" (lzwjava.github.io),
+//    "What is Flash Attention?" / "Key Mechanisms": tile Q, K, V into on-chip
+//    memory, fuse scale, mask, softmax and the weighted sum into one kernel,
+//    normalise rows incrementally with an online softmax; the result is exact.
+//  * yelogs.com Flash Attention2-in-Triton article, "核心 Kernel 實現": one
+//    program per (batch*head, query tile); fp32 running max m, normaliser l and
+//    output accumulator; loop over key/value tiles; epilogue O /= l and the
+//    stored statistic m + log l. "因果掩碼的高效實現": key visible iff key
+//    position <= query position; the loop stops at the last key tile that
+//    touches the query tile. "Softmax 的在線計算": m_new = max(m_old, max s),
+//    l_new = exp(m_old - m_new) l_old + sum exp(s - m_new).
+//    "多查詢注意力（MQA）": query heads share a kv head (read in place, never
+//    expanded).
+//
+// gfx950 design (not the pages' Triton/CUDA design):
+//  * One work-group = 4 waves (256 lanes) = one 128-row query tile of one
+//    (batch, head). Each wave owns 32 query rows for the whole key loop.
+//  * Scores are computed transposed, S^T = K Q^T, on 32x32 MFMA. In the 32x32
+//    accumulator layout lane (col, half) holds column col = query row and 16
+//    key rows, so every softmax statistic of a query row lives in one lane pair
+//    (lane, lane^32): row max/sum are in-lane reductions plus one
+//    v_permlane32_swap, and the rescale factor is a per-lane scalar.
+//  * The output is accumulated transposed too, O^T += V^T P^T: P^T is used as
+//    the B operand straight from the score registers (no LDS round trip); V is
+//    stored transposed in LDS with a key permutation that makes each lane's
+//    8 keys contiguous, so the A operand is one 16-byte LDS read.
+//  * K/V tiles (64 keys, bf16; 32 keys, fp32) are double-buffered in LDS with
+//    the next tile's global loads issued before the current tile's math; one
+//    barrier per tile. LDS row strides are padded so the MFMA operand reads
+//    and the staging writes are bank-conflict free.
+//  * The scale is applied to fp32 scores (folded with log2 e into one FMA
+//    before exp2); q is never rescaled in its input precision. A negative scale
+//    flips q's sign bits in registers (exact) so the kernel always sees c > 0.
+//  * Causal: key tiles past the query tile are never loaded; a wave skips the
+//    math of tiles wholly in its future; only tiles that touch the diagonal or
+//    the ragged end T are masked element-wise. Query tiles are issued
+//    heaviest-first.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 waves of 64
+constexpr int kBQ = 128;        // query rows per work-group (32 per wave)
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct FwdParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    long long qs[3], ks[3], vs[3], os[3];  // element strides {batch, token, head}
+    int B, H, H_kv, T;
+    int group;      // H / H_kv
+    int nq;         // query tiles per (batch, head)
+    int nbh;        // B * H
+    float c;        // |scale| * log2(e), > 0
+    unsigned qsign; // XOR mask applied to q's bits (sign flip for scale < 0)
+};
+
+// Cross-half (lane <-> lane^32) reductions of a per-lane value.
+__device__ __forceinline__ float half_swap_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work unit of this work-group: heaviest query tiles first (causal), then
+// (batch, head).
+struct Unit {
+    int b, h, g, q0;
+};
+__device__ __forceinline__ Unit unit_of(const FwdParams &p) {
+    const int id = blockIdx.x;
+    const int t = id / p.nbh;
+    const int bh = id - t * p.nbh;
+    Unit u;
+    u.b = bh / p.H;
+    u.h = bh - u.b * p.H;
+    u.g = u.h / p.group;
+    u.q0 = (p.nq - 1 - t) * kBQ;
+    return u;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel: bf16 operands, fp32 accumulation, 64-key tiles.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
+    constexpr int BK = 64;
+    constexpr int KS = D / 16;              // MFMA k-steps over the head dim
+    constexpr int ND = (D + 31) / 32;       // 32-row blocks of O^T
+    constexpr int KST = D + 8;              // K row stride in LDS (bf16 elements)
+    constexpr int VST = BK + 8;             // V^T row stride in LDS (bf16 elements)
+    constexpr int KCH = BK * D / 8;         // 16-byte chunks per K tile
+    constexpr int KPT = (KCH + kThreads - 1) / kThreads;
+    constexpr int VUNITS = (BK / 4) * (D / 8);  // (4 keys x 8 dims) units per V tile
+    static_assert(VUNITS <= kThreads, "V staging assumes one unit per lane");
+
+    __shared__ __attribute__((aligned(16))) unsigned short k_lds[2][BK * KST];
+    __shared__ __attribute__((aligned(16))) unsigned short vt_lds[2][D * VST];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int T = p.T;
+    const Unit u = unit_of(p);
+    const int wq0 = u.q0 + wave * 32;       // first query row of this wave
+    const int qrow = wq0 + col;             // this lane's query row
+
+    const unsigned short *kbase =
+        (const unsigned short *)p.k + u.b * p.ks[0] + u.g * p.ks[2];
+    const unsigned short *vbase =
+        (const unsigned short *)p.v + u.b * p.vs[0] + u.g * p.vs[2];
+
+    // Q fragment = B operand of S^T = K Q^T: lane (col, half) holds
+    // q[qrow, 16*ks + 8*half + 0..7].
+    bf16x8_t qf[KS];
+    {
+        const unsigned short *qr = (const unsigned short *)p.q + u.b * p.qs[0] +
+                                   u.h * p.qs[2] + (long long)qrow * p.qs[1] + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4_t x = {0u, 0u, 0u, 0u};
+            if (qrow < T) x = *(const u32x4_t *)(qr + 16 * ks);
+            x ^= p.qsign;
+            qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+        }
+    }
+
+    const int kend = CAUSAL ? min(T, u.q0 + kBQ) : T;
+    const int nkt = (kend + BK - 1) / BK;
+
+    // Staging registers for the next K/V tile.
+    u32x4_t kreg[KPT];
+    u32x4_t vreg[4];
+    const int vkq = tid & 15;               // V unit: key quad
+    const int vdc = tid >> 4;               // V unit: 8-dim chunk
+
+    auto load_tile = [&](int j) {
+        const int key0 = j * BK;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int c = tid + i * kThreads;
+            if (KCH % kThreads == 0 || c < KCH) {
+                const int row = c / (D / 8), dc = c % (D / 8);
+                const int key = key0 + row;
+                u32x4_t x = {0u, 0u, 0u, 0u};
+                if (key < T) x = *(const u32x4_t *)(kbase + (long long)key * p.ks[1] + 8 * dc);
+                kreg[i] = x;
+            }
+        }
+        if (tid < VUNITS) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 4 * vkq + r;
+                u32x4_t x = {0u, 0u, 0u, 0u};
+                if (key < T) x = *(const u32x4_t *)(vbase + (long long)key * p.vs[1] + 8 * vdc);
+                vreg[r] = x;
+            }
+        }
+    };
+
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int c = tid + i * kThreads;
+            if (KCH % kThreads == 0 || c < KCH) {
+                const int row = c / (D / 8), dc = c % (D / 8);
+                *(u32x4_t *)&k_lds[buf][row * KST + 8 * dc] = kreg[i];
+            }
+        }
+        if (tid < VUNITS) {
+            // Key quad kq = 4s + 2x + y' holds keys 16s + 8x + 4y' + (0..3); it is
+            // stored at quad position 4s + 2y' + x so that lane half y' later
+            // reads its 8 keys {16s + 4y' + (0..3), 16s + 8 + 4y' + (0..3)}
+            // as one contiguous 16-byte run.
+            const int pq = (vkq & ~3) | ((vkq & 1) << 1) | ((vkq >> 1) & 1);
+#pragma unroll
+            for (int dd = 0; dd < 8; ++dd) {
+                const int w = dd >> 1;
+                u32x2_t out;
+                if (dd & 1) {
+                    out[0] = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
+                    out[1] = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
+                } else {
+                    out[0] = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
+                    out[1] = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
+                }
+                *(u32x2_t *)&vt_lds[buf][(8 * vdc + dd) * VST + 4 * pq] = out;
+            }
+        }
+    };
+
+    f32x16_t oacc[ND];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) oacc[n] = f32x16_t{};
+    float mc = -INFINITY;   // running row max, log2 domain (max score * c)
+    float lsum = 0.f;       // this lane's partial normaliser (its 16-key half)
+    const float c = p.c;
+    const bool wave_live = wq0 < T;
+
+    load_tile(0);
+    for (int j = 0; j < nkt; ++j) {
+        const int buf = j & 1;
+        store_tile(buf);
+        __syncthreads();
+        if (j + 1 < nkt) load_tile(j + 1);
+
+        const int key0 = j * BK;
+        const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        if (!active) continue;
+
+        // S^T tile: 64 keys x 32 queries as two 32x32 blocks.
+        f32x16_t s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8_t a =
+                    *(const bf16x8_t *)&k_lds[buf][(32 * kb + col) * KST + 16 * ks + 8 * half];
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+            }
+        }
+
+        // Element (kb, r) of this lane is key key0 + 32kb + 8(r/4) + 4half + r%4.
+        const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const bool vis = key < T && (!CAUSAL || key <= qrow);
+                    s[kb][r] = vis ? s[kb][r] : -INFINITY;
+                }
+        }
+
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = half_swap_max(mx);
+        const float mc_new = fmaxf(mc, mx * c);
+        const float mref = (mc_new == -INFINITY) ? 0.f : mc_new;
+        const float alpha = fast_exp2(mc - mref);
+        mc = mc_new;
+
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = fast_exp2(fmaf(s[kb][r], c, -mref));
+                psum += s[kb][r];
+            }
+        lsum = fmaf(lsum, alpha, psum);
+#pragma unroll
+        for (int n = 0; n < ND; ++n) oacc[n] *= alpha;
+
+        // P^T as the B operand: k-step s4 covers keys 16*s4 .. 16*s4+15; lane
+        // half y, element e is key 16*s4 + 8*(e/4) + 4*y + e%4, which is score
+        // register 8*(s4%2) + e of block s4/2.
+        bf16x8_t pb[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[s4][e] = (__bf16)s[s4 >> 1][8 * (s4 & 1) + e];
+
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                bf16x8_t a = {};
+                if (D >= 32 || col < D)
+                    a = *(const bf16x8_t *)&vt_lds[buf][(32 * n + col) * VST + 16 * s4 + 8 * half];
+                oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s4], oacc[n], 0, 0, 0);
+            }
+        }
+    }
+
+    if (!wave_live) return;
+    const float lt = half_swap_sum(lsum);
+    if (qrow >= T) return;
+    const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+    unsigned short *orow = (unsigned short *)p.o + u.b * p.os[0] + (long long)qrow * p.os[1] +
+                           u.h * p.os[2];
+    // O^T register r of block n is dim 32n + 8(r/4) + 4half + r%4 of this row.
+#pragma unroll
+    for (int n = 0; n < ND; ++n)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d = 32 * n + 8 * rg + 4 * half;
+            if (D >= 32 || d < D) {
+                bf16x4_t o4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[n][4 * rg + e] * inv);
+                *(u32x2_t *)(orow + d) = __builtin_bit_cast(u32x2_t, o4);
+            }
+        }
+    if (half == 0)
+        p.lse[((long long)u.b * p.H + u.h) * T + qrow] =
+            lt > 0.f ? (mc + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: fp32 operands on fp32 MFMA (32x32x2), 32-key tiles. Weights stay
+// fp32 for P.V.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
+    constexpr int BK = 32;
+    constexpr int KS = D / 2;               // MFMA k-steps over the head dim
+    constexpr int ND = (D + 31) / 32;
+    constexpr int KST = D + 1;              // odd stride: column reads hit 32 banks
+    constexpr int VST = D;
+    constexpr int CH = BK * D / 4;          // float4 chunks per tile
+    constexpr int CPT = (CH + kThreads - 1) / kThreads;
+
+    __shared__ float k_lds[2][BK * KST];
+    __shared__ __attribute__((aligned(16))) float v_lds[2][BK * VST];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int T = p.T;
+    const Unit u = unit_of(p);
+    const int wq0 = u.q0 + wave * 32;
+    const int qrow = wq0 + col;
+
+    const float *kbase = (const float *)p.k + u.b * p.ks[0] + u.g * p.ks[2];
+    const float *vbase = (const float *)p.v + u.b * p.vs[0] + u.g * p.vs[2];
+
+    // Q fragment: lane (col, half) holds q[qrow, 2*ks + half].
+    float qf[KS];
+    {
+        const float *qr = (const float *)p.q + u.b * p.qs[0] + u.h * p.qs[2] +
+                          (long long)qrow * p.qs[1];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            unsigned x = 0u;
+            if (qrow < T) x = __float_as_uint(qr[2 * ks + half]);
+            qf[ks] = __uint_as_float(x ^ p.qsign);
+        }
+    }
+
+    const int kend = CAUSAL ? min(T, u.q0 + kBQ) : T;
+    const int nkt = (kend + BK - 1) / BK;
+
+    f32x4_t kreg[CPT], vreg[CPT];
+    auto load_tile = [&](int j) {
+        const int key0 = j * BK;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            if (CH % kThreads == 0 || c < CH) {
+                const int row = c / (D / 4), dc = c % (D / 4);
+                const int key = key0 + row;
+                f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+                if (key < T) {
+                    x = *(const f32x4_t *)(kbase + (long long)key * p.ks[1] + 4 * dc);
+                    y = *(const f32x4_t *)(vbase + (long long)key * p.vs[1] + 4 * dc);
+                }
+                kreg[i] = x;
+                vreg[i] = y;
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * kThreads;
+            if (CH % kThreads == 0 || c < CH) {
+                const int row = c / (D / 4), dc = c % (D / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) k_lds[buf][row * KST + 4 * dc + e] = kreg[i][e];
+                *(f32x4_t *)&v_lds[buf][row * VST + 4 * dc] = vreg[i];
+            }
+        }
+    };
+
+    f32x16_t oacc[ND];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) oacc[n] = f32x16_t{};
+    float mc = -INFINITY, lsum = 0.f;
+    const float c = p.c;
+    const bool wave_live = wq0 < T;
+
+    load_tile(0);
+    for (int j = 0; j < nkt; ++j) {
+        const int buf = j & 1;
+        store_tile(buf);
+        __syncthreads();
+        if (j + 1 < nkt) load_tile(j + 1);
+
+        const int key0 = j * BK;
+        const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        if (!active) continue;
+
+        // S^T block: 32 keys x 32 queries; register r is key key0 + 8(r/4) + 4half + r%4.
+        f32x16_t s = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            s = __builtin_amdgcn_mfma_f32_32x32x2f32(k_lds[buf][col * KST + 2 * ks + half],
+                                                     qf[ks], s, 0, 0, 0);
+
+        const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
+        if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                const bool vis = key < T && (!CAUSAL || key <= qrow);
+                s[r] = vis ? s[r] : -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = half_swap_max(mx);
+        const float mc_new = fmaxf(mc, mx * c);
+        const float mref = (mc_new == -INFINITY) ? 0.f : mc_new;
+        const float alpha = fast_exp2(mc - mref);
+        mc = mc_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[r] = fast_exp2(fmaf(s[r], c, -mref));
+            psum += s[r];
+        }
+        lsum = fmaf(lsum, alpha, psum);
+#pragma unroll
+        for (int n = 0; n < ND; ++n) oacc[n] *= alpha;
+
+        // O^T += V^T P^T, k-step st: lane half y supplies key 8(st/4) + 4y + st%4,
+        // which is its own score register st.
+#pragma unroll
+        for (int n = 0; n < ND; ++n)
+#pragma unroll
+            for (int st = 0; st < 16; ++st) {
+                const int key = 8 * (st >> 2) + 4 * half + (st & 3);
+                float a = 0.f;
+                if (D >= 32 || col < D) a = v_lds[buf][key * VST + 32 * n + col];
+                oacc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[st], oacc[n], 0, 0, 0);
+            }
+    }
+
+    if (!wave_live) return;
+    const float lt = half_swap_sum(lsum);
+    if (qrow >= T) return;
+    const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+    float *orow = (float *)p.o + u.b * p.os[0] + (long long)qrow * p.os[1] + u.h * p.os[2];
+#pragma unroll
+    for (int n = 0; n < ND; ++n)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d = 32 * n + 8 * rg + 4 * half;
+            if (D >= 32 || d < D) {
+                f32x4_t o4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = oacc[n][4 * rg + e] * inv;
+                *(f32x4_t *)(orow + d) = o4;
+            }
+        }
+    if (half == 0)
+        p.lse[((long long)u.b * p.H + u.h) * T + qrow] =
+            lt > 0.f ? (mc + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation (no HIP calls), dispatch, launch.
+// ---------------------------------------------------------------------------
+constexpr long long kMaxOffset = 1LL << 62;
+constexpr long long kMaxGrid = (1LL << 24) - 1;
+
+// Largest element offset + 1 of a [B, T, heads, D] view; -1 on overflow.
+long long extent(const long long s[3], int B, int T, int heads, int D) {
+    long long e = D, t;
+    const long long n[3] = {B - 1LL, T - 1LL, heads - 1LL};
+    for (int i = 0; i < 3; ++i) {
+        if (__builtin_mul_overflow(n[i], s[i], &t) || __builtin_add_overflow(e, t, &e))
+            return -1;
+    }
+    return e;
+}
+
+bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+template <int D, bool CAUSAL>
+void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
+    if (dtype == FA_DTYPE_BF16)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
+}
+
+template <bool CAUSAL>
+void launch_d(const FwdParams &p, int D, int dtype, dim3 grid, hipStream_t stream) {
+    switch (D) {
+        case 16: launch<16, CAUSAL>(p, dtype, grid, stream); break;
+        case 32: launch<32, CAUSAL>(p, dtype, grid, stream); break;
+        case 64: launch<64, CAUSAL>(p, dtype, grid, stream); break;
+        default: launch<128, CAUSAL>(p, dtype, grid, stream); break;
+    }
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int B, int H, int H_kv, int T, int D, int causal, float scale,
+                              int dtype, const long long q_strides[3],
+                              const long long k_strides[3], const long long v_strides[3],
+                              const long long o_strides[3], void *stream) {
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+    if (B < 0 || T < 0 || H < 1 || H_kv < 1) return FA_ERR_BAD_SHAPE;
+    if (H % H_kv != 0) return FA_ERR_HEADS;
+    if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
+    float c = fabsf(scale) * kLog2e;
+    if (!isfinite(c)) return FA_ERR_SCALE;
+    if (B == 0 || T == 0) return FA_OK;
+    if (!q || !k || !v || !o || !lse || !q_strides || !k_strides || !v_strides || !o_strides)
+        return FA_ERR_NULL_PTR;
+    const long long *st[4] = {q_strides, k_strides, v_strides, o_strides};
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 3; ++j)
+            if (st[i][j] < 0) return FA_ERR_STRIDE;
+    const long long vec = dtype == FA_DTYPE_BF16 ? 8 : 4;  // elements per 16 bytes
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 3; ++j)
+            if (st[i][j] % vec != 0) return FA_ERR_ALIGN;
+    const long long eq = extent(q_strides, B, T, H, D), eo = extent(o_strides, B, T, H, D);
+    const long long ek = extent(k_strides, B, T, H_kv, D), ev = extent(v_strides, B, T, H_kv, D);
+    if (eq < 0 || eo < 0 || ek < 0 || ev < 0 || eq > kMaxOffset || eo > kMaxOffset ||
+        ek > kMaxOffset || ev > kMaxOffset)
+        return FA_ERR_OVERFLOW;
+    const long long nq = (T + kBQ - 1) / kBQ;
+    const long long nbh = (long long)B * H;
+    if (nbh > kMaxGrid || nbh * nq > kMaxGrid || nbh * T > kMaxOffset) return FA_ERR_OVERFLOW;
+
+    FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    for (int j = 0; j < 3; ++j) {
+        p.qs[j] = q_strides[j]; p.ks[j] = k_strides[j];
+        p.vs[j] = v_strides[j]; p.os[j] = o_strides[j];
+    }
+    p.B = B; p.H = H; p.H_kv = H_kv; p.T = T;
+    p.group = H / H_kv;
+    p.nq = (int)nq;
+    p.nbh = (int)nbh;
+    // scale == 0 means uniform weights; the smallest normal c reproduces them
+    // exactly in fp32 (every c*s rounds to a value whose exp2 is 1).
+    p.c = c > 0.f ? c : 1.17549435e-38f;
+    p.qsign = scale < 0.f ? (dtype == FA_DTYPE_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+
+    const dim3 grid((unsigned)(nbh * nq));
+    hipStream_t s = (hipStream_t)stream;
+    if (causal)
+        launch_d<true>(p, D, dtype, grid, s);
+    else
+        launch_d<false>(p, D, dtype, grid, s);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                      int H, int H_kv, int T, int D, int causal, float scale, int dtype,
+                      void *stream) {
+    const long long qs[3] = {(long long)T * H * D, (long long)H * D, D};
+    const long long ks[3] = {(long long)T * H_kv * D, (long long)H_kv * D, D};
+    return fa_fwd_strided(q, k, v, o, lse, B, H, H_kv, T, D, causal, scale, dtype, qs, ks, ks,
+                          qs, stream);
+}
+
+extern "C" const char *fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL_PTR: return "null pointer argument";
+        case FA_ERR_BAD_SHAPE: return "bad shape: need B >= 0, T >= 0, H >= 1, H_kv >= 1";
+        case FA_ERR_HEADS: return "H must be a multiple of H_kv";
+        case FA_ERR_HEAD_DIM: return "head dim D must be 16, 32, 64 or 128";
+        case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
+        case FA_ERR_SCALE: return "scale must be finite (and |scale|*log2(e) finite)";
+        case FA_ERR_ALIGN:
+            return "misaligned: q/k/v/o need 16-byte alignment and 16-byte-multiple strides, "
+                   "lse 4-byte alignment";
+        case FA_ERR_OVERFLOW: return "size overflow: offsets beyond 2^62 or grid beyond 2^24-1";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_STRIDE: return "negative stride";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int fa_version(void) { return 100; }

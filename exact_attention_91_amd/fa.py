@@ -21,6 +21,7 @@ FA_DTYPE_BF16 = 1
 _I = ctypes.c_int
 _VP = ctypes.c_void_p
 _LL3 = ctypes.c_longlong * 3
+_LLP = ctypes.POINTER(ctypes.c_longlong)
 
 
 def lib_path() -> str:
@@ -35,10 +36,10 @@ def _lib():
                 f"libfa.so not found at {_LIB_PATH}: build it first "
                 "(python -c 'import __graft_entry__ as g; g.build()')")
         lib = ctypes.CDLL(_LIB_PATH)
-        lib.fa_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP] + [_I] * 7 + [ctypes.c_float, _I, _VP]
+        lib.fa_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP] + [_I] * 6 + [ctypes.c_float, _I, _VP]
         lib.fa_fwd.restype = _I
-        lib.fa_fwd_strided.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 7 +
-                                       [ctypes.c_float, _I] + [_LL3] * 4 + [_VP])
+        lib.fa_fwd_strided.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
+                                       [ctypes.c_float, _I] + [_LLP] * 4 + [_VP])
         lib.fa_fwd_strided.restype = _I
         lib.fa_status_str.argtypes = [_I]
         lib.fa_status_str.restype = ctypes.c_char_p

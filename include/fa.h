@@ -1,0 +1,117 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact, IO-aware, tiled attention forward on
+ * MI355X (gfx950).
+ *
+ * What it computes. For every batch b, query head h and query row i, with kv
+ * head g = h / (H / H_kv) and visible keys V_i = { j < T : !causal or j <= i }:
+ *   s_ij = scale * q[b,i,h,:] . k[b,j,g,:]
+ *   o[b,i,h,:] = sum_{j in V_i} softmax_j(s_i.) * v[b,j,g,:]
+ *   lse[b,h,i] = ln sum_{j in V_i} exp(s_ij)
+ * in one fused kernel: the T x T score matrix never reaches device memory.
+ * This is the forward pass described by
+ *  - "Flash Attention Memory Optimization Explained" (lzwjava.github.io),
+ *    sections "What is Flash Attention?" and "Key Mechanisms" (tiling into
+ *    on-chip memory, one fused kernel, online softmax, exact result, causal
+ *    masking built in), and
+ *  - the yelogs.com Flash Attention2-in-Triton article, sections
+ *    "核心 Kernel 實現" (per query tile: loop over key/value tiles, running max m,
+ *    normaliser l and output accumulator in fp32, final O /= l and stored
+ *    statistic m + log l), "因果掩碼的高效實現" (a key is visible iff its position
+ *    is <= the query position; key tiles wholly in the future are skipped),
+ *    "Softmax 的在線計算" (the rescaling recurrence) and "多查詢注意力（MQA）"
+ *    (several query heads sharing one kv head).
+ * The statistic is stored with eps = 0, as the natural-log logsumexp of the
+ * scaled scores (the article's epilogue adds an eps inside the log; the
+ * normaliser is always >= 1, so eps <= 1e-6 moves it by at most 1e-6).
+ *
+ * Precision. bf16 path: q, k, v, o in bfloat16; both products on bf16 MFMA
+ * with fp32 accumulation; scale applied to the fp32 scores (q is never
+ * rescaled in bf16); softmax weights rounded to bf16 (nearest even) only as
+ * the operand of P.V, while the normaliser sums the fp32 weights; o rounded to
+ * nearest even. fp32 path: everything in fp32 (fp32 MFMA), no down-conversion.
+ *
+ * Layout. Elements are addressed with element strides (batch, token, head);
+ * the head-dim stride is 1.
+ *   fa_fwd:         q, o contiguous [B, T, H, D]; k, v contiguous [B, T, H_kv, D]
+ *   fa_fwd_strided: any non-negative strides (e.g. [B, H, T, D] storage)
+ *   lse:            always contiguous float32 [B, H, T]
+ *
+ * Ownership. All pointers are device memory owned by the caller. The library
+ * allocates nothing, frees nothing and keeps no pointer after returning.
+ * o and lse must not overlap q, k, v or each other.
+ *
+ * Execution. Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns without synchronising. Inputs must stay valid
+ * until that work completes. Calls are thread-safe (no mutable global state).
+ *
+ * Errors. Arguments are validated completely before any HIP call; on an
+ * invalid argument nothing is launched and a nonzero fa_status_t is returned.
+ * A launch rejected by the runtime returns FA_ERR_LAUNCH. Faults during
+ * execution surface at the caller's next synchronisation, as for any kernel.
+ * B == 0 or T == 0 is a valid empty call: it returns FA_OK and launches
+ * nothing (pointers may then be NULL).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL_PTR = 1,   /* a required pointer is NULL                       */
+    FA_ERR_BAD_SHAPE = 2,  /* B < 0, T < 0, H < 1 or H_kv < 1                  */
+    FA_ERR_HEADS = 3,      /* H is not a multiple of H_kv                      */
+    FA_ERR_HEAD_DIM = 4,   /* D not in {16, 32, 64, 128}                       */
+    FA_ERR_DTYPE = 5,      /* dtype not an fa_dtype_t value                    */
+    FA_ERR_SCALE = 6,      /* scale is NaN or infinite                         */
+    FA_ERR_ALIGN = 7,      /* q/k/v/o not 16-byte aligned, lse not 4-byte
+                              aligned, or a stride not a multiple of 16 bytes  */
+    FA_ERR_OVERFLOW = 8,   /* an element offset would exceed 2^62, or the grid
+                              would exceed 2^24 - 1 work-groups                */
+    FA_ERR_LAUNCH = 9,     /* the HIP runtime rejected the kernel launch       */
+    FA_ERR_STRIDE = 10     /* a negative stride                                */
+} fa_status_t;
+
+/*
+ * Attention forward on contiguous BNHD tensors.
+ *   q    [B, T, H, D]     dtype      read
+ *   k, v [B, T, H_kv, D]  dtype      read
+ *   o    [B, T, H, D]     dtype      written
+ *   lse  [B, H, T]        float32    written (natural-log logsumexp per row)
+ *   causal: nonzero = key j visible to query i iff j <= i.
+ *   scale:  any finite value, applied to q.k (1/sqrt(D) is the usual choice).
+ *   dtype:  FA_DTYPE_BF16 or FA_DTYPE_F32 (applies to q, k, v and o).
+ *   stream: hipStream_t or NULL.
+ * Returns an fa_status_t.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+           int B, int H, int H_kv, int T, int D, int causal, float scale,
+           int dtype, void *stream);
+
+/*
+ * Same computation, with element strides {batch, token, head} for each of q,
+ * k, v and o (head-dim stride 1). Lets callers pass [B, H, T, D] storage or
+ * other views without a copy. Strides must be >= 0 and multiples of 8 (bf16)
+ * or 4 (fp32) elements.
+ */
+int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int H_kv, int T, int D, int causal, float scale,
+                   int dtype, const long long q_strides[3],
+                   const long long k_strides[3], const long long v_strides[3],
+                   const long long o_strides[3], void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *fa_status_str(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: libfa.so loads, exports every function that
+include/fa.h declares, and rejects every invalid argument before any HIP call
+(validation is pure host code, so these calls never reach the device)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_attention_91_amd import fa
+    if not os.path.exists(fa.lib_path()):
+        from exact_attention_91_amd import build
+        build.build()
+    return fa._lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+
+
+def _enum_values(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef enum \{([^}]*)\}\s*" + name, text).group(1)
+    return dict((k, int(v)) for k, v in re.findall(r"(FA_\w+)\s*=\s*(\d+)", body))
+
+
+ST = _enum_values("fa_status_t")
+DT = _enum_values("fa_dtype_t")
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_status_str", "fa_version"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    # and nothing else with the fa_ prefix escapes the library
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "exact_attention_91_amd",
+                          "libfa.so")], capture_output=True, text=True, check=True).stdout
+    exported = sorted(set(re.findall(r"\bT (fa_\w+)", out)))
+    assert exported == _declared_functions()
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fa_version() == 100
+    seen = set()
+    for code in ST.values():
+        s = lib.fa_status_str(code).decode()
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == len(ST)
+    assert lib.fa_status_str(12345).decode() == "unknown status"
+    assert lib.fa_status_str(-1).decode() == "unknown status"
+
+
+# A fake, 16-byte aligned, never-dereferenced device address: every call below
+# fails validation, which runs entirely on the host before any HIP call.
+P = 4096
+
+
+def call(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, T=100, D=64, causal=1,
+             scale=0.125, dtype=DT["FA_DTYPE_BF16"], stream=None)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"],
+                      a["T"], a["D"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+def call_strided(lib, qs=(0, 0, 0), ks=(0, 0, 0), vs=(0, 0, 0), os_=(0, 0, 0), **kw):
+    from exact_attention_91_amd.fa import _LL3
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, T=100, D=64, causal=0,
+             scale=0.125, dtype=DT["FA_DTYPE_BF16"])
+    a.update(kw)
+    return lib.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                              a["H_kv"], a["T"], a["D"], a["causal"], a["scale"], a["dtype"],
+                              _LL3(*qs), _LL3(*ks), _LL3(*vs), _LL3(*os_), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), "FA_ERR_DTYPE"),
+    (dict(dtype=-1), "FA_ERR_DTYPE"),
+    (dict(B=-1), "FA_ERR_BAD_SHAPE"),
+    (dict(T=-5), "FA_ERR_BAD_SHAPE"),
+    (dict(H=0), "FA_ERR_BAD_SHAPE"),
+    (dict(H_kv=0), "FA_ERR_BAD_SHAPE"),
+    (dict(H=6, H_kv=4), "FA_ERR_HEADS"),
+    (dict(H=2, H_kv=4), "FA_ERR_HEADS"),
+    (dict(D=8), "FA_ERR_HEAD_DIM"),
+    (dict(D=48), "FA_ERR_HEAD_DIM"),
+    (dict(D=256), "FA_ERR_HEAD_DIM"),
+    (dict(scale=math.nan), "FA_ERR_SCALE"),
+    (dict(scale=math.inf), "FA_ERR_SCALE"),
+    (dict(scale=-math.inf), "FA_ERR_SCALE"),
+    (dict(scale=3.0e38), "FA_ERR_SCALE"),        # |scale| * log2(e) overflows fp32
+    (dict(q=None), "FA_ERR_NULL_PTR"),
+    (dict(lse=None), "FA_ERR_NULL_PTR"),
+    (dict(o=None), "FA_ERR_NULL_PTR"),
+    (dict(q=P + 8), "FA_ERR_ALIGN"),
+    (dict(v=P + 2), "FA_ERR_ALIGN"),
+    (dict(lse=P + 2), "FA_ERR_ALIGN"),
+    (dict(B=1 << 20, H=1 << 10, H_kv=1, T=1 << 12), "FA_ERR_OVERFLOW"),   # grid > 2^24-1
+])
+def test_fa_fwd_rejects(lib, kw, code):
+    assert call(lib, **kw) == ST[code]
+
+
+def test_fp32_alignment_rule(lib):
+    # fp32 rows need 16-byte alignment too
+    assert call(lib, dtype=DT["FA_DTYPE_F32"], k=P + 4) == ST["FA_ERR_ALIGN"]
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(B=0, q=None, k=None, v=None, o=None,
+                                                            lse=None)])
+def test_empty_call_is_a_noop(lib, kw):
+    # nothing to compute: success without a launch (null pointers allowed)
+    assert call(lib, **kw) == ST["FA_OK"]
+
+
+def test_strided_rejects(lib):
+    good = (100 * 4 * 64, 4 * 64, 64)
+    kvs = (100 * 2 * 64, 2 * 64, 64)
+    base = dict(qs=good, ks=kvs, vs=kvs, os_=good)
+    bad_neg = dict(base, ks=(-64, 128, 64))
+    assert call_strided(lib, **bad_neg) == ST["FA_ERR_STRIDE"]
+    bad_mult = dict(base, vs=(100 * 2 * 64, 2 * 64 + 4, 64))
+    assert call_strided(lib, **bad_mult) == ST["FA_ERR_ALIGN"]
+    huge = dict(base, qs=(1 << 62, 4 * 64, 64))
+    assert call_strided(lib, **huge) == ST["FA_ERR_OVERFLOW"]
+    wrap = dict(base, os_=((1 << 62) + 8, 4 * 64, 64))
+    assert call_strided(lib, **wrap) == ST["FA_ERR_OVERFLOW"]
+    from exact_attention_91_amd.fa import _LL3
+    rc = lib.fa_fwd_strided(P, P, P, P, P, 2, 4, 2, 100, 64, 0, 0.125, 1,
+                            None, _LL3(*kvs), _LL3(*kvs), _LL3(*good), None)
+    assert rc == ST["FA_ERR_NULL_PTR"]
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from exact_attention_91_amd import fa
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing" / "libfa.so"))
+    with pytest.raises(RuntimeError, match="libfa.so not found"):
+        fa.version()

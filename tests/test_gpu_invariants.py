@@ -1,0 +1,146 @@
+"""Properties of the HIP path that hold bitwise: determinism, causal
+future-independence, shared kv heads == expanded copies, layout independence,
+untouched memory around the outputs, empty calls and error reporting."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_91_amd import fa
+from exact_attention_91_amd.inputs import generate
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run(q, k, v, causal, scale=0.125):
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_deterministic(dtype):
+    x = generate(4, 6, 2, 777, 64, dtype, 301)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o1, l1 = _run(q, k, v, True)
+    o2, l2 = _run(q, k, v, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("t0", [1, 64, 200, 511])
+def test_causal_future_independence(dtype, t0):
+    """Changing K/V rows >= t0 leaves causal outputs of rows < t0 bitwise equal."""
+    B, H, T, D = 2, 3, 512, 64
+    x = generate(B, H, 1, T, D, dtype, 302)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o1, l1 = _run(q, k, v, True)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, t0:] = torch.randn_like(k2[:, t0:]) * 3
+    v2[:, t0:] = torch.randn_like(v2[:, t0:]) * 3
+    o2, l2 = _run(q, k2, v2, True)
+    assert torch.equal(o1[:, :t0], o2[:, :t0])
+    assert torch.equal(l1[:, :, :t0], l2[:, :, :t0])
+    assert not torch.equal(o1[:, t0:], o2[:, t0:])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("H_kv", [1, 2])
+def test_shared_kv_equals_expanded(dtype, H_kv):
+    B, H, T, D = 2, 6, 333, 64
+    x = generate(B, H, H_kv, T, D, dtype, 303)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    ke = k.repeat_interleave(H // H_kv, dim=2).contiguous()
+    ve = v.repeat_interleave(H // H_kv, dim=2).contiguous()
+    for causal in (False, True):
+        o1, l1 = _run(q, k, v, causal)
+        o2, l2 = _run(q, ke, ve, causal)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_bhtd_equals_contiguous(dtype):
+    """[B, H, T, D] storage through fa_fwd_strided gives the same bits."""
+    B, H, T, D = 2, 4, 250, 32
+    x = generate(B, H, 2, T, D, dtype, 304)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o1, l1 = _run(q, k, v, True)
+    qh = q.transpose(1, 2).contiguous().transpose(1, 2)   # [B,H,T,D] storage
+    kh = k.transpose(1, 2).contiguous().transpose(1, 2)
+    vh = v.transpose(1, 2).contiguous().transpose(1, 2)
+    o2, l2 = fa.fwd_strided(qh, kh, vh, causal=True, scale=0.125, out_layout="bhtd")
+    torch.cuda.synchronize()
+    assert o2.stride() != o1.stride()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_guard_bands_untouched(dtype):
+    """Only o and lse are written: sentinel memory around them stays intact."""
+    B, H, T, D = 2, 3, 100, 64
+    x = generate(B, H, 1, T, D, dtype, 305)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    pad = 4096
+    n_o, n_l = B * T * H * D, B * H * T
+    obuf = torch.full((n_o + 2 * pad,), 7.0, dtype=q.dtype, device="cuda")
+    lbuf = torch.full((n_l + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + n_o]
+    l = lbuf[pad:pad + n_l]
+    q_before = q.clone()
+    rc = fa._lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                          B, H, 1, T, D, 1, 0.125, fa._dtype_code(q),
+                          torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.all(obuf[:pad] == 7.0) and torch.all(obuf[pad + n_o:] == 7.0)
+    assert torch.all(lbuf[:pad] == 7.0) and torch.all(lbuf[pad + n_l:] == 7.0)
+    assert torch.equal(q, q_before)
+    o_ref, l_ref = _run(q, k, v, True)
+    assert torch.equal(o.view(B, T, H, D), o_ref) and torch.equal(l.view(B, H, T), l_ref)
+
+
+def test_no_nan_on_extreme_scores():
+    B, H, T, D = 1, 2, 600, 128
+    x = generate(B, H, 1, T, D, "bf16", 306, qk_sigma=30.0)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    for causal in (False, True):
+        o, lse = _run(q, k, v, causal)
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_empty_inputs():
+    for B, T in ((0, 16), (2, 0)):
+        q = torch.empty((B, T, 2, 64), dtype=torch.bfloat16, device="cuda")
+        k = torch.empty((B, T, 1, 64), dtype=torch.bfloat16, device="cuda")
+        o, lse = _run(q, k, k, True)
+        assert o.shape == (B, T, 2, 64) and lse.shape == (B, 2, T)
+
+
+def test_errors_raise_through_binding():
+    q = torch.zeros((1, 8, 2, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="head dim"):
+        fa.fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous())
+    q = torch.zeros((1, 8, 3, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 8, 2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(RuntimeError, match="multiple of H_kv"):
+        fa.fwd(q, k, k)
+
+
+def test_runs_on_side_stream():
+    x = generate(2, 2, 1, 300, 64, "bf16", 307)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o1, l1 = _run(q, k, v, True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o2, l2 = fa.fwd(q, k, v, causal=True, scale=0.125)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
