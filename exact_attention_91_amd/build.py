@@ -8,9 +8,15 @@ SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
 LIB = os.path.join(HERE, "libfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed fp32 VALU ops are disabled for all device code.
+# Packed fp32 VALU ops are disabled for all device code. MFMA accumulators are
+# kept in ordinary VGPRs (the softmax rescales them every tile; AGPR
+# accumulators would need a copy to VGPRs and back each time).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-         "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
+         # NaN inputs are unsupported (documented in fa.h); without this every
+         # fmaxf on an MFMA result gets an extra NaN-quieting copy.
+         "-fno-honor-nans"]
 
 
 def build(verbose: bool = False, extra=()) -> str:

@@ -86,6 +86,11 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
+
 // Work unit of this work-group: heaviest query tiles first (causal), then
 // (batch, head).
 struct Unit {
@@ -105,21 +110,83 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 
 // ---------------------------------------------------------------------------
 // bf16 kernel: bf16 operands, fp32 accumulation, 64-key tiles.
+//
+// LDS layouts (one buffer; two buffers alternate between key tiles):
+//   K tile [64 keys][D], V tile [64 keys][D], rows of 2D bytes, unpadded. The
+//   16-byte chunks of each row are XOR-permuted so that the MFMA operand reads
+//   are bank-conflict free:
+//     K: physical chunk = c ^ ((row / R) % C),   C = D/8 chunks per row,
+//                                                R = 16/C rows per 256 bytes
+//     V: physical chunk = c ^ vswz(row)  (D=64: 4*((row>>1)&1); D=128: 4*(row&3))
+//   Tiles are written by buffer_load_dwordx4 ... lds straight from global
+//   memory: each 64-lane load fills 1 KB of LDS in lane order, so every lane
+//   fetches the global chunk that belongs at its LDS slot. Rows past T are
+//   outside the buffer's range and arrive as zeros.
+//   V^T fragments for P.V come from ds_read_b64_tr_b16: in each 16-lane group,
+//   lane i receives element 16e+i (e = 0..3) of the 64 halfwords the group
+//   reads, so a group reading a 4-key x 16-dim block row by row hands lane i
+//   the 4 keys of dim i.
 // ---------------------------------------------------------------------------
+template <int D>
+struct Bf16Layout {
+    static constexpr int BK = 64;                 // keys per tile
+    static constexpr int C = D / 8;               // 16-byte chunks per row
+    static constexpr int R = 16 / C;              // rows per 256 bytes
+    static constexpr int ROWB = 2 * D;            // bytes per row
+    static constexpr int TILEB = BK * ROWB;       // bytes per K (or V) tile
+    static constexpr int NLOAD = TILEB / 1024;    // 1 KB wave loads per tile
+    static constexpr int ROWS_PER_LOAD = 1024 / ROWB;
+    __device__ static int kswz(int row) { return (row / R) % C; }
+    __device__ static int vswz(int row) {
+        return D == 64 ? 4 * ((row >> 1) & 1) : (D == 128 ? 4 * (row & 3) : 0);
+    }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 family)
+constexpr float kRescaleThreshold = 8.0f;      // log2 units: weights stay <= 2^8
+
+// Issue this wave's share of the global->LDS copies of one K tile and one V
+// tile (buffer loads straight into LDS; rows past T read as zeros).
+template <int D>
+__device__ __forceinline__ void stage_tile(const unsigned short *kbase, const unsigned short *vbase,
+                                           long long ks1, long long vs1, int T, int key0,
+                                           int wave, const int *koff, const int *voff,
+                                           unsigned char *kdst, unsigned char *vdst) {
+    using L = Bf16Layout<D>;
+    constexpr int NI = (L::NLOAD + 3) / 4;
+    // Valid bytes from this tile's first row; (63 * stride + D) * 2 < 2^31 is
+    // checked on the host.
+    const int rows = min(T - key0, L::BK);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short *>(kbase + (long long)key0 * ks1), (short)0,
+        ((rows - 1) * (int)ks1 + D) * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short *>(vbase + (long long)key0 * vs1), (short)0,
+        ((rows - 1) * (int)vs1 + D) * 2, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int idx = wave + 4 * i;
+        if (L::NLOAD % 4 == 0 || idx < L::NLOAD) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kdst + idx * 1024), 16,
+                                                     koff[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + idx * 1024), 16,
+                                                     voff[i], 0, 0, 0);
+        }
+    }
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
-    constexpr int BK = 64;
+    using L = Bf16Layout<D>;
+    constexpr int BK = L::BK;
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     constexpr int ND = (D + 31) / 32;       // 32-row blocks of O^T
-    constexpr int KST = D + 8;              // K row stride in LDS (bf16 elements)
-    constexpr int VST = BK + 8;             // V^T row stride in LDS (bf16 elements)
-    constexpr int KCH = BK * D / 8;         // 16-byte chunks per K tile
-    constexpr int KPT = (KCH + kThreads - 1) / kThreads;
-    constexpr int VUNITS = (BK / 4) * (D / 8);  // (4 keys x 8 dims) units per V tile
-    static_assert(VUNITS <= kThreads, "V staging assumes one unit per lane");
+    constexpr int NV = D >= 32 ? D / 32 : 1;  // V^T address variants (one per block)
 
-    __shared__ __attribute__((aligned(16))) unsigned short k_lds[2][BK * KST];
-    __shared__ __attribute__((aligned(16))) unsigned short vt_lds[2][D * VST];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][L::TILEB];  // [buf][K,V]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -133,6 +200,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         (const unsigned short *)p.k + u.b * p.ks[0] + u.g * p.ks[2];
     const unsigned short *vbase =
         (const unsigned short *)p.v + u.b * p.vs[0] + u.g * p.vs[2];
+    const long long ks1 = p.ks[1], vs1 = p.vs[1];
 
     // Q fragment = B operand of S^T = K Q^T: lane (col, half) holds
     // q[qrow, 16*ks + 8*half + 0..7].
@@ -152,153 +220,144 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
     const int kend = CAUSAL ? min(T, u.q0 + kBQ) : T;
     const int nkt = (kend + BK - 1) / BK;
 
-    // Staging registers for the next K/V tile.
-    u32x4_t kreg[KPT];
-    u32x4_t vreg[4];
-    const int vkq = tid & 15;               // V unit: key quad
-    const int vdc = tid >> 4;               // V unit: 8-dim chunk
+    // Staging: this wave issues 1 KB loads wave, wave+4, ... of each tile.
+    // Lane slot (row, physical chunk) -> global byte offset within the tile.
+    int koff[(L::NLOAD + 3) / 4], voff[(L::NLOAD + 3) / 4];
+#pragma unroll
+    for (int i = 0; i < (L::NLOAD + 3) / 4; ++i) {
+        const int idx = wave + 4 * i;
+        const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
+        const int pc = lane % L::C;
+        koff[i] = row * (int)ks1 * 2 + 16 * (pc ^ L::kswz(row));
+        voff[i] = row * (int)vs1 * 2 + 16 * (pc ^ L::vswz(row));
+    }
 
-    auto load_tile = [&](int j) {
-        const int key0 = j * BK;
+    // Loop-invariant LDS byte offsets of this lane's operand reads.
+    int kaddr[KS];
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * kThreads;
-            if (KCH % kThreads == 0 || c < KCH) {
-                const int row = c / (D / 8), dc = c % (D / 8);
-                const int key = key0 + row;
-                u32x4_t x = {0u, 0u, 0u, 0u};
-                if (key < T) x = *(const u32x4_t *)(kbase + (long long)key * p.ks[1] + 8 * dc);
-                kreg[i] = x;
-            }
-        }
-        if (tid < VUNITS) {
+    for (int ks = 0; ks < KS; ++ks)
+        kaddr[ks] = col * L::ROWB + 16 * ((2 * ks + half) ^ L::kswz(col));
+    int vaddr[NV];
+    {
+        const int r0 = 4 * half + ((lane & 15) >> 2);     // row within a 16-key step
+        const int dl = (D >= 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = key0 + 4 * vkq + r;
-                u32x4_t x = {0u, 0u, 0u, 0u};
-                if (key < T) x = *(const u32x4_t *)(vbase + (long long)key * p.vs[1] + 8 * vdc);
-                vreg[r] = x;
-            }
+        for (int n = 0; n < NV; ++n) {
+            const int d = 32 * n + dl;
+            vaddr[n] = r0 * L::ROWB + 16 * ((d >> 3) ^ L::vswz(r0)) + 2 * (d & 7);
         }
-    };
-
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * kThreads;
-            if (KCH % kThreads == 0 || c < KCH) {
-                const int row = c / (D / 8), dc = c % (D / 8);
-                *(u32x4_t *)&k_lds[buf][row * KST + 8 * dc] = kreg[i];
-            }
-        }
-        if (tid < VUNITS) {
-            // Key quad kq = 4s + 2x + y' holds keys 16s + 8x + 4y' + (0..3); it is
-            // stored at quad position 4s + 2y' + x so that lane half y' later
-            // reads its 8 keys {16s + 4y' + (0..3), 16s + 8 + 4y' + (0..3)}
-            // as one contiguous 16-byte run.
-            const int pq = (vkq & ~3) | ((vkq & 1) << 1) | ((vkq >> 1) & 1);
-#pragma unroll
-            for (int dd = 0; dd < 8; ++dd) {
-                const int w = dd >> 1;
-                u32x2_t out;
-                if (dd & 1) {
-                    out[0] = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-                    out[1] = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
-                } else {
-                    out[0] = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-                    out[1] = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
-                }
-                *(u32x2_t *)&vt_lds[buf][(8 * vdc + dd) * VST + 4 * pq] = out;
-            }
-        }
-    };
+    }
+    const bool vzero = D < 32 && col >= D;  // D=16: rows 16..31 of V^T are zero
 
     f32x16_t oacc[ND];
 #pragma unroll
     for (int n = 0; n < ND; ++n) oacc[n] = f32x16_t{};
-    float mc = -INFINITY;   // running row max, log2 domain (max score * c)
-    float lsum = 0.f;       // this lane's partial normaliser (its 16-key half)
+    float mref = -INFINITY;  // reference max of this row, log2 domain (score * c)
+    float lsum = 0.f;        // this lane's partial normaliser (its 16-key half)
     const float c = p.c;
     const bool wave_live = wq0 < T;
 
-    load_tile(0);
-    for (int j = 0; j < nkt; ++j) {
-        const int buf = j & 1;
-        store_tile(buf);
-        __syncthreads();
-        if (j + 1 < nkt) load_tile(j + 1);
-
+    auto tile = [&](auto mask_tag, int j, int buf) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int key0 = j * BK;
-        const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
-        if (!active) continue;
+        const unsigned char *kt = &lds[buf][0][0];
+        const unsigned char *vt = &lds[buf][1][0];
 
         // S^T tile: 64 keys x 32 queries as two 32x32 blocks.
-        f32x16_t s[2];
+        f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16_t{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8_t a =
-                    *(const bf16x8_t *)&k_lds[buf][(32 * kb + col) * KST + 16 * ks + 8 * half];
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t a0 = *(const lds_bf16x8_t *)(kt + kaddr[ks]);
+            const bf16x8_t a1 = *(const lds_bf16x8_t *)(kt + kaddr[ks] + 32 * L::ROWB);
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
         }
 
-        // Element (kb, r) of this lane is key key0 + 32kb + 8(r/4) + 4half + r%4.
-        const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const bool vis = key < T && (!CAUSAL || key <= qrow);
-                    s[kb][r] = vis ? s[kb][r] : -INFINITY;
-                }
-        }
-
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = half_swap_max(mx);
-        const float mc_new = fmaxf(mc, mx * c);
-        const float mref = (mc_new == -INFINITY) ? 0.f : mc_new;
-        const float alpha = fast_exp2(mc - mref);
-        mc = mc_new;
-
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        // Element r of block kb is key key0 + 32kb + 8(r/4) + 4half + r%4.
+        if (MASK) {
+            const int lim = (CAUSAL ? min(qrow, T - 1) : T - 1) - key0 - 4 * half;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s[kb][r] = fast_exp2(fmaf(s[kb][r], c, -mref));
-                psum += s[kb][r];
+                const int off = 8 * (r >> 2) + (r & 3);
+                s0[r] = off <= lim ? s0[r] : -INFINITY;
+                s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
             }
-        lsum = fmaf(lsum, alpha, psum);
+        }
+
+        // Row max over this lane's 32 scores as a chain of 3-input maxima.
+        float mx = fmaxf(fmaxf(s0[0], s1[0]), s0[1]);
+        mx = fmaxf(mx, s1[1]);
 #pragma unroll
-        for (int n = 0; n < ND; ++n) oacc[n] *= alpha;
+        for (int r = 2; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
+        mx = half_swap_max(mx);
+        const float mt = mx * c;
+        // Lazy rescaling: the reference max only moves when some row of the
+        // wave has grown by more than the threshold; the final O and L do not
+        // depend on the reference, only the size of the unnormalised weights.
+        if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleThreshold)) {
+            const float mnew = fmaxf(mref, mt);
+            const float alpha = mref == -INFINITY ? 0.f : fast_exp2(mref - mnew);
+            mref = mnew;
+            lsum *= alpha;
+#pragma unroll
+            for (int n = 0; n < ND; ++n) oacc[n] *= alpha;
+        }
+        const float mr = mref == -INFINITY ? 0.f : mref;
+
+        float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s0[r] = fast_exp2(fmaf(s0[r], c, -mr));
+            s1[r] = fast_exp2(fmaf(s1[r], c, -mr));
+            ps0 += s0[r];
+            ps1 += s1[r];
+        }
+        lsum += ps0 + ps1;
 
         // P^T as the B operand: k-step s4 covers keys 16*s4 .. 16*s4+15; lane
-        // half y, element e is key 16*s4 + 8*(e/4) + 4*y + e%4, which is score
-        // register 8*(s4%2) + e of block s4/2.
+        // half y, element e is key 16*s4 + 8*(e/4) + 4*y + e%4 = register
+        // 8*(s4%2) + e of block s4/2.
         bf16x8_t pb[4];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
+        for (int e = 0; e < 8; ++e) {
+            pb[0][e] = (__bf16)s0[e];
+            pb[1][e] = (__bf16)s0[8 + e];
+            pb[2][e] = (__bf16)s1[e];
+            pb[3][e] = (__bf16)s1[8 + e];
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[s4][e] = (__bf16)s[s4 >> 1][8 * (s4 & 1) + e];
-
+        for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
-        for (int n = 0; n < ND; ++n) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                bf16x8_t a = {};
-                if (D >= 32 || col < D)
-                    a = *(const bf16x8_t *)&vt_lds[buf][(32 * n + col) * VST + 16 * s4 + 8 * half];
+            for (int n = 0; n < ND; ++n) {
+                const unsigned char *va = vt + vaddr[D >= 32 ? n : 0] + 16 * s4 * L::ROWB;
+                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)va);
+                const bf16x4_t hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(va + 8 * L::ROWB));
+                bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                if (vzero) a = bf16x8_t{};
                 oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s4], oacc[n], 0, 0, 0);
             }
+        }
+    };
+
+    // One barrier per tile: after it, tile j is in LDS for every wave and every
+    // wave has finished reading the buffer that tile j+1 is loaded into.
+    stage_tile<D>(kbase, vbase, ks1, vs1, T, 0, wave, koff, voff, &lds[0][0][0], &lds[0][1][0]);
+    for (int j = 0; j < nkt; ++j) {
+        const int buf = j & 1;
+        __builtin_amdgcn_s_waitcnt(0);   // this lane's loads of tile j have landed
+        __syncthreads();
+        if (j + 1 < nkt)
+            stage_tile<D>(kbase, vbase, ks1, vs1, T, (j + 1) * BK, wave, koff, voff,
+                          &lds[buf ^ 1][0][0], &lds[buf ^ 1][1][0]);
+        const int key0 = j * BK;
+        const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
+        if (active) {
+            if (need_mask)
+                tile(BoolC<true>{}, j, buf);
+            else
+                tile(BoolC<false>{}, j, buf);
         }
     }
 
@@ -323,9 +382,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         }
     if (half == 0)
         p.lse[((long long)u.b * p.H + u.h) * T + qrow] =
-            lt > 0.f ? (mc + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+            lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
 }
-
 // ---------------------------------------------------------------------------
 // fp32 kernel: fp32 operands on fp32 MFMA (32x32x2), 32-key tiles. Weights stay
 // fp32 for P.V.
@@ -558,6 +616,11 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     const long long ek = extent(k_strides, B, T, H_kv, D), ev = extent(v_strides, B, T, H_kv, D);
     if (eq < 0 || eo < 0 || ek < 0 || ev < 0 || eq > kMaxOffset || eo > kMaxOffset ||
         ek > kMaxOffset || ev > kMaxOffset)
+        return FA_ERR_OVERFLOW;
+    // The bf16 kernel addresses one 64-key tile with 32-bit byte offsets.
+    if (dtype == FA_DTYPE_BF16 &&
+        (64 * 2 * (k_strides[1] > v_strides[1] ? k_strides[1] : v_strides[1]) + 2 * D >
+         (1LL << 31) - 1))
         return FA_ERR_OVERFLOW;
     const long long nq = (T + kBQ - 1) / kBQ;
     const long long nbh = (long long)B * H;

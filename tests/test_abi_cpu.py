@@ -151,3 +151,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_LIB_PATH", str(tmp_path / "missing" / "libfa.so"))
     with pytest.raises(RuntimeError, match="libfa.so not found"):
         fa.version()
+
+
+def test_no_unresolved_kernel_stubs(lib):
+    """Every kernel the host code launches has its launch stub in the library
+    (a kernel template the host pass silently failed to instantiate would leave
+    an undefined stub symbol and make dlopen fail at first use)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", os.path.join(ROOT, "exact_attention_91_amd", "libfa.so")],
+                         capture_output=True, text=True, check=True).stdout
+    assert not re.findall(r"\bU \S*device_stub\S*", out)
