@@ -16,7 +16,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          # NaN inputs are unsupported (documented in fa.h); without this every
          # fmaxf on an MFMA result gets an extra NaN-quieting copy.
-         "-fno-honor-nans"]
+         "-fno-honor-nans",
+         # Keep the hand-interleaved MFMA/VALU phases in source order: do not
+         # hoist instructions common to both arms of a branch above it.
+         "-mllvm", "-simplifycfg-hoist-common=false"]
 
 
 def build(verbose: bool = False, extra=()) -> str:

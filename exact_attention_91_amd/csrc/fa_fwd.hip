@@ -146,7 +146,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 family)
-constexpr float kRescaleThreshold = 8.0f;      // log2 units: weights stay <= 2^8
 
 // Issue this wave's share of the global->LDS copies of one K tile and one V
 // tile (buffer loads straight into LDS; rows past T read as zeros).
@@ -189,7 +188,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][L::TILEB];  // [buf][K,V]
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
     const Unit u = unit_of(p);
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
     f32x16_t oacc[ND];
 #pragma unroll
     for (int n = 0; n < ND; ++n) oacc[n] = f32x16_t{};
-    float mref = -INFINITY;  // reference max of this row, log2 domain (score * c)
+    float mref = -INFINITY;  // running row max, log2 domain (score * c)
     float lsum = 0.f;        // this lane's partial normaliser (its 16-key half)
     const float c = p.c;
     const bool wave_live = wq0 < T;
@@ -291,13 +291,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         for (int r = 2; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
         mx = half_swap_max(mx);
         const float mt = mx * c;
-        // Lazy rescaling: the reference max only moves when some row of the
-        // wave has grown by more than the threshold; the final O and L do not
-        // depend on the reference, only the size of the unnormalised weights.
-        if (__builtin_amdgcn_ballot_w64(mt > mref + kRescaleThreshold)) {
-            const float mnew = fmaxf(mref, mt);
-            const float alpha = mref == -INFINITY ? 0.f : fast_exp2(mref - mnew);
-            mref = mnew;
+        // Fold the tile into the running max. A row rescales its normaliser
+        // and output only when its own max grew; the wave-wide test just skips
+        // the multiply loop when no row of the wave grew (rows that did not
+        // grow multiply by exactly 1, so each row's result depends on its own
+        // scores alone). The reference stays the exact running max, so the
+        // largest weight of a row is exactly 1 and is not rounded when the
+        // weights go to bf16.
+        const bool grow = mt > mref;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float alpha =
+                grow ? (mref == -INFINITY ? 0.f : fast_exp2(mref - mt)) : 1.f;
+            mref = grow ? mt : mref;
             lsum *= alpha;
 #pragma unroll
             for (int n = 0; n < ND; ++n) oacc[n] *= alpha;
