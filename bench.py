@@ -2,8 +2,9 @@
 
 One step = one fa_fwd call over the whole workload (default: the GPT-2 124M
 attention layer, B=16 H=12 T=1024 D=64, BNHD, bf16, causal), inputs resident
-in HBM. W untimed warm-up steps, then K steps timed with HIP events on the
-stream the kernel is launched on, bracketed by device synchronisation.
+in HBM. W untimed warm-up steps (default 2000, so the GPU clock has settled),
+then K steps timed with HIP events on the stream the kernel is launched on,
+bracketed by device synchronisation.
 
 Counted FLOP per step: 4*B*H*T^2*D, halved when causal (the dense-contraction
 count; the masked upper triangle is not counted).
@@ -34,8 +35,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_gpt2_traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    # The GPU's clock takes several hundred back-to-back launches (tens of ms)
+    # to settle; shorter warm-ups time the ramp, not the kernel.
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="gpt2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,

@@ -25,13 +25,16 @@
 //    (lane, lane^32): row max/sum are in-lane reductions plus one
 //    v_permlane32_swap, and the rescale factor is a per-lane scalar.
 //  * The output is accumulated transposed too, O^T += V^T P^T: P^T is used as
-//    the B operand straight from the score registers (no LDS round trip); V is
-//    stored transposed in LDS with a key permutation that makes each lane's
-//    8 keys contiguous, so the A operand is one 16-byte LDS read.
+//    the B operand straight from the score registers (no LDS round trip). In
+//    the bf16 kernel V stays row-major in LDS and the V^T operand comes from
+//    transposing LDS reads (ds_read_b64_tr_b16); the fp32 kernel reads V^T
+//    element-wise from a padded row-major tile.
 //  * K/V tiles (64 keys, bf16; 32 keys, fp32) are double-buffered in LDS with
 //    the next tile's global loads issued before the current tile's math; one
-//    barrier per tile. LDS row strides are padded so the MFMA operand reads
-//    and the staging writes are bank-conflict free.
+//    barrier per tile. The bf16 kernel copies tiles straight from global
+//    memory into LDS (buffer loads to LDS) with XOR-permuted 16-byte chunks;
+//    the fp32 kernel stages through registers into padded rows. Either way
+//    the MFMA operand reads are bank-conflict free.
 //  * The scale is applied to fp32 scores (folded with log2 e into one FMA
 //    before exp2); q is never rescaled in its input precision. A negative scale
 //    flips q's sign bits in registers (exact) so the kernel always sees c > 0.
@@ -58,6 +61,7 @@ constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kBQ = 128;        // query rows per work-group (32 per wave)
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kMaxFloor = -1e30f;
 
 struct FwdParams {
     const void *q, *k, *v;
@@ -185,7 +189,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
     constexpr int ND = (D + 31) / 32;       // 32-row blocks of O^T
     constexpr int NV = D >= 32 ? D / 32 : 1;  // V^T address variants (one per block)
 
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2][2][L::TILEB];  // [buf][K,V]
+    // Two K/V buffers as four distinct LDS variables: the accesses of each loop
+    // step name their buffers statically, so the compiler knows the copies into
+    // one buffer never alias the operand reads of the other and does not make
+    // the reads wait for the copies.
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[L::TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -252,16 +263,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
     f32x16_t oacc[ND];
 #pragma unroll
     for (int n = 0; n < ND; ++n) oacc[n] = f32x16_t{};
-    float mref = -INFINITY;  // running row max, log2 domain (score * c)
+    // Running row max in the log2 domain (score * c); kMaxFloor stands for
+    // "no visible key yet" (fully masked keys give exp2(-inf) = 0 against it).
+    float mref = kMaxFloor;
     float lsum = 0.f;        // this lane's partial normaliser (its 16-key half)
-    const float c = p.c;
+    // The scale lives in a VGPR: a VOP3 FMA with an SGPR operand issues more
+    // slowly than one with three VGPR operands.
+    float c;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
     const bool wave_live = wq0 < T;
 
-    auto tile = [&](auto mask_tag, int j, int buf) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+    auto tile = [&](bool need_mask, int j, const unsigned char *kt, const unsigned char *vt) {
         const int key0 = j * BK;
-        const unsigned char *kt = &lds[buf][0][0];
-        const unsigned char *vt = &lds[buf][1][0];
 
         // S^T tile: 64 keys x 32 queries as two 32x32 blocks.
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
@@ -274,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         }
 
         // Element r of block kb is key key0 + 32kb + 8(r/4) + 4half + r%4.
-        if (MASK) {
+        if (need_mask) {
             const int lim = (CAUSAL ? min(qrow, T - 1) : T - 1) - key0 - 4 * half;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -291,23 +304,23 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         for (int r = 2; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
         mx = half_swap_max(mx);
         const float mt = mx * c;
-        // Fold the tile into the running max. A row rescales its normaliser
-        // and output only when its own max grew; the wave-wide test just skips
-        // the multiply loop when no row of the wave grew (rows that did not
-        // grow multiply by exactly 1, so each row's result depends on its own
-        // scores alone). The reference stays the exact running max, so the
-        // largest weight of a row is exactly 1 and is not rounded when the
-        // weights go to bf16.
-        const bool grow = mt > mref;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-            const float alpha =
-                grow ? (mref == -INFINITY ? 0.f : fast_exp2(mref - mt)) : 1.f;
-            mref = grow ? mt : mref;
+        // Fold the tile into the running max: rows whose max grew rescale
+        // their normaliser and output by exp2(m_old - m_new); the others are
+        // left alone (the branch is skipped when no row of the wave grew), so
+        // each row depends on its own scores alone. The reference stays the
+        // exact running max, so the largest weight of a row is exactly 1 and
+        // is not rounded when the weights go to bf16. mref starts at a finite
+        // floor, so the first visible tile gets alpha = 0 without -inf
+        // arithmetic.
+        const float mnew = fmaxf(mref, mt);
+        if (mnew > mref) {
+            const float alpha = fast_exp2(mref - mnew);
             lsum *= alpha;
 #pragma unroll
             for (int n = 0; n < ND; ++n) oacc[n] *= alpha;
         }
-        const float mr = mref == -INFINITY ? 0.f : mref;
+        mref = mnew;
+        const float mr = mref;
 
         float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -346,24 +359,23 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
     };
 
     // One barrier per tile: after it, tile j is in LDS for every wave and every
-    // wave has finished reading the buffer that tile j+1 is loaded into.
-    stage_tile<D>(kbase, vbase, ks1, vs1, T, 0, wave, koff, voff, &lds[0][0][0], &lds[0][1][0]);
-    for (int j = 0; j < nkt; ++j) {
-        const int buf = j & 1;
+    // wave has finished reading the buffer that tile j+1 is loaded into. The
+    // loop is unrolled by two so each step names its buffers statically.
+    auto step = [&](int j, const unsigned char *kt, const unsigned char *vt, unsigned char *kn,
+                    unsigned char *vn) {
         __builtin_amdgcn_s_waitcnt(0);   // this lane's loads of tile j have landed
         __syncthreads();
         if (j + 1 < nkt)
-            stage_tile<D>(kbase, vbase, ks1, vs1, T, (j + 1) * BK, wave, koff, voff,
-                          &lds[buf ^ 1][0][0], &lds[buf ^ 1][1][0]);
+            stage_tile<D>(kbase, vbase, ks1, vs1, T, (j + 1) * BK, wave, koff, voff, kn, vn);
         const int key0 = j * BK;
         const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
         const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
-        if (active) {
-            if (need_mask)
-                tile(BoolC<true>{}, j, buf);
-            else
-                tile(BoolC<false>{}, j, buf);
-        }
+        if (active) tile(need_mask, j, kt, vt);
+    };
+    stage_tile<D>(kbase, vbase, ks1, vs1, T, 0, wave, koff, voff, k_lds0, v_lds0);
+    for (int j = 0; j < nkt; j += 2) {
+        step(j, k_lds0, v_lds0, k_lds1, v_lds1);
+        if (j + 1 < nkt) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
 
     if (!wave_live) return;
@@ -469,7 +481,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
 #pragma unroll
     for (int n = 0; n < ND; ++n) oacc[n] = f32x16_t{};
     float mc = -INFINITY, lsum = 0.f;
-    const float c = p.c;
+    // The scale lives in a VGPR: a VOP3 FMA with an SGPR operand issues more
+    // slowly than one with three VGPR operands.
+    float c;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
     const bool wave_live = wq0 < T;
 
     load_tile(0);
