@@ -27,9 +27,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of MFMA peak (GPT-2 causal bf16 shape)"
-PEAK = {"bf16": 2500.0, "f32": 157.3}     # MI355X published dense MFMA, TFLOP/s
+PEAK = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA, TFLOP/s
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_91_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_gpt2_traffic.json")
+_ELEM = {"bf16": "__bf16", "f16": "_Float16"}   # element type of the 16-bit kernel
 
 
 def parse():
@@ -147,7 +148,9 @@ def main():
     peak = PEAK[w.dtype]
     roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
             "frac": tflops / peak, "traffic": traffic_for(w.name),
-            "kernel": f"fa_fwd_{w.dtype}_kernel<D={w.D},causal={int(causal)}>"}
+            "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}>"
+                       if w.dtype in _ELEM else
+                       f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
 
     cpu = None
     if not a.no_cpu_baseline:

@@ -56,6 +56,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kBQ = 128;        // query rows per work-group (32 per wave)
@@ -113,7 +115,8 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: bf16 operands, fp32 accumulation, 64-key tiles.
+// 16-bit kernel (bfloat16 or IEEE half operands, fp32 accumulation), 64-key
+// tiles.
 //
 // LDS layouts (one buffer; two buffers alternate between key tiles):
 //   K tile [64 keys][D], V tile [64 keys][D], rows of 2D bytes, unpadded. The
@@ -149,6 +152,35 @@ struct Bf16Layout {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));   // the builtin's type
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
+
+// The 16-bit kernel for bfloat16 and for IEEE half: operand vectors, the
+// 32x32x16 MFMA with fp32 accumulation, and the transposing LDS read.
+template <typename E>
+struct Half16;
+template <>
+struct Half16<__bf16> {
+    typedef bf16x8_t v8;
+    typedef bf16x4_t v4;
+    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static v4 read_tr(const unsigned char *p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)p);
+    }
+};
+template <>
+struct Half16<_Float16> {
+    typedef f16x8_t v8;
+    typedef f16x4_t v4;
+    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static v4 read_tr(const unsigned char *p) {
+        return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t *)p));
+    }
+};
 constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 family)
 
 // Issue this wave's share of the global->LDS copies of one K tile and one V
@@ -181,9 +213,12 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
     }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;
+    using H16 = Half16<E>;
+    typedef typename H16::v8 e8_t;
+    typedef typename H16::v4 e4_t;
     constexpr int BK = L::BK;
     constexpr int KS = D / 16;              // MFMA k-steps over the head dim
     constexpr int ND = (D + 31) / 32;       // 32-row blocks of O^T
@@ -215,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
 
     // Q fragment = B operand of S^T = K Q^T: lane (col, half) holds
     // q[qrow, 16*ks + 8*half + 0..7].
-    bf16x8_t qf[KS];
+    e8_t qf[KS];
     {
         const unsigned short *qr = (const unsigned short *)p.q + u.b * p.qs[0] +
                                    u.h * p.qs[2] + (long long)qrow * p.qs[1] + 8 * half;
@@ -224,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
             u32x4_t x = {0u, 0u, 0u, 0u};
             if (qrow < T) x = *(const u32x4_t *)(qr + 16 * ks);
             x ^= p.qsign;
-            qf[ks] = __builtin_bit_cast(bf16x8_t, x);
+            qf[ks] = __builtin_bit_cast(e8_t, x);
         }
     }
 
@@ -280,10 +315,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8_t a0 = *(const lds_bf16x8_t *)(kt + kaddr[ks]);
-            const bf16x8_t a1 = *(const lds_bf16x8_t *)(kt + kaddr[ks] + 32 * L::ROWB);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+            const e8_t a0 = __builtin_bit_cast(e8_t, *(const lds_bf16x8_t *)(kt + kaddr[ks]));
+            const e8_t a1 =
+                __builtin_bit_cast(e8_t, *(const lds_bf16x8_t *)(kt + kaddr[ks] + 32 * L::ROWB));
+            s0 = H16::mfma(a0, qf[ks], s0);
+            s1 = H16::mfma(a1, qf[ks], s1);
         }
 
         // Element r of block kb is key key0 + 32kb + 8(r/4) + 4half + r%4.
@@ -335,25 +371,24 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         // P^T as the B operand: k-step s4 covers keys 16*s4 .. 16*s4+15; lane
         // half y, element e is key 16*s4 + 8*(e/4) + 4*y + e%4 = register
         // 8*(s4%2) + e of block s4/2.
-        bf16x8_t pb[4];
+        e8_t pb[4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pb[0][e] = (__bf16)s0[e];
-            pb[1][e] = (__bf16)s0[8 + e];
-            pb[2][e] = (__bf16)s1[e];
-            pb[3][e] = (__bf16)s1[8 + e];
+            pb[0][e] = (E)s0[e];
+            pb[1][e] = (E)s0[8 + e];
+            pb[2][e] = (E)s1[e];
+            pb[3][e] = (E)s1[8 + e];
         }
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
             for (int n = 0; n < ND; ++n) {
                 const unsigned char *va = vt + vaddr[D >= 32 ? n : 0] + 16 * s4 * L::ROWB;
-                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)va);
-                const bf16x4_t hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(va + 8 * L::ROWB));
-                bf16x8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                if (vzero) a = bf16x8_t{};
-                oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s4], oacc[n], 0, 0, 0);
+                const e4_t lo = H16::read_tr(va);
+                const e4_t hi = H16::read_tr(va + 8 * L::ROWB);
+                e8_t a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                if (vzero) a = e8_t{};
+                oacc[n] = H16::mfma(a, pb[s4], oacc[n]);
             }
         }
     };
@@ -391,9 +426,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_bf16_kernel(FwdParams p) {
         for (int rg = 0; rg < 4; ++rg) {
             const int d = 32 * n + 8 * rg + 4 * half;
             if (D >= 32 || d < D) {
-                bf16x4_t o4;
+                e4_t o4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(oacc[n][4 * rg + e] * inv);
+                for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[n][4 * rg + e] * inv);
                 *(u32x2_t *)(orow + d) = __builtin_bit_cast(u32x2_t, o4);
             }
         }
@@ -589,7 +624,11 @@ bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 template <int D, bool CAUSAL>
 void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
     if (dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL>), grid, dim3(kThreads), 0, stream,
+                           p);
+    else if (dtype == FA_DTYPE_F16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL>), grid, dim3(kThreads), 0,
+                           stream, p);
     else
         hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
 }
@@ -611,7 +650,9 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
                               int dtype, const long long q_strides[3],
                               const long long k_strides[3], const long long v_strides[3],
                               const long long o_strides[3], void *stream) {
-    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_DTYPE;
+    const bool half16 = dtype != FA_DTYPE_F32;   // a 16-bit element type
     if (B < 0 || T < 0 || H < 1 || H_kv < 1) return FA_ERR_BAD_SHAPE;
     if (H % H_kv != 0) return FA_ERR_HEADS;
     if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
@@ -625,7 +666,7 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     for (int i = 0; i < 4; ++i)
         for (int j = 0; j < 3; ++j)
             if (st[i][j] < 0) return FA_ERR_STRIDE;
-    const long long vec = dtype == FA_DTYPE_BF16 ? 8 : 4;  // elements per 16 bytes
+    const long long vec = half16 ? 8 : 4;  // elements per 16 bytes
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
         !aligned(lse, 4))
         return FA_ERR_ALIGN;
@@ -638,7 +679,7 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
         ek > kMaxOffset || ev > kMaxOffset)
         return FA_ERR_OVERFLOW;
     // The bf16 kernel addresses one 64-key tile with 32-bit byte offsets.
-    if (dtype == FA_DTYPE_BF16 &&
+    if (half16 &&
         (64 * 2 * (k_strides[1] > v_strides[1] ? k_strides[1] : v_strides[1]) + 2 * D >
          (1LL << 31) - 1))
         return FA_ERR_OVERFLOW;
@@ -659,7 +700,7 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     // scale == 0 means uniform weights; the smallest normal c reproduces them
     // exactly in fp32 (every c*s rounds to a value whose exp2 is 1).
     p.c = c > 0.f ? c : 1.17549435e-38f;
-    p.qsign = scale < 0.f ? (dtype == FA_DTYPE_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+    p.qsign = scale < 0.f ? (half16 ? 0x80008000u : 0x80000000u) : 0u;
 
     const dim3 grid((unsigned)(nbh * nq));
     hipStream_t s = (hipStream_t)stream;
@@ -686,7 +727,7 @@ extern "C" const char *fa_status_str(int status) {
         case FA_ERR_BAD_SHAPE: return "bad shape: need B >= 0, T >= 0, H >= 1, H_kv >= 1";
         case FA_ERR_HEADS: return "H must be a multiple of H_kv";
         case FA_ERR_HEAD_DIM: return "head dim D must be 16, 32, 64 or 128";
-        case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_F32 or FA_DTYPE_BF16";
+        case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_F32, FA_DTYPE_BF16 or FA_DTYPE_F16";
         case FA_ERR_SCALE: return "scale must be finite (and |scale|*log2(e) finite)";
         case FA_ERR_ALIGN:
             return "misaligned: q/k/v/o need 16-byte alignment and 16-byte-multiple strides, "

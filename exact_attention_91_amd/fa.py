@@ -17,6 +17,7 @@ _LIB = None
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
 
 _I = ctypes.c_int
 _VP = ctypes.c_void_p
@@ -60,9 +61,11 @@ def status_str(code: int) -> str:
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return FA_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
     if t.dtype == torch.float32:
         return FA_DTYPE_F32
-    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
 def _check(q, k, v):

@@ -7,8 +7,8 @@ Recipe: numpy PCG64 seeded with SeedSequence(seed); spawn(3) children draw q, k,
 v with standard_normal in float64, shaped and drawn in memory order: q is
 [B, T, H, D], k and v are [B, T, H_kv, D]. q and k are multiplied by `qk_sigma`
 (4 for the multi-query workload, which pushes scores to large magnitude). The
-draws are rounded to float32 (round to nearest even) and, for bf16, on to
-bfloat16 (round to nearest even, by torch on the CPU). The float64 arrays handed
+draws are rounded to float32 (round to nearest even) and, for bf16 or f16, on to
+bfloat16 or IEEE half (round to nearest even, by torch on the CPU). The float64 arrays handed
 to the oracle are the exact values of those rounded device tensors.
 
 Workloads (shapes from the yelogs.com Flash Attention2-in-Triton article,
@@ -19,6 +19,7 @@ attention layer of "Flash Attention Memory Optimization Explained"):
   gpt2              B=16 H=12 T=1024 D=64  bf16 causal, scale 1/8
   long              B=8  H=1  T=8192 D=128 bf16 causal (oracle checks sampled rows)
   mqa               B=8  H=12 H_kv=1 T=4096 D=64 bf16 causal, q,k ~ N(0, 4^2)
+  gpt2_f16          the gpt2 workload in IEEE half (seed 1006)
 Seeds: 1001, 1020+D, 1003, 1004, 1005 respectively.
 """
 from dataclasses import dataclass
@@ -36,7 +37,7 @@ class Workload:
     H_kv: int
     T: int
     D: int
-    dtype: str          # "bf16" or "f32"
+    dtype: str          # "bf16", "f16" or "f32"
     causal: tuple       # mask settings this workload is run with
     seed: int
     qk_sigma: float = 1.0
@@ -63,6 +64,7 @@ WORKLOADS = {
     "gpt2": Workload("gpt2", 16, 12, 12, 1024, 64, "bf16", (True,), 1003),
     "long": Workload("long", 8, 1, 1, 8192, 128, "bf16", (True,), 1004),
     "mqa": Workload("mqa", 8, 12, 1, 4096, 64, "bf16", (True,), 1005, qk_sigma=4.0),
+    "gpt2_f16": Workload("gpt2_f16", 16, 12, 12, 1024, 64, "f16", (True,), 1006),
 }
 
 
@@ -79,6 +81,8 @@ class Inputs:
 def torch_dtype(dtype: str):
     if dtype == "bf16":
         return torch.bfloat16
+    if dtype == "f16":
+        return torch.float16
     if dtype == "f32":
         return torch.float32
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -28,7 +28,8 @@
  * with fp32 accumulation; scale applied to the fp32 scores (q is never
  * rescaled in bf16); softmax weights rounded to bf16 (nearest even) only as
  * the operand of P.V, while the normaliser sums the fp32 weights; o rounded to
- * nearest even. fp32 path: everything in fp32 (fp32 MFMA), no down-conversion.
+ * nearest even. fp16 path: the same with IEEE half in place of bfloat16.
+ * fp32 path: everything in fp32 (fp32 MFMA), no down-conversion.
  *
  * Layout. Elements are addressed with element strides (batch, token, head);
  * the head-dim stride is 1.
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_F16 = 2 } fa_dtype_t;
 
 typedef enum {
     FA_OK = 0,
@@ -84,7 +85,8 @@ typedef enum {
  *   lse  [B, H, T]        float32    written (natural-log logsumexp per row)
  *   causal: nonzero = key j visible to query i iff j <= i.
  *   scale:  any finite value, applied to q.k (1/sqrt(D) is the usual choice).
- *   dtype:  FA_DTYPE_BF16 or FA_DTYPE_F32 (applies to q, k, v and o).
+ *   dtype:  FA_DTYPE_BF16, FA_DTYPE_F16 or FA_DTYPE_F32 (applies to q, k, v
+ *           and o).
  *   stream: hipStream_t or NULL.
  * Returns an fa_status_t.
  */

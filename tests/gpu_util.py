@@ -6,8 +6,11 @@ import numpy as np
 import torch
 
 # Tolerances on max |GPU - oracle|: fp32 in/out 1e-4 on O and L; bf16 in with
-# fp32 accumulation 2e-2 on O and 1e-3 on L.
-TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3)}
+# fp32 accumulation 2e-2 on O and 1e-3 on L. fp16: 5e-3 on O, 1e-3 on L --
+# the weights are rounded to half (relative 2^-11) for P.V and O to half
+# (half an ulp is <= 2^-9 for |O| < 8), so |dO| stays below ~2^-9 + 8*2^-11
+# ~ 6e-3 in the worst case of a one-hot row with |v| ~ 4; L is computed in fp32.
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 1e-3), "f16": (5e-3, 1e-3)}
 
 
 def say(*a):

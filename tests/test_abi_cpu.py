@@ -88,7 +88,7 @@ def call_strided(lib, qs=(0, 0, 0), ks=(0, 0, 0), vs=(0, 0, 0), os_=(0, 0, 0), *
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=2), "FA_ERR_DTYPE"),
+    (dict(dtype=3), "FA_ERR_DTYPE"),
     (dict(dtype=-1), "FA_ERR_DTYPE"),
     (dict(B=-1), "FA_ERR_BAD_SHAPE"),
     (dict(T=-5), "FA_ERR_BAD_SHAPE"),

@@ -26,7 +26,7 @@ def _run(q, k, v, causal, scale=0.125):
     return o, lse
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_deterministic(dtype):
     x = generate(4, 6, 2, 777, 64, dtype, 301)
     q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
@@ -35,7 +35,7 @@ def test_deterministic(dtype):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("t0", [1, 64, 200, 511])
 def test_causal_future_independence(dtype, t0):
     """Changing K/V rows >= t0 leaves causal outputs of rows < t0 bitwise equal."""
@@ -52,7 +52,7 @@ def test_causal_future_independence(dtype, t0):
     assert not torch.equal(o1[:, t0:], o2[:, t0:])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("H_kv", [1, 2])
 def test_shared_kv_equals_expanded(dtype, H_kv):
     B, H, T, D = 2, 6, 333, 64
@@ -66,7 +66,7 @@ def test_shared_kv_equals_expanded(dtype, H_kv):
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_strided_bhtd_equals_contiguous(dtype):
     """[B, H, T, D] storage through fa_fwd_strided gives the same bits."""
     B, H, T, D = 2, 4, 250, 32
@@ -82,7 +82,7 @@ def test_strided_bhtd_equals_contiguous(dtype):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_guard_bands_untouched(dtype):
     """Only o and lse are written: sentinel memory around them stays intact."""
     B, H, T, D = 2, 3, 100, 64

@@ -25,7 +25,7 @@ def _need_gpu():
 SMALL_T = [1, 7, 63, 64, 65, 127, 129, 300, 1000]
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("T", SMALL_T)
@@ -39,7 +39,7 @@ def test_small_elementwise(dtype, D, causal, T):
     check_full(x, dtype, causal, scale, o, lse, "small")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("H,H_kv", [(4, 4), (6, 2), (8, 1)])
 def test_kv_head_groups(dtype, H, H_kv):
     B, T, D = 2, 200, 64
@@ -50,7 +50,7 @@ def test_kv_head_groups(dtype, H, H_kv):
         check_full(x, dtype, causal, 0.125, o, lse, f"groups causal={causal}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.9, 1e-3])
 def test_scale_values(dtype, scale):
     """Any finite scale: 0 gives uniform weights, negative flips the scores."""
@@ -91,8 +91,9 @@ def test_workload_batched(D):
     check_full(x, w.dtype, True, w.scale, o, lse, w.name)
 
 
-def test_workload_gpt2():
-    w = WORKLOADS["gpt2"]
+@pytest.mark.parametrize("name", ["gpt2", "gpt2_f16"])
+def test_workload_gpt2(name):
+    w = WORKLOADS[name]
     say(f"workload {w.name}")
     x = generate_workload(w)
     o, lse = run_gpu(x, True, w.scale)
