@@ -1,6 +1,7 @@
 """Benchmark: attention forward TFLOP/s on one MI355X, through the C ABI.
 
-One step = one fa_fwd call over the whole workload (default: the GPT-2 124M
+One step = one fa_fwd call (or, with --nsplit > 1, one fa_fwd_splitk call)
+over the whole workload (default: the GPT-2 124M
 attention layer, B=16 H=12 T=1024 D=64, BNHD, bf16, causal), inputs resident
 in HBM. W untimed warm-up steps (default 2000, so the GPU clock has settled),
 then K steps timed with HIP events on the stream the kernel is launched on,
@@ -41,6 +42,9 @@ def parse():
     # to settle; shorter warm-ups time the ramp, not the kernel.
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="gpt2")
+    ap.add_argument("--nsplit", type=int, default=1,
+                    help="> 1: time fa_fwd_splitk (key split into this many parts "
+                         "plus the logsumexp combine) instead of fa_fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle until this much wall time has passed")
@@ -97,10 +101,20 @@ def main():
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             w.B, w.H, w.H_kv, w.T, w.D, int(causal), w.scale, dcode, sp)
 
-    def step():
-        rc = lib.fa_fwd(*args)
-        if rc:
-            raise RuntimeError(fa.status_str(rc))
+    if a.nsplit > 1:
+        nbytes = fa.splitk_workspace_bytes(w.B, w.H, w.T, w.D, a.nsplit)
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+        sargs = args[:-1] + (a.nsplit, ws.data_ptr(), nbytes, sp)
+
+        def step():
+            rc = lib.fa_fwd_splitk(*sargs)
+            if rc:
+                raise RuntimeError(fa.status_str(rc))
+    else:
+        def step():
+            rc = lib.fa_fwd(*args)
+            if rc:
+                raise RuntimeError(fa.status_str(rc))
 
     if a.calib_copy_mib:
         n = a.calib_copy_mib * (1 << 20) // 4
@@ -148,9 +162,13 @@ def main():
     peak = PEAK[w.dtype]
     roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
             "frac": tflops / peak, "traffic": traffic_for(w.name),
-            "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}>"
-                       if w.dtype in _ELEM else
+            "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
+                       f"{str(a.nsplit > 1).lower()}>" if w.dtype in _ELEM else
                        f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
+    if a.nsplit > 1:
+        # one step = the split kernel plus the combine kernel; the rate is over both
+        roof["kernel"] += f" + fa_lse_combine_kernel<{_ELEM[w.dtype]}, {w.D}>"
+        roof["traffic"] = None
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -181,7 +199,8 @@ def main():
         "config": {"workload": f"{w.name}: B={w.B} H={w.H} H_kv={w.H_kv} T={w.T} D={w.D} "
                                f"BNHD {w.dtype} causal={causal}",
                    "B": w.B, "H": w.H, "H_kv": w.H_kv, "T": w.T, "D": w.D,
-                   "causal": causal, "layout": "BNHD", "parallelism": "single GPU"},
+                   "causal": causal, "layout": "BNHD", "parallelism": "single GPU",
+                   "nsplit": a.nsplit},
         "flop_per_step": flops,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -76,6 +76,12 @@ struct FwdParams {
     int nbh;        // B * H
     float c;        // |scale| * log2(e), > 0
     unsigned qsign; // XOR mask applied to q's bits (sign flip for scale < 0)
+    // Key-split mode: work-group id = (unit, split s); split s of a query tile
+    // covers key tiles [s*n/nsplit, (s+1)*n/nsplit) of its n, and writes its
+    // partial result, normalised over its own keys, to opart[s][b][h][t][:]
+    // (fp32) and its logsumexp to lpart[s][b][h][t].
+    int nsplit;
+    float *opart, *lpart;
 };
 
 // Cross-half (lane <-> lane^32) reductions of a per-lane value.
@@ -100,13 +106,18 @@ struct BoolC {
 // Work unit of this work-group: heaviest query tiles first (causal), then
 // (batch, head).
 struct Unit {
-    int b, h, g, q0;
+    int b, h, g, q0, s;
 };
 __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
-    const int id = blockIdx.x;
+    int id = blockIdx.x;
+    Unit u;
+    u.s = 0;
+    if (p.nsplit > 1) {
+        u.s = id % p.nsplit;
+        id /= p.nsplit;
+    }
     const int t = id / p.nbh;
     const int bh = id - t * p.nbh;
-    Unit u;
     u.b = bh / p.H;
     u.h = bh - u.b * p.H;
     u.g = u.h / p.group;
@@ -213,7 +224,7 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
     }
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
@@ -265,6 +276,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
 
     const int kend = CAUSAL ? min(T, u.q0 + kBQ) : T;
     const int nkt = (kend + BK - 1) / BK;
+    // Key tiles of this work-group: all of them, or split u.s's share.
+    const int jbeg = SPLIT ? u.s * nkt / p.nsplit : 0;
+    const int jend = SPLIT ? (u.s + 1) * nkt / p.nsplit : nkt;
 
     // Staging: this wave issues 1 KB loads wave, wave+4, ... of each tile.
     // Lane slot (row, physical chunk) -> global byte offset within the tile.
@@ -400,23 +414,44 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
                     unsigned char *vn) {
         __builtin_amdgcn_s_waitcnt(0);   // this lane's loads of tile j have landed
         __syncthreads();
-        if (j + 1 < nkt)
+        if (j + 1 < jend)
             stage_tile<D>(kbase, vbase, ks1, vs1, T, (j + 1) * BK, wave, koff, voff, kn, vn);
         const int key0 = j * BK;
         const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
         const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
         if (active) tile(need_mask, j, kt, vt);
     };
-    stage_tile<D>(kbase, vbase, ks1, vs1, T, 0, wave, koff, voff, k_lds0, v_lds0);
-    for (int j = 0; j < nkt; j += 2) {
+    if (jbeg < jend)
+        stage_tile<D>(kbase, vbase, ks1, vs1, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
+    for (int j = jbeg; j < jend; j += 2) {
         step(j, k_lds0, v_lds0, k_lds1, v_lds1);
-        if (j + 1 < nkt) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+        if (j + 1 < jend) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
     }
 
     if (!wave_live) return;
     const float lt = half_swap_sum(lsum);
     if (qrow >= T) return;
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+    const float lse_row = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    if (SPLIT) {
+        // Partial result over this split's keys, normalised by its own l.
+        const long long row = (((long long)u.s * p.B + u.b) * p.H + u.h) * T + qrow;
+        float *orow = p.opart + row * D;
+#pragma unroll
+        for (int n = 0; n < ND; ++n)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d = 32 * n + 8 * rg + 4 * half;
+                if (D >= 32 || d < D) {
+                    f32x4_t o4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o4[e] = oacc[n][4 * rg + e] * inv;
+                    *(f32x4_t *)(orow + d) = o4;
+                }
+            }
+        if (half == 0) p.lpart[row] = lse_row;
+        return;
+    }
     unsigned short *orow = (unsigned short *)p.o + u.b * p.os[0] + (long long)qrow * p.os[1] +
                            u.h * p.os[2];
     // O^T register r of block n is dim 32n + 8(r/4) + 4half + r%4 of this row.
@@ -432,9 +467,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
                 *(u32x2_t *)(orow + d) = __builtin_bit_cast(u32x2_t, o4);
             }
         }
-    if (half == 0)
-        p.lse[((long long)u.b * p.H + u.h) * T + qrow] =
-            lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    if (half == 0) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
 }
 // ---------------------------------------------------------------------------
 // fp32 kernel: fp32 operands on fp32 MFMA (32x32x2), 32-key tiles. Weights stay
@@ -603,6 +636,74 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Combine of partial results over disjoint key ranges. For every row,
+//   L = ln sum_s e^{L_s},  O = sum_s e^{L_s - L} O_s,
+// the same merge the online softmax applies between two key tiles ("Softmax
+// 的在線計算": rescale each partial by exp(m_s - m_new)). Rows with no key
+// in any part (all L_s = -inf) get O = 0 and L = -inf. Each thread handles
+// four consecutive dims of one row; parts are fp32 [n][B][H][T][D] and
+// [n][B][H][T]; o is written in its own dtype with element strides os.
+// ---------------------------------------------------------------------------
+struct CombineParams {
+    const float *opart, *lpart;
+    void *o;
+    float *lse;
+    long long os[3];
+    int n, B, H, T;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void fa_lse_combine_kernel(CombineParams p) {
+    constexpr int TPR = D / 4;                  // threads per row
+    const long long rows = (long long)p.B * p.H * p.T;
+    const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int d = 4 * (threadIdx.x % TPR);
+    if (row >= rows) return;
+    // One pass, merging part by part with a running max (the online-softmax
+    // update): every load is independent of the arithmetic, so the loads of
+    // an unrolled group are all in flight together.
+    const float *lp = p.lpart + row;
+    const float *op = p.opart + row * D + d;
+    float m = -INFINITY, l = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto merge = [&](float ls, f32x4_t os) __attribute__((always_inline)) {
+        if (ls > -INFINITY) {
+            const float mn = fmaxf(m, ls);
+            const float a = expf(m - mn), w = expf(ls - mn);
+            l = fmaf(l, a, w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(acc[e], a, w * os[e]);
+            m = mn;
+        }
+    };
+    int s = 0;
+    for (; s + 4 <= p.n; s += 4) {
+        float ls[4];
+        f32x4_t os[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ls[i] = lp[(s + i) * rows];
+            os[i] = *(const f32x4_t *)(op + (s + i) * rows * D);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) merge(ls[i], os[i]);
+    }
+    for (; s < p.n; ++s) merge(lp[s * rows], *(const f32x4_t *)(op + s * rows * D));
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float L = l > 0.f ? m + logf(l) : -INFINITY;
+    const int t = (int)(row % p.T);
+    const long long bh = row / p.T;
+    const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+    E *orow = (E *)p.o + b * p.os[0] + (long long)t * p.os[1] + h * p.os[2] + d;
+    typedef E e4v __attribute__((ext_vector_type(4)));
+    e4v o4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = (E)(acc[e] * inv);
+    *(e4v *)orow = o4;
+    if (d == 0) p.lse[row] = L;
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation (no HIP calls), dispatch, launch.
 // ---------------------------------------------------------------------------
 constexpr long long kMaxOffset = 1LL << 62;
@@ -621,35 +722,36 @@ long long extent(const long long s[3], int B, int T, int heads, int D) {
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
     if (dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL>), grid, dim3(kThreads), 0, stream,
-                           p);
-    else if (dtype == FA_DTYPE_F16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL>), grid, dim3(kThreads), 0,
+        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT>), grid, dim3(kThreads), 0,
                            stream, p);
-    else
+    else if (dtype == FA_DTYPE_F16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT>), grid, dim3(kThreads),
+                           0, stream, p);
+    else if (!SPLIT)
         hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool SPLIT>
 void launch_d(const FwdParams &p, int D, int dtype, dim3 grid, hipStream_t stream) {
     switch (D) {
-        case 16: launch<16, CAUSAL>(p, dtype, grid, stream); break;
-        case 32: launch<32, CAUSAL>(p, dtype, grid, stream); break;
-        case 64: launch<64, CAUSAL>(p, dtype, grid, stream); break;
-        default: launch<128, CAUSAL>(p, dtype, grid, stream); break;
+        case 16: launch<16, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
+        case 32: launch<32, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
+        case 64: launch<64, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
+        default: launch<128, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
     }
 }
 
-}  // namespace
-
-extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
-                              int B, int H, int H_kv, int T, int D, int causal, float scale,
-                              int dtype, const long long q_strides[3],
-                              const long long k_strides[3], const long long v_strides[3],
-                              const long long o_strides[3], void *stream) {
+// Validation shared by the entry points (no HIP calls) and the kernel
+// parameters. Sets *empty for B == 0 or T == 0 (a valid no-op).
+int prepare(const void *q, const void *k, const void *v, const void *o, const float *lse,
+            int B, int H, int H_kv, int T, int D, float scale, int dtype,
+            const long long q_strides[3], const long long k_strides[3],
+            const long long v_strides[3], const long long o_strides[3], FwdParams *pp,
+            bool *empty) {
+    *empty = false;
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
         return FA_ERR_DTYPE;
     const bool half16 = dtype != FA_DTYPE_F32;   // a 16-bit element type
@@ -659,7 +761,10 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     if (!isfinite(scale)) return FA_ERR_SCALE;
     float c = fabsf(scale) * kLog2e;
     if (!isfinite(c)) return FA_ERR_SCALE;
-    if (B == 0 || T == 0) return FA_OK;
+    if (B == 0 || T == 0) {
+        *empty = true;
+        return FA_OK;
+    }
     if (!q || !k || !v || !o || !lse || !q_strides || !k_strides || !v_strides || !o_strides)
         return FA_ERR_NULL_PTR;
     const long long *st[4] = {q_strides, k_strides, v_strides, o_strides};
@@ -678,7 +783,7 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     if (eq < 0 || eo < 0 || ek < 0 || ev < 0 || eq > kMaxOffset || eo > kMaxOffset ||
         ek > kMaxOffset || ev > kMaxOffset)
         return FA_ERR_OVERFLOW;
-    // The bf16 kernel addresses one 64-key tile with 32-bit byte offsets.
+    // The 16-bit kernel addresses one 64-key tile with 32-bit byte offsets.
     if (half16 &&
         (64 * 2 * (k_strides[1] > v_strides[1] ? k_strides[1] : v_strides[1]) + 2 * D >
          (1LL << 31) - 1))
@@ -687,8 +792,8 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     const long long nbh = (long long)B * H;
     if (nbh > kMaxGrid || nbh * nq > kMaxGrid || nbh * T > kMaxOffset) return FA_ERR_OVERFLOW;
 
-    FwdParams p;
-    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    FwdParams &p = *pp;
+    p.q = q; p.k = k; p.v = v; p.o = (void *)o; p.lse = (float *)lse;
     for (int j = 0; j < 3; ++j) {
         p.qs[j] = q_strides[j]; p.ks[j] = k_strides[j];
         p.vs[j] = v_strides[j]; p.os[j] = o_strides[j];
@@ -701,23 +806,151 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     // exactly in fp32 (every c*s rounds to a value whose exp2 is 1).
     p.c = c > 0.f ? c : 1.17549435e-38f;
     p.qsign = scale < 0.f ? (half16 ? 0x80008000u : 0x80000000u) : 0u;
+    p.nsplit = 1;
+    p.opart = p.lpart = nullptr;
+    return FA_OK;
+}
 
-    const dim3 grid((unsigned)(nbh * nq));
+void contiguous_strides(int T, int heads, int D, long long s[3]) {
+    s[0] = (long long)T * heads * D;
+    s[1] = (long long)heads * D;
+    s[2] = D;
+}
+
+// Bytes of split-K workspace: fp32 partial outputs then partial logsumexps;
+// -1 on overflow.
+long long splitk_bytes(int B, int H, int T, int D, int nsplit) {
+    long long rows, r;
+    if (__builtin_mul_overflow((long long)B * H, (long long)T, &rows) ||
+        __builtin_mul_overflow(rows, (long long)nsplit, &rows) ||
+        __builtin_mul_overflow(rows, (long long)(D + 1) * 4, &r))
+        return -1;
+    return r;
+}
+
+int launch_combine(const float *opart, const float *lpart, int n, int B, int H, int T, int D,
+                   void *o, const long long os[3], float *lse, int dtype, hipStream_t stream) {
+    CombineParams c;
+    c.opart = opart; c.lpart = lpart; c.o = o; c.lse = lse;
+    for (int j = 0; j < 3; ++j) c.os[j] = os[j];
+    c.n = n; c.B = B; c.H = H; c.T = T;
+    const long long rows = (long long)B * H * T;
+    const long long per_block = 256 / (D / 4);
+    const long long blocks = (rows + per_block - 1) / per_block;
+    if (blocks > kMaxGrid) return FA_ERR_OVERFLOW;
+    const dim3 grid((unsigned)blocks);
+#define FA_COMBINE(E, DD) \
+    hipLaunchKernelGGL((fa_lse_combine_kernel<E, DD>), grid, dim3(256), 0, stream, c)
+#define FA_COMBINE_D(E)                          \
+    switch (D) {                                 \
+        case 16: FA_COMBINE(E, 16); break;       \
+        case 32: FA_COMBINE(E, 32); break;       \
+        case 64: FA_COMBINE(E, 64); break;       \
+        default: FA_COMBINE(E, 128); break;      \
+    }
+    if (dtype == FA_DTYPE_BF16) {
+        FA_COMBINE_D(__bf16)
+    } else if (dtype == FA_DTYPE_F16) {
+        FA_COMBINE_D(_Float16)
+    } else {
+        FA_COMBINE_D(float)
+    }
+#undef FA_COMBINE_D
+#undef FA_COMBINE
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int B, int H, int H_kv, int T, int D, int causal, float scale,
+                              int dtype, const long long q_strides[3],
+                              const long long k_strides[3], const long long v_strides[3],
+                              const long long o_strides[3], void *stream) {
+    FwdParams p;
+    bool empty;
+    const int st = prepare(q, k, v, o, lse, B, H, H_kv, T, D, scale, dtype, q_strides, k_strides,
+                           v_strides, o_strides, &p, &empty);
+    if (st != FA_OK || empty) return st;
+    const dim3 grid((unsigned)((long long)p.nbh * p.nq));
     hipStream_t s = (hipStream_t)stream;
     if (causal)
-        launch_d<true>(p, D, dtype, grid, s);
+        launch_d<true, false>(p, D, dtype, grid, s);
     else
-        launch_d<false>(p, D, dtype, grid, s);
+        launch_d<false, false>(p, D, dtype, grid, s);
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                       int H, int H_kv, int T, int D, int causal, float scale, int dtype,
                       void *stream) {
-    const long long qs[3] = {(long long)T * H * D, (long long)H * D, D};
-    const long long ks[3] = {(long long)T * H_kv * D, (long long)H_kv * D, D};
+    long long qs[3], ks[3];
+    contiguous_strides(T, H, D, qs);
+    contiguous_strides(T, H_kv, D, ks);
     return fa_fwd_strided(q, k, v, o, lse, B, H, H_kv, T, D, causal, scale, dtype, qs, ks, ks,
                           qs, stream);
+}
+
+extern "C" long long fa_fwd_splitk_workspace_bytes(int B, int H, int T, int D, int nsplit) {
+    if (B < 0 || H < 1 || T < 0 || nsplit < 1 || (D != 16 && D != 32 && D != 64 && D != 128))
+        return -1;
+    return splitk_bytes(B, H, T, D, nsplit);
+}
+
+extern "C" int fa_fwd_splitk(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int B, int H, int H_kv, int T, int D, int causal, float scale,
+                             int dtype, int nsplit, void *workspace, long long workspace_bytes,
+                             void *stream) {
+    long long qs[3], ks[3];
+    contiguous_strides(T, H, D, qs);
+    contiguous_strides(T, H_kv, D, ks);
+    FwdParams p;
+    bool empty;
+    int st = prepare(q, k, v, o, lse, B, H, H_kv, T, D, scale, dtype, qs, ks, ks, qs, &p, &empty);
+    if (st != FA_OK) return st;
+    if (nsplit < 1) return FA_ERR_BAD_SHAPE;
+    if (dtype == FA_DTYPE_F32) return FA_ERR_DTYPE;   // key split runs on the 16-bit kernel
+    if (empty) return FA_OK;
+    if (nsplit == 1)
+        return fa_fwd_strided(q, k, v, o, lse, B, H, H_kv, T, D, causal, scale, dtype, qs, ks,
+                              ks, qs, stream);
+    const long long need = splitk_bytes(B, H, T, D, nsplit);
+    if (need < 0) return FA_ERR_OVERFLOW;
+    if (!workspace) return FA_ERR_NULL_PTR;
+    if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+    const long long units = (long long)p.nbh * p.nq;
+    if (units * nsplit > kMaxGrid) return FA_ERR_OVERFLOW;
+    const long long rows = (long long)B * H * T;
+    p.nsplit = nsplit;
+    p.opart = (float *)workspace;
+    p.lpart = p.opart + rows * nsplit * D;
+    const dim3 grid((unsigned)(units * nsplit));
+    hipStream_t s = (hipStream_t)stream;
+    if (causal)
+        launch_d<true, true>(p, D, dtype, grid, s);
+    else
+        launch_d<false, true>(p, D, dtype, grid, s);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    return launch_combine(p.opart, p.lpart, nsplit, B, H, T, D, o, qs, lse, dtype, s);
+}
+
+extern "C" int fa_lse_combine(const float *o_parts, const float *lse_parts, int n, int B, int H,
+                              int T, int D, void *o, float *lse, int dtype, void *stream) {
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_DTYPE;
+    if (n < 1 || B < 0 || H < 1 || T < 0) return FA_ERR_BAD_SHAPE;
+    if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if (B == 0 || T == 0) return FA_OK;
+    if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL_PTR;
+    if (!aligned(o_parts, 16) || !aligned(lse_parts, 4) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    if (splitk_bytes(B, H, T, D, n) < 0 || (long long)B * H * T * D > kMaxOffset)
+        return FA_ERR_OVERFLOW;
+    long long os[3];
+    contiguous_strides(T, H, D, os);
+    return launch_combine(o_parts, lse_parts, n, B, H, T, D, o, os, lse, dtype,
+                          (hipStream_t)stream);
 }
 
 extern "C" const char *fa_status_str(int status) {
@@ -735,6 +968,8 @@ extern "C" const char *fa_status_str(int status) {
         case FA_ERR_OVERFLOW: return "size overflow: offsets beyond 2^62 or grid beyond 2^24-1";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_STRIDE: return "negative stride";
+        case FA_ERR_WORKSPACE:
+            return "workspace smaller than fa_fwd_splitk_workspace_bytes() for these sizes";
         default: return "unknown status";
     }
 }

@@ -42,6 +42,13 @@ def _lib():
         lib.fa_fwd_strided.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
                                        [ctypes.c_float, _I] + [_LLP] * 4 + [_VP])
         lib.fa_fwd_strided.restype = _I
+        lib.fa_fwd_splitk.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
+                                      [ctypes.c_float, _I, _I, _VP, ctypes.c_longlong, _VP])
+        lib.fa_fwd_splitk.restype = _I
+        lib.fa_fwd_splitk_workspace_bytes.argtypes = [_I] * 5
+        lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
+        lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
+        lib.fa_lse_combine.restype = _I
         lib.fa_status_str.argtypes = [_I]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -88,7 +95,7 @@ def _raise(rc: int, fn: str):
 def fwd(q, k, v, causal: bool = False, scale=None):
     """Attention forward on BNHD-contiguous tensors.
 
-    q: [B, T, H, D], k and v: [B, T, H_kv, D] (bf16 or fp32, contiguous).
+    q: [B, T, H, D], k and v: [B, T, H_kv, D] (bf16, fp16 or fp32, contiguous).
     Returns (o [B, T, H, D] in q's dtype, lse [B, H, T] float32), where lse is
     the natural-log logsumexp of each row's scaled, masked scores.
     """
@@ -142,4 +149,64 @@ def fwd_strided(q, k, v, causal: bool = False, scale=None, out_layout: str = "bt
                                float(scale), _dtype_code(q), st(q), st(k), st(v), st(o),
                                stream)
     _raise(rc, "fa_fwd_strided")
+    return o, lse
+
+
+def splitk_workspace_bytes(B: int, H: int, T: int, D: int, nsplit: int) -> int:
+    """Bytes of device workspace fwd_splitk needs (-1 for invalid sizes)."""
+    return int(_lib().fa_fwd_splitk_workspace_bytes(B, H, T, D, nsplit))
+
+
+def fwd_splitk(q, k, v, causal: bool = False, scale=None, nsplit: int = 2, workspace=None):
+    """Split-K attention forward (bf16 or fp16, contiguous BNHD): every query
+    tile's keys are divided into `nsplit` ranges computed by separate
+    work-groups and merged by their logsumexps. Same result as fwd up to
+    rounding. `workspace` (optional): a device tensor of at least
+    splitk_workspace_bytes(...) bytes; allocated here when None.
+    Returns (o, lse) like fwd."""
+    _check(q, k, v)
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"fwd_splitk takes bfloat16 or float16 inputs, got {q.dtype}")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fwd_splitk needs contiguous [B,T,H,D] tensors")
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = splitk_workspace_bytes(B, H, T, D, nsplit)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = _lib().fa_fwd_splitk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, H_kv, T, D, int(bool(causal)),
+                              float(scale), _dtype_code(q), int(nsplit),
+                              workspace.data_ptr(), nbytes, stream)
+    _raise(rc, "fa_fwd_splitk")
+    return o, lse
+
+
+def lse_combine(o_parts, lse_parts, dtype=torch.bfloat16):
+    """Merge partial results over disjoint key ranges on the GPU.
+
+    o_parts: float32 [n, B, H, T, D], lse_parts: float32 [n, B, H, T]
+    (contiguous). Returns (o [B, T, H, D] in `dtype`, lse [B, H, T] float32)
+    with L = ln sum_s exp(L_s) and O = sum_s exp(L_s - L) O_s."""
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("o_parts and lse_parts must be float32")
+    if not (o_parts.is_cuda and lse_parts.is_cuda):
+        raise ValueError("o_parts and lse_parts must be GPU tensors")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    if o_parts.dim() != 5 or tuple(o_parts.shape[:4]) != tuple(lse_parts.shape):
+        raise ValueError("o_parts must be [n, B, H, T, D] and lse_parts [n, B, H, T]")
+    n, B, H, T, D = o_parts.shape
+    o = torch.empty((B, T, H, D), dtype=dtype, device=o_parts.device)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=o_parts.device)
+    stream = torch.cuda.current_stream(o_parts.device).cuda_stream
+    rc = _lib().fa_lse_combine(o_parts.data_ptr(), lse_parts.data_ptr(), n, B, H, T, D,
+                               o.data_ptr(), lse.data_ptr(), _dtype_code(o), stream)
+    _raise(rc, "fa_lse_combine")
     return o, lse

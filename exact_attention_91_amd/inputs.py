@@ -20,6 +20,8 @@ attention layer of "Flash Attention Memory Optimization Explained"):
   long              B=8  H=1  T=8192 D=128 bf16 causal (oracle checks sampled rows)
   mqa               B=8  H=12 H_kv=1 T=4096 D=64 bf16 causal, q,k ~ N(0, 4^2)
   gpt2_f16          the gpt2 workload in IEEE half (seed 1006)
+  gpt2_b2, long_b1  gpt2 at B=2 and long at B=1 (one GPU's share of a batch
+                    split over 8 GPUs), seeds 1007 and 1008
 Seeds: 1001, 1020+D, 1003, 1004, 1005 respectively.
 """
 from dataclasses import dataclass
@@ -65,6 +67,10 @@ WORKLOADS = {
     "long": Workload("long", 8, 1, 1, 8192, 128, "bf16", (True,), 1004),
     "mqa": Workload("mqa", 8, 12, 1, 4096, 64, "bf16", (True,), 1005, qk_sigma=4.0),
     "gpt2_f16": Workload("gpt2_f16", 16, 12, 12, 1024, 64, "f16", (True,), 1006),
+    # One GPU's share when the gpt2 and long workloads are split by batch over
+    # 8 GPUs: fewer work-groups than compute units (the key-split regime).
+    "gpt2_b2": Workload("gpt2_b2", 2, 12, 12, 1024, 64, "bf16", (True,), 1007),
+    "long_b1": Workload("long_b1", 1, 1, 1, 8192, 128, "bf16", (True,), 1008),
 }
 
 

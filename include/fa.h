@@ -74,7 +74,8 @@ typedef enum {
     FA_ERR_OVERFLOW = 8,   /* an element offset would exceed 2^62, or the grid
                               would exceed 2^24 - 1 work-groups                */
     FA_ERR_LAUNCH = 9,     /* the HIP runtime rejected the kernel launch       */
-    FA_ERR_STRIDE = 10     /* a negative stride                                */
+    FA_ERR_STRIDE = 10,    /* a negative stride                                */
+    FA_ERR_WORKSPACE = 11  /* split-K workspace smaller than required          */
 } fa_status_t;
 
 /*
@@ -97,14 +98,62 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * Same computation, with element strides {batch, token, head} for each of q,
  * k, v and o (head-dim stride 1). Lets callers pass [B, H, T, D] storage or
- * other views without a copy. Strides must be >= 0 and multiples of 8 (bf16)
- * or 4 (fp32) elements.
+ * other views without a copy. Strides must be >= 0 and multiples of 8 (bf16,
+ * fp16) or 4 (fp32) elements.
  */
 int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
                    int B, int H, int H_kv, int T, int D, int causal, float scale,
                    int dtype, const long long q_strides[3],
                    const long long k_strides[3], const long long v_strides[3],
                    const long long o_strides[3], void *stream);
+
+/*
+ * Split-K forward (the same result as fa_fwd up to rounding, for bf16 and
+ * fp16): the key tiles of every 128-row query tile are divided into nsplit
+ * contiguous ranges, each handled by its own work-group, so shapes with few
+ * (batch, head) pairs or long causal rows keep the GPU busy. Each range
+ * writes a partial result -- attention over its own keys, O_s normalised by
+ * its own sum, and L_s = ln of that sum of exp(scores), -inf for an empty
+ * range -- and a second kernel merges them:
+ *   L = ln sum_s exp(L_s),   O = sum_s exp(L_s - L) O_s,
+ * which is the online-softmax update of "Softmax 的在線計算" (yelogs.com Flash
+ * Attention2-in-Triton article) applied across ranges instead of tiles.
+ * Tensors as in fa_fwd (contiguous BNHD). nsplit >= 1; nsplit == 1 is fa_fwd
+ * (workspace unused). workspace: caller-owned device memory, 16-byte
+ * aligned, at least fa_fwd_splitk_workspace_bytes(B, H, T, D, nsplit) bytes;
+ * its contents are scratch (overwritten; calls sharing one workspace must be
+ * ordered on one stream). fp32 inputs return FA_ERR_DTYPE; a workspace too
+ * small returns FA_ERR_WORKSPACE. Two kernels are enqueued on `stream`.
+ * After the call the workspace holds the partials: float32 O_s
+ * [nsplit][B][H][T][D], then float32 L_s [nsplit][B][H][T]. Part s of the
+ * 128-row query tile starting at row q0 covers key tiles
+ * [s*n/nsplit, (s+1)*n/nsplit) (integer division) of 64 keys each, where
+ * n = ceil(kend/64), kend = min(T, q0 + 128) if causal else T.
+ */
+int fa_fwd_splitk(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int B, int H, int H_kv, int T, int D, int causal, float scale,
+                  int dtype, int nsplit, void *workspace, long long workspace_bytes,
+                  void *stream);
+
+/*
+ * Workspace bytes fa_fwd_splitk needs: nsplit * B * H * T * (D + 1) * 4
+ * (fp32 partial outputs, then fp32 partial logsumexps); -1 for invalid sizes
+ * or overflow.
+ */
+long long fa_fwd_splitk_workspace_bytes(int B, int H, int T, int D, int nsplit);
+
+/*
+ * Merge n partial results over disjoint key ranges (the combine step of
+ * fa_fwd_splitk, exposed for callers that split keys across devices):
+ *   o_parts   float32 [n][B][H][T][D]  read  (16-byte aligned)
+ *   lse_parts float32 [n][B][H][T]     read  (-inf marks an empty part)
+ *   o         [B, T, H, D] contiguous, dtype (bf16, fp16 or fp32), written
+ *   lse       float32 [B, H, T], written
+ * with L = ln sum_s exp(L_s) and O = sum_s exp(L_s - L) O_s per row; rows
+ * whose parts are all empty get O = 0, L = -inf.
+ */
+int fa_lse_combine(const float *o_parts, const float *lse_parts, int n, int B, int H,
+                   int T, int D, void *o, float *lse, int dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_str(int status);

@@ -16,6 +16,12 @@ attention_rows(..., rows)                the same for selected flat rows
 attention_online(..., chunk)             the online-softmax recurrence over key
                                          chunks (C), used to show it reaches the
                                          two-pass result.
+attention_range(..., lo, hi)             attention over keys [lo, hi) only,
+                                         normalised over them (C); partial
+                                         results for a key split.
+lse_combine(o_parts, lse_parts)          merge of partials over disjoint key
+                                         ranges: L = ln sum exp(L_s),
+                                         O = sum exp(L_s - L) O_s (C).
 brute_force(q, k, v, causal, scale)      pure Python, hand-expanded exponentials
                                          summed with math.fsum, no max
                                          subtraction; for T <= 8 only.
@@ -55,6 +61,12 @@ def _lib():
         lib.oracle_attn_rows_f64.restype = ctypes.c_int
         lib.oracle_attn_online_f64.argtypes = common + [_DP, _DP] + shape + [ctypes.c_int]
         lib.oracle_attn_online_f64.restype = ctypes.c_int
+        lib.oracle_attn_range_f64.argtypes = (common + [_DP, _DP] + shape +
+                                              [ctypes.c_int, ctypes.c_int])
+        lib.oracle_attn_range_f64.restype = ctypes.c_int
+        lib.oracle_lse_combine_f64.argtypes = [_DP, _DP, ctypes.c_int, ctypes.c_longlong,
+                                               ctypes.c_int, _DP, _DP]
+        lib.oracle_lse_combine_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _LIB = lib
@@ -125,6 +137,41 @@ def attention_online(q, k, v, causal: bool, scale: float, chunk: int):
                                        int(chunk))
     if rc:
         raise RuntimeError(f"oracle_attn_online_f64 failed ({rc})")
+    return o, lse
+
+
+def attention_range(q, k, v, causal: bool, scale: float, lo: int, hi: int):
+    """Attention over keys [lo, hi) only (intersected with the visible set),
+    normalised over those keys. Returns (o_part [B, H, T, D], lse_part
+    [B, H, T]); an empty range gives o_part = 0 and lse_part = -inf."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    o = np.empty((B, H, T, D), np.float64)
+    lse = np.empty((B, H, T), np.float64)
+    rc = _lib().oracle_attn_range_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      B, H, H_kv, T, D, int(bool(causal)), float(scale),
+                                      int(lo), int(hi))
+    if rc:
+        raise RuntimeError(f"oracle_attn_range_f64 failed ({rc})")
+    return o, lse
+
+
+def lse_combine(o_parts, lse_parts):
+    """Merge partials over disjoint key ranges. o_parts [n, ..., D] and
+    lse_parts [n, ...] (any common row shape). Returns (o [..., D], lse [...])."""
+    o_parts, lse_parts = _f64(o_parts), _f64(lse_parts)
+    n = o_parts.shape[0]
+    D = o_parts.shape[-1]
+    row_shape = lse_parts.shape[1:]
+    if o_parts.shape[:-1] != lse_parts.shape:
+        raise ValueError("o_parts must be lse_parts' shape plus a trailing D")
+    rows = int(np.prod(row_shape)) if row_shape else 1
+    o = np.empty(row_shape + (D,), np.float64)
+    lse = np.empty(row_shape, np.float64)
+    rc = _lib().oracle_lse_combine_f64(_ptr(o_parts), _ptr(lse_parts), n, rows, D,
+                                       _ptr(o), _ptr(lse))
+    if rc:
+        raise RuntimeError(f"oracle_lse_combine_f64 failed ({rc})")
     return o, lse
 
 

@@ -40,6 +40,14 @@
  * exp(m_old - m_new)), over key chunks of a caller-chosen size. It exists so a
  * test can show the recurrence reaches the two-pass result.
  *
+ * oracle_attn_range_f64 is the definition above with the visible set cut to a
+ * key range [lo, hi): output normalised over those keys only, L = ln of their
+ * sum of exp(s); an empty range gives O = 0, L = -inf. oracle_lse_combine_f64
+ * merges such partials over disjoint ranges: L = ln sum_s exp(L_s) (the max
+ * is subtracted before exponentiating), O = sum_s exp(L_s - L) O_s -- the
+ * same rescale-and-add the online recurrence applies between two chunks, with
+ * each chunk's own normaliser folded into exp(L_s).
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math, no BLAS).
  */
 #include <math.h>
@@ -222,6 +230,83 @@ int oracle_attn_online_f64(const double *q, const double *k, const double *v,
         free(p);
     }
     return fail ? -2 : 0;
+}
+
+/* Attention over keys [key_lo, key_hi) only. o_part [B, H, T, D] and
+ * lse_part [B, H, T] (row (b*H + h)*T + i). Returns 0, or -1 on bad shape. */
+int oracle_attn_range_f64(const double *q, const double *k, const double *v,
+                          double *o_part, double *lse_part,
+                          int B, int H, int H_kv, int T, int D, int causal, double scale,
+                          int key_lo, int key_hi) {
+    if (bad_args(B, H, H_kv, T, D)) return -1;
+    const long long nrows = (long long)B * H * T;
+    const int group = H / H_kv;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long long r = 0; r < nrows; ++r) {
+        const int i = (int)(r % T);
+        const int h = (int)((r / T) % H);
+        const int b = (int)(r / ((long long)T * H));
+        const int g = h / group;
+        const int nvis = causal ? i + 1 : T;
+        const int lo = key_lo < 0 ? 0 : key_lo;
+        const int hi = key_hi < nvis ? key_hi : nvis;
+        const double *qi = q + qidx(b, i, h, H, T, D);
+        double *orow = o_part + (size_t)r * D;
+        for (int d = 0; d < D; ++d) orow[d] = 0.0;
+        if (lo >= hi) {
+            lse_part[r] = -INFINITY;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int j = lo; j < hi; ++j) {
+            const double *kj = k + qidx(b, j, g, H_kv, T, D);
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+            if (scale * dot > m) m = scale * dot;
+        }
+        double z = 0.0;
+        for (int j = lo; j < hi; ++j) {
+            const double *kj = k + qidx(b, j, g, H_kv, T, D);
+            double dot = 0.0;
+            for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+            const double w = exp(scale * dot - m);
+            z += w;
+            const double *vj = v + qidx(b, j, g, H_kv, T, D);
+            for (int d = 0; d < D; ++d) orow[d] += w * vj[d];
+        }
+        for (int d = 0; d < D; ++d) orow[d] /= z;
+        lse_part[r] = m + log(z);
+    }
+    return 0;
+}
+
+/* Merge n partials: o_parts [n][rows][D], lse_parts [n][rows] -> o [rows][D],
+ * lse [rows]. Rows whose parts are all empty get o = 0, lse = -inf. */
+int oracle_lse_combine_f64(const double *o_parts, const double *lse_parts, int n,
+                           long long rows, int D, double *o, double *lse) {
+    if (n < 1 || rows < 0 || D < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (long long r = 0; r < rows; ++r) {
+        double m = -INFINITY;
+        for (int s = 0; s < n; ++s)
+            if (lse_parts[(size_t)s * rows + r] > m) m = lse_parts[(size_t)s * rows + r];
+        double *orow = o + (size_t)r * D;
+        for (int d = 0; d < D; ++d) orow[d] = 0.0;
+        if (m == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double z = 0.0;
+        for (int s = 0; s < n; ++s) z += exp(lse_parts[(size_t)s * rows + r] - m);
+        const double L = m + log(z);
+        for (int s = 0; s < n; ++s) {
+            const double w = exp(lse_parts[(size_t)s * rows + r] - L);
+            const double *op = o_parts + ((size_t)s * rows + r) * D;
+            for (int d = 0; d < D; ++d) orow[d] += w * op[d];
+        }
+        lse[r] = L;
+    }
+    return 0;
 }
 
 int oracle_num_threads(void) {

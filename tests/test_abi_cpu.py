@@ -24,7 +24,7 @@ def lib():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:\w+\s+)*\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
 
 
 def _enum_values(name):
@@ -38,7 +38,9 @@ DT = _enum_values("fa_dtype_t")
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_strided", "fa_status_str", "fa_version"]
+    assert _declared_functions() == ["fa_fwd", "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
+                                     "fa_fwd_strided", "fa_lse_combine", "fa_status_str",
+                                     "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -161,3 +163,64 @@ def test_no_unresolved_kernel_stubs(lib):
     out = subprocess.run(["nm", "-D", os.path.join(ROOT, "exact_attention_91_amd", "libfa.so")],
                          capture_output=True, text=True, check=True).stdout
     assert not re.findall(r"\bU \S*device_stub\S*", out)
+
+
+def call_splitk(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, T=100, D=64, causal=1,
+             scale=0.125, dtype=DT["FA_DTYPE_BF16"], nsplit=3, ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.fa_fwd_splitk(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                             a["H_kv"], a["T"], a["D"], a["causal"], a["scale"], a["dtype"],
+                             a["nsplit"], a["ws"], a["ws_bytes"], None)
+
+
+def test_splitk_workspace_bytes(lib):
+    f = lib.fa_fwd_splitk_workspace_bytes
+    assert f(2, 4, 100, 64, 3) == 3 * 2 * 4 * 100 * 65 * 4
+    assert f(16, 12, 1024, 128, 1) == 16 * 12 * 1024 * 129 * 4
+    assert f(0, 4, 100, 64, 2) == 0
+    assert f(2, 4, 100, 48, 2) == -1      # bad head dim
+    assert f(2, 4, 100, 64, 0) == -1      # bad split count
+    assert f(2, 0, 100, 64, 2) == -1
+    assert f(1 << 30, 1 << 30, 1 << 30, 128, 1 << 30) == -1   # overflow
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nsplit=0), "FA_ERR_BAD_SHAPE"),
+    (dict(dtype=DT["FA_DTYPE_F32"]), "FA_ERR_DTYPE"),      # split-K runs the 16-bit kernel
+    (dict(dtype=7), "FA_ERR_DTYPE"),
+    (dict(D=48), "FA_ERR_HEAD_DIM"),
+    (dict(H=6, H_kv=4), "FA_ERR_HEADS"),
+    (dict(scale=math.nan), "FA_ERR_SCALE"),
+    (dict(q=None), "FA_ERR_NULL_PTR"),
+    (dict(ws=None), "FA_ERR_NULL_PTR"),
+    (dict(ws_bytes=3 * 2 * 4 * 100 * 65 * 4 - 1), "FA_ERR_WORKSPACE"),
+    (dict(ws=P + 4), "FA_ERR_ALIGN"),
+    (dict(o=P + 8), "FA_ERR_ALIGN"),
+])
+def test_splitk_rejects(lib, kw, code):
+    assert call_splitk(lib, **kw) == ST[code]
+
+
+def test_splitk_empty_call_is_a_noop(lib):
+    assert call_splitk(lib, B=0, q=None, k=None, v=None, o=None, lse=None, ws=None,
+                       ws_bytes=0) == ST["FA_OK"]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), "FA_ERR_BAD_SHAPE"),
+    (dict(H=0), "FA_ERR_BAD_SHAPE"),
+    (dict(D=40), "FA_ERR_HEAD_DIM"),
+    (dict(dtype=9), "FA_ERR_DTYPE"),
+    (dict(op=None), "FA_ERR_NULL_PTR"),
+    (dict(lp=None), "FA_ERR_NULL_PTR"),
+    (dict(op=P + 4), "FA_ERR_ALIGN"),
+    (dict(o=P + 2), "FA_ERR_ALIGN"),
+    (dict(B=0, op=None, lp=None, o=None, lse=None), "FA_OK"),
+])
+def test_lse_combine_rejects(lib, kw, code):
+    a = dict(op=P, lp=P, n=2, B=2, H=4, T=100, D=64, o=P, lse=P, dtype=DT["FA_DTYPE_BF16"])
+    a.update(kw)
+    rc = lib.fa_lse_combine(a["op"], a["lp"], a["n"], a["B"], a["H"], a["T"], a["D"], a["o"],
+                            a["lse"], a["dtype"], None)
+    assert rc == ST[code]

@@ -247,3 +247,83 @@ def test_bad_shapes_rejected(oracle):
     q, k, v = _rand(1, 3, 2, 4, 4, seed=24)
     with pytest.raises(ValueError):
         oracle.attention(q, k, v, False, 1.0)
+
+
+# ----------------------------------------------------------- key-split partials
+
+def _partition(T, n, rng):
+    """n contiguous ranges covering [0, T) in order; some may be empty."""
+    cuts = np.sort(rng.integers(0, T + 1, size=n - 1))
+    return list(zip([0, *cuts], [*cuts, T]))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nparts", [1, 2, 3, 5])
+def test_p12_combined_ranges_equal_full_attention(oracle, causal, nparts):
+    """Attention is invariant to splitting the keys: partials over any
+    partition of [0, T), merged by L = ln sum e^{L_s}, O = sum e^{L_s-L} O_s,
+    give the two-pass result (up to float64 rounding)."""
+    B, H, H_kv, T, D = 2, 4, 2, 41, 16
+    q, k, v = _rand(B, H, H_kv, T, D, seed=30 + nparts)
+    o, lse = oracle.attention(q, k, v, causal, 0.3)
+    rng = np.random.default_rng(100 + nparts + 10 * causal)
+    for trial in range(3):
+        parts = [oracle.attention_range(q, k, v, causal, 0.3, a, b)
+                 for a, b in _partition(T, nparts, rng)]
+        oc, lc = oracle.lse_combine(np.stack([p[0] for p in parts]),
+                                    np.stack([p[1] for p in parts]))
+        np.testing.assert_allclose(oc.transpose(0, 2, 1, 3), o, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lc, lse, rtol=0, atol=1e-12)
+
+
+def test_p13_full_range_is_attention_and_single_key_range(oracle):
+    """The range [0, T) is the plain definition; a one-key range j gives
+    O = v_j and L = s_ij (for rows that can see key j)."""
+    B, H, H_kv, T, D = 1, 2, 1, 13, 8
+    q, k, v = _rand(B, H, H_kv, T, D, seed=40)
+    o, lse = oracle.attention(q, k, v, True, 0.7)
+    op, lp = oracle.attention_range(q, k, v, True, 0.7, 0, T)
+    np.testing.assert_allclose(op.transpose(0, 2, 1, 3), o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lp, lse, rtol=0, atol=1e-13)
+    j = 5
+    op, lp = oracle.attention_range(q, k, v, True, 0.7, j, j + 1)
+    for h in range(H):
+        for i in range(T):
+            if i >= j:
+                np.testing.assert_allclose(op[0, h, i], v[0, j, 0], rtol=0, atol=1e-15)
+                assert abs(lp[0, h, i] - 0.7 * float(q[0, i, h] @ k[0, j, 0])) < 1e-13
+            else:   # key j is in the future of row i: empty range
+                assert np.all(op[0, h, i] == 0.0) and lp[0, h, i] == -math.inf
+
+
+def test_p14_empty_parts_change_nothing(oracle):
+    """An empty range gives O = 0, L = -inf, and merging it in is a no-op."""
+    B, H, H_kv, T, D = 1, 2, 2, 9, 4
+    q, k, v = _rand(B, H, H_kv, T, D, seed=41)
+    oe, le = oracle.attention_range(q, k, v, False, 1.0, 4, 4)
+    assert np.all(oe == 0.0) and np.all(le == -math.inf)
+    pa = oracle.attention_range(q, k, v, False, 1.0, 0, 4)
+    pb = oracle.attention_range(q, k, v, False, 1.0, 4, 9)
+    o2, l2 = oracle.lse_combine(np.stack([pa[0], pb[0]]), np.stack([pa[1], pb[1]]))
+    o3, l3 = oracle.lse_combine(np.stack([pa[0], oe, pb[0]]), np.stack([pa[1], le, pb[1]]))
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+    oz, lz = oracle.lse_combine(np.stack([oe, oe]), np.stack([le, le]))
+    assert np.all(oz == 0.0) and np.all(lz == -math.inf)
+
+
+def test_p15_combine_hand_worked(oracle):
+    """Two parts with sums 2 and 6 of exp(scores): L = ln 8 and weights
+    2/8, 6/8 on their outputs; part order does not matter."""
+    o_parts = np.array([[[1.0, 0.0, 4.0]], [[0.0, 1.0, -4.0]]])
+    l_parts = np.array([[math.log(2.0)], [math.log(6.0)]])
+    o, l = oracle.lse_combine(o_parts, l_parts)
+    np.testing.assert_allclose(o, [[0.25, 0.75, -2.0]], rtol=0, atol=1e-15)
+    assert abs(l[0] - math.log(8.0)) < 1e-15
+    o_r, l_r = oracle.lse_combine(o_parts[::-1], l_parts[::-1])
+    np.testing.assert_allclose(o_r, o, rtol=0, atol=1e-15)
+    assert abs(l_r[0] - l[0]) < 1e-15
+    # large logsumexps: exp(800) overflows float64, so this only works with the
+    # max subtracted first (tolerance: 800 + ln 2 carries ~1e-13 of rounding)
+    o_big, l_big = oracle.lse_combine(o_parts, l_parts + 800.0)
+    np.testing.assert_allclose(o_big, o, rtol=0, atol=1e-11)
+    assert abs(l_big[0] - (800.0 + math.log(8.0))) < 1e-11
