@@ -22,7 +22,8 @@ attention layer of "Flash Attention Memory Optimization Explained"):
   gpt2_f16          the gpt2 workload in IEEE half (seed 1006)
   gpt2_b2, long_b1  gpt2 at B=2 and long at B=1 (one GPU's share of a batch
                     split over 8 GPUs), seeds 1007 and 1008
-Seeds: 1001, 1020+D, 1003, 1004, 1005 respectively.
+Seeds: 1001, 1020+D, 1003, 1004, 1005 respectively. The backward pass takes an
+upstream gradient dO drawn the same way from the fourth child of the same seed.
 """
 from dataclasses import dataclass
 import math
@@ -114,6 +115,14 @@ def generate(B, H, H_kv, T, D, dtype="bf16", seed=0, qk_sigma=1.0) -> Inputs:
     kt, k64 = _round(k, dtype)
     vt, v64 = _round(v, dtype)
     return Inputs(q64, k64, v64, qt, kt, vt)
+
+
+def generate_dout(B, H, T, D, dtype="bf16", seed=0):
+    """Upstream gradient dO [B, T, H, D] for the backward pass: standard
+    normals from the fourth child of SeedSequence(seed) (q, k, v use the
+    first three), rounded like the inputs. Returns (CPU tensor, float64)."""
+    gd = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(4)[3]))
+    return _round(gd.standard_normal((B, T, H, D)), dtype)
 
 
 def generate_workload(w: Workload) -> Inputs:

@@ -22,6 +22,10 @@ attention_range(..., lo, hi)             attention over keys [lo, hi) only,
 lse_combine(o_parts, lse_parts)          merge of partials over disjoint key
                                          ranges: L = ln sum exp(L_s),
                                          O = sum exp(L_s - L) O_s (C).
+attention_bwd(q, k, v, dout, causal, scale)
+                                         gradients (dq, dk, dv) of the same
+                                         definition for upstream gradient dO,
+                                         every intermediate recomputed (C).
 brute_force(q, k, v, causal, scale)      pure Python, hand-expanded exponentials
                                          summed with math.fsum, no max
                                          subtraction; for T <= 8 only.
@@ -32,7 +36,9 @@ Sources: the yelogs.com Flash Attention2-in-Triton article, sections
 position >= key position), "Softmax 的在線計算" (recurrence), "核心 Kernel 實現"
 (stored statistic m + ln l), "多查詢注意力（MQA）" (shared kv head); and
 "Flash Attention Memory Optimization Explained", "What is Flash Attention?"
-(the four naive steps).
+(the four naive steps), "Key Mechanisms" (backward checkpointing: the backward
+pass recomputes intermediates instead of storing them; its formulas are the
+chain rule of the naive steps).
 """
 import ctypes
 import math
@@ -67,6 +73,8 @@ def _lib():
         lib.oracle_lse_combine_f64.argtypes = [_DP, _DP, ctypes.c_int, ctypes.c_longlong,
                                                ctypes.c_int, _DP, _DP]
         lib.oracle_lse_combine_f64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_f64.argtypes = common + [_DP, _DP, _DP, _DP] + shape
+        lib.oracle_attn_bwd_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _LIB = lib
@@ -173,6 +181,24 @@ def lse_combine(o_parts, lse_parts):
     if rc:
         raise RuntimeError(f"oracle_lse_combine_f64 failed ({rc})")
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, causal: bool, scale: float):
+    """Gradients of attention for upstream gradient dout (same shape as q).
+    Returns (dq [B, T, H, D], dk, dv [B, T, H_kv, D]); dk and dv of a shared
+    kv head are summed over its query heads."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _lib().oracle_attn_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, H, H_kv, T, D, int(bool(causal)), float(scale))
+    if rc:
+        raise RuntimeError(f"oracle_attn_bwd_f64 failed ({rc})")
+    return dq, dk, dv
 
 
 def brute_force(q, k, v, causal: bool, scale: float):

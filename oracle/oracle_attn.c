@@ -48,6 +48,20 @@
  * same rescale-and-add the online recurrence applies between two chunks, with
  * each chunk's own normaliser folded into exp(L_s).
  *
+ * oracle_attn_bwd_f64 is the gradient of that definition, for a loss whose
+ * gradient with respect to O is dO (L is treated as an auxiliary output that
+ * the loss does not use). "Flash Attention Memory Optimization Explained",
+ * "Key Mechanisms" (backward checkpointing: the backward pass recomputes the
+ * forward's intermediates instead of reading them back) says what the method
+ * keeps, not the formulas; those are the chain rule applied to the four naive
+ * steps, written out here with every intermediate recomputed from q, k, v:
+ *     P_ij  = exp(s_ij - m_i) / Z_i                     (two-pass, as above)
+ *     dV_j += P_ij dO_i                  dP_ij = dO_i . v_j
+ *     dS_ij = P_ij (dP_ij - sum_{k in V_i} P_ik dP_ik)  (softmax Jacobian)
+ *     dQ_i  = scale sum_j dS_ij k_j      dK_j += scale dS_ij q_i
+ * with dK and dV of a kv head summed over the query heads that share it. It
+ * uses neither L nor the identity sum_k P_ik dP_ik = dO_i . O_i.
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math, no BLAS).
  */
 #include <math.h>
@@ -307,6 +321,82 @@ int oracle_lse_combine_f64(const double *o_parts, const double *lse_parts, int n
         lse[r] = L;
     }
     return 0;
+}
+
+/* Gradients of full attention. dout, dq: [B, T, H, D]; dk, dv: [B, T, H_kv, D]
+ * (overwritten). Parallel over (batch, kv head); each task owns the dk/dv rows
+ * of its kv head, so no two tasks write the same element. */
+int oracle_attn_bwd_f64(const double *q, const double *k, const double *v, const double *dout,
+                        double *dq, double *dk, double *dv,
+                        int B, int H, int H_kv, int T, int D, int causal, double scale) {
+    if (bad_args(B, H, H_kv, T, D)) return -1;
+    const int group = H / H_kv;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)T);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)T);
+        if (!p || !dp) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long long task = 0; task < (long long)B * H_kv; ++task) {
+                const int b = (int)(task / H_kv), g = (int)(task % H_kv);
+                for (int j = 0; j < T; ++j)
+                    for (int d = 0; d < D; ++d) {
+                        dk[qidx(b, j, g, H_kv, T, D) + d] = 0.0;
+                        dv[qidx(b, j, g, H_kv, T, D) + d] = 0.0;
+                    }
+                for (int h = g * group; h < (g + 1) * group; ++h)
+                    for (int i = 0; i < T; ++i) {
+                        const int nvis = causal ? i + 1 : T;
+                        const double *qi = q + qidx(b, i, h, H, T, D);
+                        const double *doi = dout + qidx(b, i, h, H, T, D);
+                        /* forward recomputed: scores, max, normaliser, P */
+                        double m = -INFINITY;
+                        for (int j = 0; j < nvis; ++j) {
+                            const double *kj = k + qidx(b, j, g, H_kv, T, D);
+                            double dot = 0.0;
+                            for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+                            p[j] = scale * dot;
+                            if (p[j] > m) m = p[j];
+                        }
+                        double z = 0.0;
+                        for (int j = 0; j < nvis; ++j) {
+                            p[j] = exp(p[j] - m);
+                            z += p[j];
+                        }
+                        for (int j = 0; j < nvis; ++j) p[j] /= z;
+                        /* dP and the softmax Jacobian's row term */
+                        double rowdot = 0.0;
+                        for (int j = 0; j < nvis; ++j) {
+                            const double *vj = v + qidx(b, j, g, H_kv, T, D);
+                            double dot = 0.0;
+                            for (int d = 0; d < D; ++d) dot += doi[d] * vj[d];
+                            dp[j] = dot;
+                            rowdot += p[j] * dot;
+                        }
+                        double *dqi = dq + qidx(b, i, h, H, T, D);
+                        for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+                        for (int j = 0; j < nvis; ++j) {
+                            const double ds = p[j] * (dp[j] - rowdot);
+                            const double *kj = k + qidx(b, j, g, H_kv, T, D);
+                            double *dkj = dk + qidx(b, j, g, H_kv, T, D);
+                            double *dvj = dv + qidx(b, j, g, H_kv, T, D);
+                            for (int d = 0; d < D; ++d) {
+                                dqi[d] += scale * ds * kj[d];
+                                dkj[d] += scale * ds * qi[d];
+                                dvj[d] += p[j] * doi[d];
+                            }
+                        }
+                    }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return fail ? -2 : 0;
 }
 
 int oracle_num_threads(void) {

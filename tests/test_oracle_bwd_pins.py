@@ -1,0 +1,208 @@
+"""Pins for the float64 oracle's attention gradients (oracle.attention_bwd).
+
+Each test checks the gradients against something other than the oracle's own
+formula: hand-worked values, central finite differences of the oracle's
+forward, torch's float64 autograd through the naive module, closed forms
+(one key, zero scale, constant values) and invariants of softmax attention
+(shifting every key by one vector changes nothing, so the key gradients sum to
+zero; the weights of a row sum to one, so the value gradients sum to the
+upstream gradients). Together they fail on a dropped Jacobian term, a wrong
+sign, a missing scale, a transposed operand, a wrong mask or kv-head map.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from exact_attention_91_amd.inputs import generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked_bwd.json")
+
+
+def _rand(B, H, H_kv, T, D, seed, sigma=1.0):
+    x = generate(B, H, H_kv, T, D, dtype="f32", seed=seed, qk_sigma=sigma)
+    rng = np.random.default_rng(seed + 99)
+    dout = rng.standard_normal(x.q64.shape)
+    return x.q64, x.k64, x.v64, dout
+
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_b1_hand_worked_golden(oracle, case):
+    B, H, H_kv, T, D = case["B"], case["H"], case["H_kv"], case["T"], case["D"]
+    q = np.array(case["q"], np.float64).reshape(B, T, H, D)
+    k = np.array(case["k"], np.float64).reshape(B, T, H_kv, D)
+    v = np.array(case["v"], np.float64).reshape(B, T, H_kv, D)
+    do = np.array(case["dout"], np.float64).reshape(B, T, H, D)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, case["causal"], case["scale"])
+    np.testing.assert_allclose(dq.ravel(), case["dq"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dk.ravel(), case["dk"], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv.ravel(), case["dv"], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(1, 1), (2, 1)])
+def test_b2_finite_differences(oracle, causal, H, H_kv):
+    """Central differences of loss = sum(O * dO) through the forward oracle."""
+    B, T, D = 1, 5, 3
+    scale = 0.7
+    q, k, v, do = _rand(B, H, H_kv, T, D, seed=201 + H)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, scale)
+
+    def loss(q, k, v):
+        o, _ = oracle.attention(q, k, v, causal, scale)
+        return float(np.sum(o * do))
+
+    h = 1e-5
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = args[name].copy(), args[name].copy()
+            xp[idx] += h
+            xm[idx] -= h
+            lp = loss(**dict(args, **{name: xp}))
+            lm = loss(**dict(args, **{name: xm}))
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=0, atol=2e-8, err_msg=name)
+
+
+def _torch_reference(q, k, v, do, causal, scale):
+    """torch float64 autograd through the naive module (scores, mask, softmax,
+    weighted sum), on the CPU."""
+    import torch
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    g = H // H_kv
+    tq = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    tk = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    tv = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    qh = tq.permute(0, 2, 1, 3)                                   # [B, H, T, D]
+    kh = tk.permute(0, 2, 1, 3).repeat_interleave(g, dim=1)       # [B, H, T, D]
+    vh = tv.permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    s = scale * torch.matmul(qh, kh.transpose(-1, -2).contiguous())
+    if causal:
+        mask = torch.triu(torch.ones(T, T, dtype=torch.bool), diagonal=1)
+        s = s.masked_fill(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = torch.matmul(p, vh).permute(0, 2, 1, 3)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (4, 2), (3, 1)])
+def test_b3_torch_autograd(oracle, causal, H, H_kv):
+    B, T, D = 2, 37, 16
+    q, k, v, do = _rand(B, H, H_kv, T, D, seed=300 + 10 * H + H_kv, sigma=1.5)
+    scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, scale)
+    rq, rk, rv = _torch_reference(q, k, v, do, causal, scale)
+    for name, a, b in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12, err_msg=name)
+
+
+def test_b4_single_key(oracle):
+    """T = 1: the weight is 1 whatever the score, so dQ = dK = 0 and dV is the
+    upstream gradient summed over the query heads of the kv head."""
+    q, k, v, do = _rand(2, 4, 2, 1, 8, seed=401)
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, 0.9)
+        assert np.all(dq == 0.0) and np.all(dk == 0.0)
+        expect = do.reshape(2, 1, 2, 2, 8).sum(axis=3)
+        np.testing.assert_allclose(dv, expect, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_b5_zero_scale(oracle, causal):
+    """scale = 0: uniform weights over the visible keys; dQ = dK = 0 and
+    dV_j = sum over rows i that see j of dO_i / (number of keys row i sees)."""
+    B, H, T, D = 1, 2, 9, 4
+    q, k, v, do = _rand(B, H, H, T, D, seed=501)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, 0.0)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    expect = np.zeros_like(v)
+    for h in range(H):
+        for i in range(T):
+            n = i + 1 if causal else T
+            for j in range(n):
+                expect[0, j, h] += do[0, i, h] / n
+    np.testing.assert_allclose(dv, expect, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_b6_invariants(oracle, causal):
+    """Adding one vector to every key leaves each row's softmax unchanged, so
+    the key gradients of a kv head sum to zero; each row's weights sum to 1, so
+    the value gradients sum to the upstream gradients of the head group."""
+    B, H, H_kv, T, D = 2, 6, 2, 31, 8
+    q, k, v, do = _rand(B, H, H_kv, T, D, seed=601, sigma=2.0)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, 0.35)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, rtol=0, atol=1e-12)
+    do_groups = do.reshape(B, T, H_kv, H // H_kv, D).sum(axis=3).sum(axis=1)
+    np.testing.assert_allclose(dv.sum(axis=1), do_groups, rtol=0, atol=1e-12)
+
+
+def test_b7_constant_values(oracle):
+    """All value rows equal: O does not depend on the weights, so dQ = dK = 0."""
+    B, H, T, D = 1, 2, 11, 4
+    q, k, _, do = _rand(B, H, H, T, D, seed=701)
+    v = np.broadcast_to(np.array([0.5, -1.0, 2.0, 0.25]), (B, T, H, D)).copy()
+    for causal in (False, True):
+        dq, dk, _ = oracle.attention_bwd(q, k, v, do, causal, 0.6)
+        np.testing.assert_allclose(dq, 0.0, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dk, 0.0, rtol=0, atol=1e-13)
+
+
+def test_b8_linear_in_upstream_gradient(oracle):
+    B, H, T, D = 1, 2, 13, 8
+    q, k, v, do1 = _rand(B, H, 1, T, D, seed=801)
+    do2 = np.random.default_rng(802).standard_normal(do1.shape)
+    g1 = oracle.attention_bwd(q, k, v, do1, True, 0.4)
+    g2 = oracle.attention_bwd(q, k, v, do2, True, 0.4)
+    g3 = oracle.attention_bwd(q, k, v, 2.0 * do1 - 3.0 * do2, True, 0.4)
+    for a, b, c in zip(g1, g2, g3):
+        np.testing.assert_allclose(c, 2.0 * a - 3.0 * b, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_b9_shared_kv_head_equals_expanded(oracle, causal):
+    """A kv head shared by 3 query heads gets the sum of the gradients the
+    three would get from private copies."""
+    B, H, H_kv, T, D = 1, 6, 2, 17, 8
+    q, k, v, do = _rand(B, H, H_kv, T, D, seed=901)
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, 0.3)
+    ke = np.repeat(k, 3, axis=2)
+    ve = np.repeat(v, 3, axis=2)
+    eq, ek, ev = oracle.attention_bwd(q, ke, ve, do, causal, 0.3)
+    np.testing.assert_array_equal(dq, eq)
+    np.testing.assert_allclose(dk, ek.reshape(B, T, H_kv, 3, D).sum(axis=3), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(dv, ev.reshape(B, T, H_kv, 3, D).sum(axis=3), rtol=0, atol=1e-13)
+
+
+def test_b10_causal_future_independence(oracle):
+    """Causal: dQ of row i depends only on positions <= i, so changing q, k, v
+    and dO at the last position leaves dQ of every earlier row unchanged."""
+    B, H, T, D = 1, 2, 12, 4
+    q, k, v, do = _rand(B, H, H, T, D, seed=1001)
+    dq, _, _ = oracle.attention_bwd(q, k, v, do, True, 0.5)
+    q2, k2, v2, do2 = q.copy(), k.copy(), v.copy(), do.copy()
+    for x in (q2, k2, v2, do2):
+        x[:, -1] += 3.0
+    dq2, _, _ = oracle.attention_bwd(q2, k2, v2, do2, True, 0.5)
+    np.testing.assert_array_equal(dq[:, :-1], dq2[:, :-1])
+
+
+def test_bwd_bad_shapes_rejected(oracle):
+    q = np.zeros((1, 4, 3, 8))
+    k = np.zeros((1, 4, 2, 8))
+    with pytest.raises(ValueError):
+        oracle.attention_bwd(q, k, k, q, False, 1.0)
+    with pytest.raises(ValueError):
+        oracle.attention_bwd(q, q, q, np.zeros((1, 4, 3, 4)), False, 1.0)
