@@ -1,0 +1,613 @@
+// fa_bwd.hip -- attention backward for MI355X (gfx950), and its C ABI
+// (fa_bwd, fa_bwd_workspace_bytes in include/fa.h).
+//
+// Method: "Flash Attention Memory Optimization Explained" (lzwjava.github.io),
+// "Key Mechanisms", backward checkpointing -- the backward pass recomputes the
+// forward's intermediates (scores, weights) from q, k and the stored
+// per-row logsumexp L instead of keeping the T x T matrices. The gradients are
+// the chain rule of the forward's definition:
+//   P = exp(scale QK^T - L),  dV = P^T dO,  dP = dO V^T,
+//   dS = P o (dP - Delta),  Delta_i = dO_i . O_i,  dQ = scale dS K,  dK = scale dS^T Q.
+//
+// gfx950 design (three kernels on one stream, no atomics, deterministic):
+//  * fa_bwd_pre_kernel: Delta = rowsum(dO o O) and L2 = L log2(e) per row,
+//    into the caller's workspace (HBM-bound, one pass over O and dO).
+//  * fa_bwd_dkdv_kernel: one work-group per 128-key tile of one (batch, kv
+//    head); each wave keeps its 32 keys' K and V rows in registers as MFMA
+//    operands and its dK, dV accumulators in registers for the whole loop,
+//    and streams 64-row tiles of Q, dO (and their L2, Delta) of every query
+//    head of the group through double-buffered LDS. Scores are computed as
+//    S = Q K^T, so a lane owns one key column: P and dS feed the B operand of
+//    dV^T += dO^T P and dK^T += Q^T dS straight from registers, with dO^T and
+//    Q^T read from the same LDS tiles by transposing reads.
+//  * fa_bwd_dq_kernel: the forward's decomposition (one work-group per
+//    128-row query tile, heaviest causal tiles first); each wave keeps its 32
+//    query rows of Q and dO in registers, streams K and V tiles, computes
+//    S^T = K Q^T and dP^T = V dO^T, and accumulates dQ^T += K^T dS^T with K^T
+//    from transposing reads of the K tile.
+//  Tiles read both as rows and transposed use the dual swizzle (dswz) of
+//  fa_device.h. Causal: key tiles wholly after a query tile are never loaded;
+//  query tiles wholly before a key tile are never loaded; waves skip the math
+//  of blocks wholly masked; only blocks that touch the diagonal or the ragged
+//  end T are masked element-wise.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_device.h"
+
+namespace {
+
+constexpr int kBlk = 128;   // query rows (dQ) or keys (dK/dV) per work-group
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
+
+struct BwdParams {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    float *delta, *l2;      // workspace, [B][H][T] each
+    int B, H, H_kv, T;
+    int group;              // H / H_kv
+    int nblk;               // 128-row tiles per sequence
+    float c;                // scale * log2(e) (signed)
+    float scale;
+};
+
+// ---------------------------------------------------------------------------
+// Delta_i = sum_d dO[i,d] O[i,d] (fp32) and L2_i = L_i log2(e), per row
+// (b, h, t), stored at (b*H + h)*T + t. D/8 threads per row, 8 elements each.
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
+    using H16 = Half16<E>;
+    typedef typename H16::v8 e8_t;
+    constexpr int TPR = D / 8;
+    const long long rows = (long long)p.B * p.H * p.T;
+    const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int part = threadIdx.x % TPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const int t = (int)(row % p.T);
+        const long long bh = row / p.T;
+        const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+        const long long off = (((long long)b * p.T + t) * p.H + h) * D + 8 * part;
+        const e8_t ov = __builtin_bit_cast(e8_t, *(const u32x4_t *)((const unsigned short *)p.o + off));
+        const e8_t dv =
+            __builtin_bit_cast(e8_t, *(const u32x4_t *)((const unsigned short *)p.dout + off));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)ov[e], (float)dv[e], acc);
+    }
+    // TPR consecutive lanes hold one row (TPR divides the wave size).
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (row < rows && part == 0) {
+        p.delta[row] = acc;
+        p.l2[row] = p.lse[row] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV. Work-group: keys [k0, k0 + 128) of kv head g of batch b, wave w
+// owns keys wk0 = k0 + 32w .. wk0 + 31 (lane col = key wk0 + col).
+// Query tiles: 64 rows; LDS holds Q and dO tiles (dual swizzle) and the
+// tile's L2 and Delta (64 floats each), two buffers alternating.
+// In the 32x32 accumulator layout of S = Q K^T (a 32-query block x 32 keys),
+// lane (col, half) register r is query 8(r/4) + 4half + r%4 of the block and
+// key col: the B operand of the 32-query reduction for k-step s2 is
+// registers 8 s2 .. 8 s2 + 7, whose queries 16 s2 + 8(e/4) + 4half + e%4 are
+// exactly the rows the transposing reads of dO^T / Q^T hand lane (d, half).
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
+    using L = Bf16Layout<D>;
+    using H16 = Half16<E>;
+    typedef typename H16::v8 e8_t;
+    typedef typename H16::v4 e4_t;
+    constexpr int BQ = L::BK;               // 64 query rows per staged tile
+    constexpr int KS = D / 16;              // k-steps over the head dim
+    constexpr int ND = (D + 31) / 32;       // 32-row blocks of dK^T / dV^T
+    constexpr int NV = D >= 32 ? D / 32 : 1;
+    constexpr int NI = (L::NLOAD + 3) / 4;
+
+    __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char o_lds0[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char o_lds1[L::TILEB];
+    __shared__ __attribute__((aligned(16))) float st_lds0[2 * BQ];   // L2 then Delta
+    __shared__ __attribute__((aligned(16))) float st_lds1[2 * BQ];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int T = p.T;
+    const int nbg = p.B * p.H_kv;
+    const int tk = blockIdx.x / nbg;          // key tile; tile 0 (most work) first
+    const int bg = blockIdx.x - tk * nbg;
+    const int b = bg / p.H_kv, g = bg - b * p.H_kv;
+    const int k0 = tk * kBlk;
+    const int wk0 = k0 + 32 * wave;
+    const int key = wk0 + col;
+    const bool wave_live = wk0 < T;
+    const long long qrs = (long long)p.H * D;      // row stride of q, o, dout, dq
+    const long long krs = (long long)p.H_kv * D;   // row stride of k, v, dk, dv
+
+    // K and V rows of this lane's key as B operands: lane (col, half) holds
+    // dims 16 ks + 8 half + 0..7.
+    e8_t kf[KS], vf[KS];
+    {
+        const long long off = ((long long)b * T + key) * krs + (long long)g * D + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+            if (key < T) {
+                x = *(const u32x4_t *)((const unsigned short *)p.k + off + 16 * ks);
+                y = *(const u32x4_t *)((const unsigned short *)p.v + off + 16 * ks);
+            }
+            kf[ks] = __builtin_bit_cast(e8_t, x);
+            vf[ks] = __builtin_bit_cast(e8_t, y);
+        }
+    }
+
+    // Staging offsets: row within the tile and physical chunk of each lane.
+    int qoff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int idx = wave + 4 * i;
+        const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
+        qoff[i] = row * (int)qrs * 2 + 16 * ((lane % L::C) ^ L::dswz(row));
+    }
+    // Row reads (A operand of S = Q K^T and dP = dO V^T): lane (col, half)
+    // reads row col (+32 for the second block), dims 16 ks + 8 half + 0..7.
+    int raddr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        raddr[ks] = col * L::ROWB + 16 * ((2 * ks + half) ^ L::dswz(col));
+    // Transposing reads (A operand dO^T / Q^T): rows r0 and r0 + 8 of each
+    // 16-row step, dims 32 n + dl .. + 3.
+    int taddr[NV], taddr8[NV];
+    {
+        const int r0 = 4 * half + ((lane & 15) >> 2);
+        const int dl = (D >= 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int d = 32 * n + dl;
+            taddr[n] = r0 * L::ROWB + 16 * ((d >> 3) ^ L::dswz(r0)) + 2 * (d & 7);
+            taddr8[n] = (r0 + 8) * L::ROWB + 16 * ((d >> 3) ^ L::dswz(r0 + 8)) + 2 * (d & 7);
+        }
+    }
+    const bool tzero = D < 32 && col >= D;   // D=16: rows 16..31 of dO^T / Q^T are zero
+
+    f32x16_t dkacc[ND], dvacc[ND];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+        dkacc[n] = f32x16_t{};
+        dvacc[n] = f32x16_t{};
+    }
+    float c;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
+
+    // Query tiles: every query head of the group, tiles that reach this key
+    // tile (causal: rows >= k0).
+    const int nqt_all = (T + BQ - 1) / BQ;
+    const int i_beg = CAUSAL ? k0 / BQ : 0;
+    const int nqt = nqt_all - i_beg;
+    const int nit = p.group * nqt;
+
+    auto stage = [&](int it, unsigned char *qd, unsigned char *od, float *sd)
+        __attribute__((always_inline)) {
+        const int h = g * p.group + it / nqt;
+        const int q0 = (i_beg + it % nqt) * BQ;
+        const long long hoff = (long long)b * T * qrs + (long long)h * D;
+        stage_tile<D>((const unsigned short *)p.q + hoff, (const unsigned short *)p.dout + hoff,
+                      qrs, qrs, T, q0, wave, qoff, qoff, qd, od);
+        if (wave < 2) {
+            const long long r = ((long long)b * p.H + h) * T + q0;
+            const float *src = (wave == 0 ? p.l2 : p.delta) + r;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(src), (short)0, min(T - q0, BQ) * 4, kRsrcWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sd + BQ * wave), 4,
+                                                     lane * 4, 0, 0, 0);
+        }
+    };
+
+    auto compute = [&](int it, const unsigned char *qt, const unsigned char *ot, const float *st)
+        __attribute__((always_inline)) {
+        const int q0 = (i_beg + it % nqt) * BQ;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int n0 = q0 + 32 * sub;
+            if (n0 >= T || (CAUSAL && n0 + 31 < wk0)) continue;   // wave-uniform
+            const bool need_mask = (CAUSAL && n0 < wk0 + 31) || (wk0 + 31 >= T);
+            f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const e8_t a = __builtin_bit_cast(
+                    e8_t, *(const lds_bf16x8_t *)(qt + raddr[ks] + 32 * sub * L::ROWB));
+                const e8_t a2 = __builtin_bit_cast(
+                    e8_t, *(const lds_bf16x8_t *)(ot + raddr[ks] + 32 * sub * L::ROWB));
+                s = H16::mfma(a, kf[ks], s);
+                dp = H16::mfma(a2, vf[ks], dp);
+            }
+            // P and dS; register r is query n0 + 8(r/4) + 4half + r%4.
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4_t l4 = *(const lds_f32x4_t *)(st + 32 * sub + 8 * gq + 4 * half);
+                const f32x4_t d4 = *(const lds_f32x4_t *)(st + BQ + 32 * sub + 8 * gq + 4 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * gq + e;
+                    const float pr = fast_exp2(fmaf(s[r], c, -l4[e]));
+                    s[r] = pr;
+                    dp[r] = pr * (dp[r] - d4[e]);
+                }
+            }
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qn = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const bool ok = key < T && (!CAUSAL || key <= qn);
+                    s[r] = ok ? s[r] : 0.f;
+                    dp[r] = ok ? dp[r] : 0.f;
+                }
+            }
+            e8_t pb[2], sb[2];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[0][e] = (E)s[e];
+                pb[1][e] = (E)s[8 + e];
+                sb[0][e] = (E)dp[e];
+                sb[1][e] = (E)dp[8 + e];
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int ro = (32 * sub + 16 * s2) * L::ROWB;
+#pragma unroll
+                for (int n = 0; n < ND; ++n) {
+                    const int tn = D >= 32 ? n : 0;
+                    e8_t ao = __builtin_shufflevector(H16::read_tr(ot + taddr[tn] + ro),
+                                                      H16::read_tr(ot + taddr8[tn] + ro), 0, 1, 2,
+                                                      3, 4, 5, 6, 7);
+                    e8_t aq = __builtin_shufflevector(H16::read_tr(qt + taddr[tn] + ro),
+                                                      H16::read_tr(qt + taddr8[tn] + ro), 0, 1, 2,
+                                                      3, 4, 5, 6, 7);
+                    if (tzero) {
+                        ao = e8_t{};
+                        aq = e8_t{};
+                    }
+                    dvacc[n] = H16::mfma(ao, pb[s2], dvacc[n]);
+                    dkacc[n] = H16::mfma(aq, sb[s2], dkacc[n]);
+                }
+            }
+        }
+    };
+
+    auto step = [&](int it, const unsigned char *qt, const unsigned char *ot, const float *st,
+                    unsigned char *qn, unsigned char *on, float *sn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of tile `it` have landed
+        __syncthreads();
+        if (it + 1 < nit) stage(it + 1, qn, on, sn);
+        if (wave_live) compute(it, qt, ot, st);
+    };
+    stage(0, q_lds0, o_lds0, st_lds0);
+    for (int it = 0; it < nit; it += 2) {
+        step(it, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1);
+        if (it + 1 < nit) step(it + 1, q_lds1, o_lds1, st_lds1, q_lds0, o_lds0, st_lds0);
+    }
+
+    if (!wave_live || key >= T) return;
+    // dK^T / dV^T register r of block n is dim 32n + 8(r/4) + 4half + r%4.
+    const long long off = ((long long)b * T + key) * krs + (long long)g * D;
+    unsigned short *dkrow = (unsigned short *)p.dk + off;
+    unsigned short *dvrow = (unsigned short *)p.dv + off;
+    const float sc = p.scale;
+#pragma unroll
+    for (int n = 0; n < ND; ++n)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d = 32 * n + 8 * rg + 4 * half;
+            if (D >= 32 || d < D) {
+                e4_t k4, v4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    k4[e] = (E)(dkacc[n][4 * rg + e] * sc);
+                    v4[e] = (E)dvacc[n][4 * rg + e];
+                }
+                *(u32x2_t *)(dkrow + d) = __builtin_bit_cast(u32x2_t, k4);
+                *(u32x2_t *)(dvrow + d) = __builtin_bit_cast(u32x2_t, v4);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dQ. Work-group: query rows [q0, q0 + 128) of head h of batch b, heaviest
+// causal tiles first; wave w owns rows wq0 = q0 + 32w .. + 31 (lane col = row
+// wq0 + col). Key tiles of 64: K (dual swizzle: read as rows for S^T and
+// transposed for dQ^T) and V (row reads only) in LDS, two buffers.
+// S^T = K Q^T and dP^T = V dO^T put one query per lane column, so the row's
+// L2 and Delta are per-lane scalars; register r of block kb is key
+// key0 + 32 kb + 8(r/4) + 4half + r%4.
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
+    using L = Bf16Layout<D>;
+    using H16 = Half16<E>;
+    typedef typename H16::v8 e8_t;
+    typedef typename H16::v4 e4_t;
+    constexpr int BK = L::BK;
+    constexpr int KS = D / 16;
+    constexpr int ND = (D + 31) / 32;
+    constexpr int NV = D >= 32 ? D / 32 : 1;
+    constexpr int NI = (L::NLOAD + 3) / 4;
+
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[L::TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int T = p.T;
+    const int nbh = p.B * p.H;
+    const int tq = blockIdx.x / nbh;
+    const int bh = blockIdx.x - tq * nbh;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int g = h / p.group;
+    const int q0 = (p.nblk - 1 - tq) * kBlk;
+    const int wq0 = q0 + 32 * wave;
+    const int qrow = wq0 + col;
+    const bool wave_live = wq0 < T;
+    const long long qrs = (long long)p.H * D;
+    const long long krs = (long long)p.H_kv * D;
+    const unsigned short *kbase = (const unsigned short *)p.k + (long long)b * T * krs + g * D;
+    const unsigned short *vbase = (const unsigned short *)p.v + (long long)b * T * krs + g * D;
+
+    // Q and dO rows of this lane's query as B operands.
+    e8_t qf[KS], df[KS];
+    {
+        const long long off = ((long long)b * T + qrow) * qrs + (long long)h * D + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+            if (qrow < T) {
+                x = *(const u32x4_t *)((const unsigned short *)p.q + off + 16 * ks);
+                y = *(const u32x4_t *)((const unsigned short *)p.dout + off + 16 * ks);
+            }
+            qf[ks] = __builtin_bit_cast(e8_t, x);
+            df[ks] = __builtin_bit_cast(e8_t, y);
+        }
+    }
+    float l2 = 0.f, dl = 0.f;
+    if (qrow < T) {
+        const long long r = ((long long)b * p.H + h) * T + qrow;
+        l2 = p.l2[r];
+        dl = p.delta[r];
+    }
+
+    const int kend = CAUSAL ? min(T, q0 + kBlk) : T;
+    const int nkt = (kend + BK - 1) / BK;
+
+    int koff[NI], voff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int idx = wave + 4 * i;
+        const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
+        const int pc = lane % L::C;
+        koff[i] = row * (int)krs * 2 + 16 * (pc ^ L::dswz(row));
+        voff[i] = row * (int)krs * 2 + 16 * (pc ^ L::kswz(row));
+    }
+    int kaddr[KS], vaddr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        kaddr[ks] = col * L::ROWB + 16 * ((2 * ks + half) ^ L::dswz(col));
+        vaddr[ks] = col * L::ROWB + 16 * ((2 * ks + half) ^ L::kswz(col));
+    }
+    int taddr[NV], taddr8[NV];
+    {
+        const int r0 = 4 * half + ((lane & 15) >> 2);
+        const int dl4 = (D >= 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int d = 32 * n + dl4;
+            taddr[n] = r0 * L::ROWB + 16 * ((d >> 3) ^ L::dswz(r0)) + 2 * (d & 7);
+            taddr8[n] = (r0 + 8) * L::ROWB + 16 * ((d >> 3) ^ L::dswz(r0 + 8)) + 2 * (d & 7);
+        }
+    }
+    const bool tzero = D < 32 && col >= D;
+
+    f32x16_t dqacc[ND];
+#pragma unroll
+    for (int n = 0; n < ND; ++n) dqacc[n] = f32x16_t{};
+    float c;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
+
+    auto tile = [&](bool need_mask, int j, const unsigned char *kt, const unsigned char *vt)
+        __attribute__((always_inline)) {
+        const int key0 = j * BK;
+        f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{}, d0 = f32x16_t{}, d1 = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const e8_t a0 = __builtin_bit_cast(e8_t, *(const lds_bf16x8_t *)(kt + kaddr[ks]));
+            const e8_t a1 =
+                __builtin_bit_cast(e8_t, *(const lds_bf16x8_t *)(kt + kaddr[ks] + 32 * L::ROWB));
+            const e8_t b0 = __builtin_bit_cast(e8_t, *(const lds_bf16x8_t *)(vt + vaddr[ks]));
+            const e8_t b1 =
+                __builtin_bit_cast(e8_t, *(const lds_bf16x8_t *)(vt + vaddr[ks] + 32 * L::ROWB));
+            s0 = H16::mfma(a0, qf[ks], s0);
+            s1 = H16::mfma(a1, qf[ks], s1);
+            d0 = H16::mfma(b0, df[ks], d0);
+            d1 = H16::mfma(b1, df[ks], d1);
+        }
+        // P^T and dS^T in place of S^T (s0, s1).
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p0 = fast_exp2(fmaf(s0[r], c, -l2));
+            const float p1 = fast_exp2(fmaf(s1[r], c, -l2));
+            s0[r] = p0 * (d0[r] - dl);
+            s1[r] = p1 * (d1[r] - dl);
+        }
+        if (need_mask) {
+            const int lim = (CAUSAL ? min(qrow, T - 1) : T - 1) - key0 - 4 * half;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = 8 * (r >> 2) + (r & 3);
+                s0[r] = off <= lim ? s0[r] : 0.f;
+                s1[r] = off + 32 <= lim ? s1[r] : 0.f;
+            }
+        }
+        // dS^T as the B operand: k-step s4 covers keys 16 s4 + 8(e/4) + 4half + e%4.
+        e8_t sb[4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sb[0][e] = (E)s0[e];
+            sb[1][e] = (E)s0[8 + e];
+            sb[2][e] = (E)s1[e];
+            sb[3][e] = (E)s1[8 + e];
+        }
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+            for (int n = 0; n < ND; ++n) {
+                const int tn = D >= 32 ? n : 0;
+                const int ro = 16 * s4 * L::ROWB;
+                e8_t a = __builtin_shufflevector(H16::read_tr(kt + taddr[tn] + ro),
+                                                 H16::read_tr(kt + taddr8[tn] + ro), 0, 1, 2, 3,
+                                                 4, 5, 6, 7);
+                if (tzero) a = e8_t{};
+                dqacc[n] = H16::mfma(a, sb[s4], dqacc[n]);
+            }
+        }
+    };
+
+    auto step = [&](int j, const unsigned char *kt, const unsigned char *vt, unsigned char *kn,
+                    unsigned char *vn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 1 < nkt)
+            stage_tile<D>(kbase, vbase, krs, krs, T, (j + 1) * BK, wave, koff, voff, kn, vn);
+        const int key0 = j * BK;
+        const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
+        if (active) tile(need_mask, j, kt, vt);
+    };
+    stage_tile<D>(kbase, vbase, krs, krs, T, 0, wave, koff, voff, k_lds0, v_lds0);
+    for (int j = 0; j < nkt; j += 2) {
+        step(j, k_lds0, v_lds0, k_lds1, v_lds1);
+        if (j + 1 < nkt) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    }
+
+    if (!wave_live || qrow >= T) return;
+    unsigned short *dqrow = (unsigned short *)p.dq + ((long long)b * T + qrow) * qrs + h * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int n = 0; n < ND; ++n)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int d = 32 * n + 8 * rg + 4 * half;
+            if (D >= 32 || d < D) {
+                e4_t q4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q4[e] = (E)(dqacc[n][4 * rg + e] * sc);
+                *(u32x2_t *)(dqrow + d) = __builtin_bit_cast(u32x2_t, q4);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation (no HIP calls), launch.
+// ---------------------------------------------------------------------------
+constexpr long long kMaxElems = 1LL << 62;
+constexpr long long kMaxGridB = (1LL << 24) - 1;
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr % 16) == 0; }
+
+long long bwd_ws_bytes(int B, int H, int T) {
+    long long r;
+    if (__builtin_mul_overflow((long long)B * H, (long long)T, &r) ||
+        __builtin_mul_overflow(r, 8LL, &r))
+        return -1;
+    return r;
+}
+
+template <typename E, int D, bool CAUSAL>
+void launch_bwd(const BwdParams &p, hipStream_t s) {
+    const long long rows = (long long)p.B * p.H * p.T;
+    const long long rpb = 256 / (D / 8);
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<E, D>), dim3((unsigned)((rows + rpb - 1) / rpb)),
+                       dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL>),
+                       dim3((unsigned)((long long)p.B * p.H_kv * p.nblk)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL>),
+                       dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s, p);
+}
+
+template <typename E, bool CAUSAL>
+void launch_bwd_d(const BwdParams &p, int D, hipStream_t s) {
+    switch (D) {
+        case 16: launch_bwd<E, 16, CAUSAL>(p, s); break;
+        case 32: launch_bwd<E, 32, CAUSAL>(p, s); break;
+        case 64: launch_bwd<E, 64, CAUSAL>(p, s); break;
+        default: launch_bwd<E, 128, CAUSAL>(p, s); break;
+    }
+}
+
+}  // namespace
+
+extern "C" long long fa_bwd_workspace_bytes(int B, int H, int T) {
+    if (B < 0 || H < 1 || T < 0) return -1;
+    return bwd_ws_bytes(B, H, T);
+}
+
+extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                      int H, int H_kv, int T, int D, int causal, float scale, int dtype,
+                      void *workspace, long long workspace_bytes, void *stream) {
+    if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
+        return FA_ERR_DTYPE;
+    if (dtype == FA_DTYPE_F32) return FA_ERR_DTYPE;   // 16-bit MFMA kernels only
+    if (B < 0 || T < 0 || H < 1 || H_kv < 1) return FA_ERR_BAD_SHAPE;
+    if (H % H_kv != 0) return FA_ERR_HEADS;
+    if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if (!isfinite(scale) || !isfinite(scale * kLog2e)) return FA_ERR_SCALE;
+    if (B == 0 || T == 0) return FA_OK;
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+        return FA_ERR_NULL_PTR;
+    const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
+    for (const void *ptr : ptrs)
+        if (!aligned16(ptr)) return FA_ERR_ALIGN;
+    if (((uintptr_t)lse % 4) != 0) return FA_ERR_ALIGN;
+    const long long need = bwd_ws_bytes(B, H, T);
+    if (need < 0) return FA_ERR_OVERFLOW;
+    if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+    // element counts, 32-bit staging ranges (64 rows of a tile) and grids
+    long long e;
+    if (__builtin_mul_overflow((long long)B * T, (long long)H * D, &e) || e > kMaxElems)
+        return FA_ERR_OVERFLOW;
+    if ((63LL * H * D + D) * 2 >= (1LL << 31)) return FA_ERR_OVERFLOW;
+    const long long nblk = ((long long)T + kBlk - 1) / kBlk;
+    if ((long long)B * H * nblk > kMaxGridB) return FA_ERR_OVERFLOW;
+    if ((long long)B * H * T / (256 / (D / 8)) + 1 > kMaxGridB) return FA_ERR_OVERFLOW;
+
+    BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.delta = (float *)workspace;
+    p.l2 = p.delta + (long long)B * H * T;
+    p.B = B; p.H = H; p.H_kv = H_kv; p.T = T;
+    p.group = H / H_kv;
+    p.nblk = (int)nblk;
+    p.c = scale * kLog2e;
+    p.scale = scale;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == FA_DTYPE_BF16) {
+        if (causal) launch_bwd_d<__bf16, true>(p, D, s);
+        else launch_bwd_d<__bf16, false>(p, D, s);
+    } else {
+        if (causal) launch_bwd_d<_Float16, true>(p, D, s);
+        else launch_bwd_d<_Float16, false>(p, D, s);
+    }
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}

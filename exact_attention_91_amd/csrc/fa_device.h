@@ -1,0 +1,150 @@
+// fa_device.h -- device-side building blocks shared by the attention forward
+// (fa_fwd.hip) and backward (fa_bwd.hip) kernels for gfx950: vector types,
+// the 16-bit MFMA and transposing LDS read, cross-half lane reductions, and the
+// LDS tile layout of 64-row tiles of 16-bit elements.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // 4 waves of 64
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Cross-half (lane <-> lane^32) reductions of a per-lane value.
+__device__ __forceinline__ float half_swap_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                              false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// LDS tile of 64 rows x D 16-bit elements, rows of 2D bytes, unpadded. The
+// 16-byte chunks of each row are XOR-permuted so that the MFMA operand reads
+// are bank-conflict free (64 banks of 4 bytes; a 16-byte read serves 16 lanes
+// per cycle, an 8-byte read 32):
+//   row reads (lane = row, 16 bytes of one chunk):  chunk c -> c ^ kswz(row)
+//     kswz = (row / R) % C,   C = D/8 chunks per row, R = 16/C rows per 256 B
+//   transposed reads (ds_read_b64_tr_b16 of 4-row x 16-column blocks):
+//     chunk c -> c ^ vswz(row)   (D=64: 4*((row>>1)&1); D=128: 4*(row&3))
+//   both patterns on one tile: chunk c -> c ^ dswz(row), a permutation of
+//     the rows' chunk offsets that is conflict-free for both
+// Tiles are written by buffer_load_dwordx4 ... lds straight from global
+// memory: each 64-lane load fills 1 KB of LDS in lane order, so every lane
+// fetches the global chunk that belongs at its LDS slot. Rows past the end of
+// the tensor are outside the buffer's range and arrive as zeros.
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element 16e+i
+// (e = 0..3) of the 64 halfwords the group reads, so a group reading a
+// 4-row x 16-column block row by row hands lane i the 4 rows of column i.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Bf16Layout {
+    static constexpr int BK = 64;                 // keys per tile
+    static constexpr int C = D / 8;               // 16-byte chunks per row
+    static constexpr int R = 16 / C;              // rows per 256 bytes
+    static constexpr int ROWB = 2 * D;            // bytes per row
+    static constexpr int TILEB = BK * ROWB;       // bytes per K (or V) tile
+    static constexpr int NLOAD = TILEB / 1024;    // 1 KB wave loads per tile
+    static constexpr int ROWS_PER_LOAD = 1024 / ROWB;
+    __device__ static int kswz(int row) { return (row / R) % C; }
+    __device__ static int vswz(int row) {
+        return D == 64 ? 4 * ((row >> 1) & 1) : (D == 128 ? 4 * (row & 3) : 0);
+    }
+    // Serves both read patterns at once (tiles read as rows and transposed).
+    __device__ static int dswz(int row) {
+        if (D == 16) return (row >> 3) & 1;
+        if (D == 32) return (row >> 2) & 3;
+        if (D == 64) {
+            const int e = (row >> 1) & 7;
+            return ((e & 1) << 2) | (e >> 1);
+        }
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
+typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));   // the builtin's type
+typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
+
+// The 16-bit kernel for bfloat16 and for IEEE half: operand vectors, the
+// 32x32x16 MFMA with fp32 accumulation, and the transposing LDS read.
+template <typename E>
+struct Half16;
+template <>
+struct Half16<__bf16> {
+    typedef bf16x8_t v8;
+    typedef bf16x4_t v4;
+    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static v4 read_tr(const unsigned char *p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)p);
+    }
+};
+template <>
+struct Half16<_Float16> {
+    typedef f16x8_t v8;
+    typedef f16x4_t v4;
+    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static v4 read_tr(const unsigned char *p) {
+        return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t *)p));
+    }
+};
+constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 family)
+
+
+// Issue this wave's share (of 4 waves) of the global->LDS copies of two
+// 64-row tiles, e.g. a K tile and a V tile (buffer loads straight into LDS;
+// rows past T read as zeros). koff/voff: per-lane byte offsets of the global
+// chunk each lane fetches for its LDS slot.
+template <int D>
+__device__ __forceinline__ void stage_tile(const unsigned short *kbase, const unsigned short *vbase,
+                                           long long ks1, long long vs1, int T, int key0,
+                                           int wave, const int *koff, const int *voff,
+                                           unsigned char *kdst, unsigned char *vdst) {
+    using L = Bf16Layout<D>;
+    constexpr int NI = (L::NLOAD + 3) / 4;
+    // Valid bytes from this tile's first row; (63 * stride + D) * 2 < 2^31 is
+    // checked on the host.
+    const int rows = min(T - key0, L::BK);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short *>(kbase + (long long)key0 * ks1), (short)0,
+        ((rows - 1) * (int)ks1 + D) * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short *>(vbase + (long long)key0 * vs1), (short)0,
+        ((rows - 1) * (int)vs1 + D) * 2, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int idx = wave + 4 * i;
+        if (L::NLOAD % 4 == 0 || idx < L::NLOAD) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kdst + idx * 1024), 16,
+                                                     koff[i], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + idx * 1024), 16,
+                                                     voff[i], 0, 0, 0);
+        }
+    }
+}
+
+}  // namespace

@@ -47,22 +47,11 @@
 #include <stdint.h>
 
 #include "fa.h"
+#include "fa_device.h"
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kThreads = 256;   // 4 waves of 64
 constexpr int kBQ = 128;        // query rows per work-group (32 per wave)
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kMaxFloor = -1e30f;
 
 struct FwdParams {
@@ -83,20 +72,6 @@ struct FwdParams {
     int nsplit;
     float *opart, *lpart;
 };
-
-// Cross-half (lane <-> lane^32) reductions of a per-lane value.
-__device__ __forceinline__ float half_swap_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                              false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                              false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool B>
 struct BoolC {
@@ -127,103 +102,10 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 
 // ---------------------------------------------------------------------------
 // 16-bit kernel (bfloat16 or IEEE half operands, fp32 accumulation), 64-key
-// tiles.
-//
-// LDS layouts (one buffer; two buffers alternate between key tiles):
-//   K tile [64 keys][D], V tile [64 keys][D], rows of 2D bytes, unpadded. The
-//   16-byte chunks of each row are XOR-permuted so that the MFMA operand reads
-//   are bank-conflict free:
-//     K: physical chunk = c ^ ((row / R) % C),   C = D/8 chunks per row,
-//                                                R = 16/C rows per 256 bytes
-//     V: physical chunk = c ^ vswz(row)  (D=64: 4*((row>>1)&1); D=128: 4*(row&3))
-//   Tiles are written by buffer_load_dwordx4 ... lds straight from global
-//   memory: each 64-lane load fills 1 KB of LDS in lane order, so every lane
-//   fetches the global chunk that belongs at its LDS slot. Rows past T are
-//   outside the buffer's range and arrive as zeros.
-//   V^T fragments for P.V come from ds_read_b64_tr_b16: in each 16-lane group,
-//   lane i receives element 16e+i (e = 0..3) of the 64 halfwords the group
-//   reads, so a group reading a 4-key x 16-dim block row by row hands lane i
-//   the 4 keys of dim i.
+// tiles. K and V tiles (two buffers alternating between key tiles) use the
+// layout of fa_device.h: K is read as rows (kswz), V transposed for the V^T
+// operand of P.V (vswz).
 // ---------------------------------------------------------------------------
-template <int D>
-struct Bf16Layout {
-    static constexpr int BK = 64;                 // keys per tile
-    static constexpr int C = D / 8;               // 16-byte chunks per row
-    static constexpr int R = 16 / C;              // rows per 256 bytes
-    static constexpr int ROWB = 2 * D;            // bytes per row
-    static constexpr int TILEB = BK * ROWB;       // bytes per K (or V) tile
-    static constexpr int NLOAD = TILEB / 1024;    // 1 KB wave loads per tile
-    static constexpr int ROWS_PER_LOAD = 1024 / ROWB;
-    __device__ static int kswz(int row) { return (row / R) % C; }
-    __device__ static int vswz(int row) {
-        return D == 64 ? 4 * ((row >> 1) & 1) : (D == 128 ? 4 * (row & 3) : 0);
-    }
-};
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
-typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));   // the builtin's type
-typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
-
-// The 16-bit kernel for bfloat16 and for IEEE half: operand vectors, the
-// 32x32x16 MFMA with fp32 accumulation, and the transposing LDS read.
-template <typename E>
-struct Half16;
-template <>
-struct Half16<__bf16> {
-    typedef bf16x8_t v8;
-    typedef bf16x4_t v4;
-    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-    __device__ static v4 read_tr(const unsigned char *p) {
-        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)p);
-    }
-};
-template <>
-struct Half16<_Float16> {
-    typedef f16x8_t v8;
-    typedef f16x4_t v4;
-    __device__ static f32x16_t mfma(v8 a, v8 b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-    __device__ static v4 read_tr(const unsigned char *p) {
-        return __builtin_bit_cast(v4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4_t *)p));
-    }
-};
-constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 family)
-
-// Issue this wave's share of the global->LDS copies of one K tile and one V
-// tile (buffer loads straight into LDS; rows past T read as zeros).
-template <int D>
-__device__ __forceinline__ void stage_tile(const unsigned short *kbase, const unsigned short *vbase,
-                                           long long ks1, long long vs1, int T, int key0,
-                                           int wave, const int *koff, const int *voff,
-                                           unsigned char *kdst, unsigned char *vdst) {
-    using L = Bf16Layout<D>;
-    constexpr int NI = (L::NLOAD + 3) / 4;
-    // Valid bytes from this tile's first row; (63 * stride + D) * 2 < 2^31 is
-    // checked on the host.
-    const int rows = min(T - key0, L::BK);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned short *>(kbase + (long long)key0 * ks1), (short)0,
-        ((rows - 1) * (int)ks1 + D) * 2, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<unsigned short *>(vbase + (long long)key0 * vs1), (short)0,
-        ((rows - 1) * (int)vs1 + D) * 2, kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const int idx = wave + 4 * i;
-        if (L::NLOAD % 4 == 0 || idx < L::NLOAD) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kdst + idx * 1024), 16,
-                                                     koff[i], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + idx * 1024), 16,
-                                                     voff[i], 0, 0, 0);
-        }
-    }
-}
-
 template <typename E, int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;

@@ -1,9 +1,10 @@
 """Thin ctypes binding over libfa.so (the C ABI declared in include/fa.h).
 
 Argument marshalling only: shape/dtype/device checks, output allocation with
-torch, and the call into `fa_fwd` / `fa_fwd_strided` on torch's current
-stream. Every step of the attention forward runs in the library's HIP kernels;
-there is no fallback. If libfa.so is missing, every call raises.
+torch, and the calls into the library (forward, key-split forward, combine,
+backward) on torch's current stream. Every step of the attention runs in the
+library's HIP kernels; there is no fallback. If libfa.so is missing, every
+call raises.
 """
 import ctypes
 import math
@@ -49,6 +50,11 @@ def _lib():
         lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
         lib.fa_lse_combine.restype = _I
+        lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _VP,
+                                                        ctypes.c_longlong, _VP]
+        lib.fa_bwd.restype = _I
+        lib.fa_bwd_workspace_bytes.argtypes = [_I] * 3
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_status_str.argtypes = [_I]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -210,3 +216,49 @@ def lse_combine(o_parts, lse_parts, dtype=torch.bfloat16):
                                o.data_ptr(), lse.data_ptr(), _dtype_code(o), stream)
     _raise(rc, "fa_lse_combine")
     return o, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, T: int) -> int:
+    """Bytes of device workspace bwd needs (-1 for invalid sizes)."""
+    return int(_lib().fa_bwd_workspace_bytes(B, H, T))
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None):
+    """Attention backward on contiguous BNHD tensors (bfloat16 or float16).
+
+    q, o, dout: [B, T, H, D]; k, v: [B, T, H_kv, D]; lse: float32 [B, H, T]
+    -- o and lse as returned by fwd for the same q, k, v, causal, scale.
+    Returns (dq, dk, dv) shaped like q, k, v. `workspace` (optional): a
+    device tensor of at least bwd_workspace_bytes(B, H, T) bytes; allocated
+    here when None."""
+    _check(q, k, v)
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"bwd takes bfloat16 or float16 inputs, got {q.dtype}")
+    B, T, H, D = q.shape
+    for name, t, shape, dt in (("o", o, q.shape, q.dtype), ("dout", dout, q.shape, q.dtype),
+                               ("lse", lse, (B, H, T), torch.float32)):
+        if not isinstance(t, torch.Tensor) or t.device != q.device:
+            raise ValueError(f"{name} must be a tensor on {q.device}")
+        if tuple(t.shape) != tuple(shape) or t.dtype != dt:
+            raise ValueError(f"{name} must be {dt} of shape {tuple(shape)}, got "
+                             f"{t.dtype} {tuple(t.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
+        if not t.is_contiguous():
+            raise ValueError(f"bwd needs contiguous tensors ({name} is not)")
+    H_kv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = bwd_workspace_bytes(B, H, T)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H,
+                       H_kv, T, D, int(bool(causal)), float(scale), _dtype_code(q),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       stream)
+    _raise(rc, "fa_bwd")
+    return dq, dk, dv

@@ -1,6 +1,6 @@
 /*
- * fa.h -- C ABI of libfa.so: exact, IO-aware, tiled attention forward on
- * MI355X (gfx950).
+ * fa.h -- C ABI of libfa.so: exact, IO-aware, tiled attention forward (and
+ * its key-split variant and backward) on MI355X (gfx950).
  *
  * What it computes. For every batch b, query head h and query row i, with kv
  * head g = h / (H / H_kv) and visible keys V_i = { j < T : !causal or j <= i }:
@@ -154,6 +154,43 @@ long long fa_fwd_splitk_workspace_bytes(int B, int H, int T, int D, int nsplit);
  */
 int fa_lse_combine(const float *o_parts, const float *lse_parts, int n, int B, int H,
                    int T, int D, void *o, float *lse, int dtype, void *stream);
+
+/*
+ * Attention backward: the gradients of the forward above for an upstream
+ * gradient dO = dLoss/dO (the loss is taken not to depend on lse). The
+ * forward's intermediates are recomputed from q, k and the stored lse instead
+ * of being read back ("Flash Attention Memory Optimization Explained", "Key
+ * Mechanisms": backward checkpointing); the formulas are the chain rule of the
+ * definition above:
+ *   P_ij  = exp(s_ij - lse_i) on visible keys, 0 elsewhere
+ *   dV_j  = sum_i P_ij dO_i             dP_ij = dO_i . v_j
+ *   dS_ij = P_ij (dP_ij - Delta_i),     Delta_i = dO_i . o_i
+ *   dQ_i  = scale sum_j dS_ij k_j       dK_j = scale sum_i dS_ij q_i
+ * with dK, dV of a kv head summed over the query heads sharing it (in a fixed
+ * order: the result is deterministic). Delta uses the identity
+ * sum_j P_ij dP_ij = dO_i . o_i, so o and lse must be the forward's outputs
+ * for the same q, k, v, causal and scale.
+ *   q, o, dout, dq  [B, T, H, D]      dtype (bf16 or fp16), dq written
+ *   k, v, dk, dv    [B, T, H_kv, D]   dtype, dk and dv written
+ *   lse             [B, H, T]         float32 (the forward's)
+ * All contiguous, 16-byte aligned (lse 4-byte). Precision: P and dS are
+ * rounded to the input type only as MFMA operands, everything else is fp32;
+ * the outputs are rounded to nearest even. fp32 inputs return FA_ERR_DTYPE.
+ * workspace: caller-owned device memory, 16-byte aligned, at least
+ * fa_bwd_workspace_bytes(B, H, T) bytes: float32 Delta [B][H][T] followed by
+ * float32 lse * log2(e) [B][H][T]; overwritten (calls sharing a workspace
+ * must be ordered on one stream); FA_ERR_WORKSPACE if too small. dq, dk, dv
+ * must not overlap any input, the workspace or each other. Three kernels
+ * are enqueued on `stream`.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, int B, int H, int H_kv, int T,
+           int D, int causal, float scale, int dtype, void *workspace,
+           long long workspace_bytes, void *stream);
+
+/* Workspace bytes fa_bwd needs: 2 * B * H * T * 4; -1 for invalid sizes or
+ * overflow. */
+long long fa_bwd_workspace_bytes(int B, int H, int T);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_str(int status);

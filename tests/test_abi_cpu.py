@@ -38,7 +38,8 @@ DT = _enum_values("fa_dtype_t")
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_fwd", "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd",
+                                     "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
                                      "fa_fwd_strided", "fa_lse_combine", "fa_status_str",
                                      "fa_version"]
 
@@ -67,11 +68,20 @@ def test_version_and_status_strings(lib):
 
 
 # A fake, 16-byte aligned, never-dereferenced device address: every call below
-# fails validation, which runs entirely on the host before any HIP call.
+# is meant to fail validation, which runs entirely on the host before any HIP
+# call. Where a GPU is visible these calls are skipped, so that a case that
+# wrongly passed validation could never launch a kernel on a fake address.
 P = 4096
 
 
+def _host_only():
+    from tests.conftest import gpu_available
+    if gpu_available():
+        pytest.skip("fake-pointer validation tests run only where no GPU is visible")
+
+
 def call(lib, **kw):
+    _host_only()
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, T=100, D=64, causal=1,
              scale=0.125, dtype=DT["FA_DTYPE_BF16"], stream=None)
     a.update(kw)
@@ -80,6 +90,7 @@ def call(lib, **kw):
 
 
 def call_strided(lib, qs=(0, 0, 0), ks=(0, 0, 0), vs=(0, 0, 0), os_=(0, 0, 0), **kw):
+    _host_only()
     from exact_attention_91_amd.fa import _LL3
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, T=100, D=64, causal=0,
              scale=0.125, dtype=DT["FA_DTYPE_BF16"])
@@ -142,6 +153,7 @@ def test_strided_rejects(lib):
     wrap = dict(base, os_=((1 << 62) + 8, 4 * 64, 64))
     assert call_strided(lib, **wrap) == ST["FA_ERR_OVERFLOW"]
     from exact_attention_91_amd.fa import _LL3
+    _host_only()
     rc = lib.fa_fwd_strided(P, P, P, P, P, 2, 4, 2, 100, 64, 0, 0.125, 1,
                             None, _LL3(*kvs), _LL3(*kvs), _LL3(*good), None)
     assert rc == ST["FA_ERR_NULL_PTR"]
@@ -166,6 +178,7 @@ def test_no_unresolved_kernel_stubs(lib):
 
 
 def call_splitk(lib, **kw):
+    _host_only()
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, T=100, D=64, causal=1,
              scale=0.125, dtype=DT["FA_DTYPE_BF16"], nsplit=3, ws=P, ws_bytes=1 << 40)
     a.update(kw)
@@ -219,8 +232,60 @@ def test_splitk_empty_call_is_a_noop(lib):
     (dict(B=0, op=None, lp=None, o=None, lse=None), "FA_OK"),
 ])
 def test_lse_combine_rejects(lib, kw, code):
+    _host_only()
     a = dict(op=P, lp=P, n=2, B=2, H=4, T=100, D=64, o=P, lse=P, dtype=DT["FA_DTYPE_BF16"])
     a.update(kw)
     rc = lib.fa_lse_combine(a["op"], a["lp"], a["n"], a["B"], a["H"], a["T"], a["D"], a["o"],
                             a["lse"], a["dtype"], None)
     assert rc == ST[code]
+
+
+def call_bwd(lib, **kw):
+    _host_only()
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=2, H=4, H_kv=2, T=100,
+             D=64, causal=1, scale=0.125, dtype=DT["FA_DTYPE_BF16"], ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                      a["dv"], a["B"], a["H"], a["H_kv"], a["T"], a["D"], a["causal"],
+                      a["scale"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+def test_bwd_workspace_bytes(lib):
+    f = lib.fa_bwd_workspace_bytes
+    assert f(2, 4, 100) == 2 * 2 * 4 * 100 * 4
+    assert f(0, 4, 100) == 0
+    assert f(2, 0, 100) == -1
+    assert f(-1, 4, 100) == -1
+    assert f(1 << 30, 1 << 30, 1 << 30) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=DT["FA_DTYPE_F32"]), "FA_ERR_DTYPE"),     # 16-bit MFMA kernels only
+    (dict(dtype=5), "FA_ERR_DTYPE"),
+    (dict(B=-1), "FA_ERR_BAD_SHAPE"),
+    (dict(H_kv=0), "FA_ERR_BAD_SHAPE"),
+    (dict(H=6, H_kv=4), "FA_ERR_HEADS"),
+    (dict(D=48), "FA_ERR_HEAD_DIM"),
+    (dict(scale=math.inf), "FA_ERR_SCALE"),
+    (dict(scale=3.0e38), "FA_ERR_SCALE"),
+    (dict(o=None), "FA_ERR_NULL_PTR"),
+    (dict(do=None), "FA_ERR_NULL_PTR"),
+    (dict(dv=None), "FA_ERR_NULL_PTR"),
+    (dict(ws=None), "FA_ERR_NULL_PTR"),
+    (dict(dq=P + 8), "FA_ERR_ALIGN"),
+    (dict(do=P + 2), "FA_ERR_ALIGN"),
+    (dict(ws=P + 4), "FA_ERR_ALIGN"),
+    (dict(lse=P + 2), "FA_ERR_ALIGN"),
+    (dict(ws_bytes=2 * 2 * 4 * 100 * 4 - 1), "FA_ERR_WORKSPACE"),
+    (dict(B=1 << 20, H=1 << 10, H_kv=1, T=1 << 12, ws_bytes=1 << 62), "FA_ERR_OVERFLOW"),
+    (dict(B=1, H=1 << 18, H_kv=1, T=64, D=128), "FA_ERR_OVERFLOW"),   # 64-row tile > 2 GiB
+])
+def test_bwd_rejects(lib, kw, code):
+    assert call_bwd(lib, **kw) == ST[code]
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0),
+                                dict(B=0, q=None, k=None, v=None, o=None, lse=None, do=None,
+                                     dq=None, dk=None, dv=None, ws=None, ws_bytes=0)])
+def test_bwd_empty_call_is_a_noop(lib, kw):
+    assert call_bwd(lib, **kw) == ST["FA_OK"]

@@ -1,0 +1,186 @@
+"""Attention backward (fa_bwd) through the C ABI against the float64 oracle.
+
+The GPU forward produces o and lse, the GPU backward the gradients; the oracle
+(oracle.attention_bwd) recomputes everything from q, k, v and dO alone.
+
+Tolerance: max|grad_gpu - grad_ref| <= rtol * max(1, max|grad_ref|) per
+tensor, rtol = 2e-2 for bf16 and 3e-3 for fp16. Derivation: a float64
+emulation of the kernels' rounding points (P and dS rounded to the 16-bit type
+as MFMA operands, Delta from the 16-bit O, fp32 accumulation, outputs rounded
+to nearest even) gives worst errors of 7.0e-3 (bf16) and 4.6e-4 (fp16) times
+max|grad_ref| on these shapes (q, k ~ N(0, 1) and N(0, 4^2), T up to 2048,
+D 16..128); the bound leaves a factor ~3 (bf16) and ~6 (fp16) above that.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_attention_91_amd.inputs import WORKLOADS, default_scale, generate, generate_dout, \
+    generate_workload
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"bf16": 2e-2, "f16": 3e-3}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_bwd(x, do, causal, scale, o_lse=None):
+    from exact_attention_91_amd import fa
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    if o_lse is None:
+        o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    else:
+        o, lse = o_lse[0].cuda(), o_lse[1].cuda()
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return tuple(t.double().cpu().numpy() for t in (dq, dk, dv))
+
+
+def check_grads(x, do64, dtype, causal, scale, got, label=""):
+    from oracle import oracle as orc
+    ref = orc.attention_bwd(x.q64, x.k64, x.v64, do64, causal, scale)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(g)), f"{name} not finite"
+        err = float(np.max(np.abs(g - r))) if r.size else 0.0
+        mx = float(np.max(np.abs(r))) if r.size else 0.0
+        tol = RTOL[dtype] * max(1.0, mx)
+        say(f"  {label} {name}: max|ref|={mx:.3f} max|err|={err:.3e} (tol {tol:.3e})")
+        assert err <= tol, f"{name} error {err} > {tol}"
+
+
+def case(B, H, H_kv, T, D, dtype, seed, sigma=1.0):
+    x = generate(B, H, H_kv, T, D, dtype, seed, qk_sigma=sigma)
+    do, do64 = generate_dout(B, H, T, D, dtype, seed)
+    return x, do, do64
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [1, 63, 65, 129, 300, 1000])
+def test_bwd_small_elementwise(dtype, D, causal, T):
+    B, H, H_kv = (2, 3, 1) if T < 500 else (1, 2, 2)
+    seed = 9000 + T * 10 + D
+    say(f"case bwd dtype={dtype} D={D} causal={causal} B={B} H={H} H_kv={H_kv} T={T} seed={seed}")
+    x, do, do64 = case(B, H, H_kv, T, D, dtype, seed)
+    scale = default_scale(D)
+    got = run_bwd(x, do, causal, scale)
+    check_grads(x, do64, dtype, causal, scale, got, "small")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (6, 2), (8, 1)])
+def test_bwd_kv_head_groups(dtype, H, H_kv):
+    x, do, do64 = case(2, H, H_kv, 200, 64, dtype, 9100 + 10 * H + H_kv)
+    for causal in (False, True):
+        say(f"case bwd groups dtype={dtype} H={H} H_kv={H_kv} causal={causal}")
+        got = run_bwd(x, do, causal, 0.125)
+        check_grads(x, do64, dtype, causal, 0.125, got, "groups")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.9, 1e-3])
+def test_bwd_scale_values(scale):
+    x, do, do64 = case(1, 2, 1, 150, 32, "bf16", 9200)
+    for causal in (False, True):
+        say(f"case bwd scale={scale} causal={causal}")
+        got = run_bwd(x, do, causal, scale)
+        check_grads(x, do64, "bf16", causal, scale, got, f"scale={scale}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_large_scores(causal):
+    """q, k ~ N(0, 4^2): scores of magnitude ~100, weights near one-hot."""
+    x, do, do64 = case(2, 4, 1, 700, 64, "bf16", 9300, sigma=4.0)
+    got = run_bwd(x, do, causal, 0.125)
+    check_grads(x, do64, "bf16", causal, 0.125, got, "sigma4")
+
+
+def test_bwd_with_oracle_forward_outputs():
+    """The backward fed the oracle's o (rounded to bf16) and lse (fp32) instead
+    of the GPU forward's: the same gradients within tolerance."""
+    from oracle import oracle as orc
+    x, do, do64 = case(2, 4, 2, 333, 64, "bf16", 9400)
+    o64, l64 = orc.attention(x.q64, x.k64, x.v64, True, 0.125)
+    o = torch.tensor(o64, dtype=torch.float32).to(torch.bfloat16)
+    lse = torch.tensor(l64, dtype=torch.float32)
+    got = run_bwd(x, do, True, 0.125, o_lse=(o, lse))
+    check_grads(x, do64, "bf16", True, 0.125, got, "oracle o/lse")
+
+
+def test_bwd_deterministic():
+    """Two calls give bitwise identical gradients (no atomics; fixed order)."""
+    x, do, _ = case(2, 6, 2, 517, 64, "bf16", 9500)
+    a = run_bwd(x, do, True, 0.125)
+    b = run_bwd(x, do, True, 0.125)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+def test_bwd_invariants():
+    """Gradients of a kv head's keys sum to ~0 (softmax is invariant to a
+    common shift of all keys); dV sums to the group's dO sum."""
+    B, H, H_kv, T, D = 1, 4, 2, 400, 64
+    x, do, do64 = case(B, H, H_kv, T, D, "f16", 9600)
+    dq, dk, dv = run_bwd(x, do, False, 0.125)
+    assert np.max(np.abs(dk.sum(axis=1))) <= 0.05
+    do_groups = do64.reshape(B, T, H_kv, H // H_kv, D).sum(axis=3).sum(axis=1)
+    assert np.max(np.abs(dv.sum(axis=1) - do_groups)) <= 0.05
+
+
+def test_bwd_binding_errors():
+    from exact_attention_91_amd import fa
+    x, do, _ = case(1, 2, 1, 64, 64, "bf16", 9700)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o, lse = fa.fwd(q, k, v, causal=True)
+    with pytest.raises(RuntimeError, match="workspace"):
+        fa.bwd(q, k, v, o, lse, do.cuda(), causal=True,
+               workspace=torch.empty((64,), dtype=torch.uint8, device="cuda"))
+    with pytest.raises(TypeError):
+        fa.bwd(q.float(), k.float(), v.float(), o.float(), lse, do.cuda().float())
+    with pytest.raises(ValueError):
+        fa.bwd(q, k, v, o, lse[:, :, :10], do.cuda())
+
+
+def test_bwd_empty():
+    from exact_attention_91_amd import fa
+    q = torch.empty((0, 5, 2, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((0, 5, 1, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((0, 2, 5), dtype=torch.float32, device="cuda")
+    dq, dk, dv = fa.bwd(q, k, k, q, lse, q)
+    assert dq.shape == q.shape and dk.shape == k.shape
+
+
+# ---------------------------------------------------------------- full size
+
+@pytest.mark.parametrize("name", ["gpt2", "gpt2_f16"])
+def test_bwd_workload_gpt2(name):
+    """The GPT-2 attention layer (B=16 H=12 T=1024 D=64, causal), compared in full."""
+    w = WORKLOADS[name]
+    say(f"workload bwd {w.name}")
+    x = generate_workload(w)
+    do, do64 = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)
+    got = run_bwd(x, do, True, w.scale)
+    check_grads(x, do64, w.dtype, True, w.scale, got, w.name)
+
+
+def test_bwd_mqa_head_shape():
+    """Twelve query heads on one kv head, q, k ~ N(0, 4^2): the mqa workload's
+    head structure at one batch and T = 1024, compared in full."""
+    x, do, do64 = case(1, 12, 1, 1024, 64, "bf16", 1005, sigma=4.0)
+    got = run_bwd(x, do, True, 0.125)
+    check_grads(x, do64, "bf16", True, 0.125, got, "mqa-shape")
+
+
+def test_bwd_long_rows_d128():
+    """D = 128, T = 4096, one head (the long workload's head shape)."""
+    x, do, do64 = case(1, 1, 1, 4096, 128, "bf16", 1004)
+    got = run_bwd(x, do, True, default_scale(128))
+    check_grads(x, do64, "bf16", True, default_scale(128), got, "long-shape")
