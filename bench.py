@@ -28,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of MFMA peak (GPT-2 causal bf16 shape)"
+METRIC_BWD = "attention bwd TFLOP/s (5 contractions counted) and % of MFMA peak"
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA, TFLOP/s
 KERNEL_SRC = os.path.join(ROOT, "exact_attention_91_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_gpt2_traffic.json")
@@ -42,6 +43,9 @@ def parse():
     # to settle; shorter warm-ups time the ramp, not the kernel.
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="gpt2")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="bwd: time fa_bwd (gradients for a seeded dO, from the "
+                         "forward's o and lse computed once before timing)")
     ap.add_argument("--nsplit", type=int, default=1,
                     help="> 1: time fa_fwd_splitk (key split into this many parts "
                          "plus the logsumexp combine) instead of fa_fwd")
@@ -101,7 +105,26 @@ def main():
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             w.B, w.H, w.H_kv, w.T, w.D, int(causal), w.scale, dcode, sp)
 
-    if a.nsplit > 1:
+    if a.which == "bwd":
+        from exact_attention_91_amd.inputs import generate_dout
+        if a.nsplit > 1:
+            raise SystemExit("--nsplit applies to the forward only")
+        rc = lib.fa_fwd(*args)
+        if rc:
+            raise RuntimeError(fa.status_str(rc))
+        do = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)[0].cuda()
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        nbytes = fa.bwd_workspace_bytes(w.B, w.H, w.T)
+        ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+        bargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.H_kv,
+                 w.T, w.D, int(causal), w.scale, dcode, ws.data_ptr(), nbytes, sp)
+
+        def step():
+            rc = lib.fa_bwd(*bargs)
+            if rc:
+                raise RuntimeError(fa.status_str(rc))
+    elif a.nsplit > 1:
         nbytes = fa.splitk_workspace_bytes(w.B, w.H, w.T, w.D, a.nsplit)
         ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
         sargs = args[:-1] + (a.nsplit, ws.data_ptr(), nbytes, sp)
@@ -136,7 +159,8 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
-    flops = w.flops(causal)
+    # backward: five contractions (S, dP, dV, dK, dQ) against the forward's two
+    flops = w.flops(causal) * (2.5 if a.which == "bwd" else 1.0)
     tflops = flops / (ms * 1e-3) / 1e12
 
     cold = None
@@ -165,13 +189,36 @@ def main():
             "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
                        f"{str(a.nsplit > 1).lower()}>" if w.dtype in _ELEM else
                        f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
+    if a.which == "bwd":
+        roof["kernel"] = (f"fa_bwd_pre_kernel + fa_bwd_dkdv_kernel<{_ELEM[w.dtype]}, {w.D}, "
+                          f"{str(causal).lower()}> + fa_bwd_dq_kernel (rate over the three)")
+        roof["traffic"] = None
     if a.nsplit > 1:
         # one step = the split kernel plus the combine kernel; the rate is over both
         roof["kernel"] += f" + fa_lse_combine_kernel<{_ELEM[w.dtype]}, {w.D}>"
         roof["traffic"] = None
 
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and a.which == "bwd":
+        from oracle import oracle as orc
+        torch.cuda.synchronize()
+        got = [t.to(torch.float64).cpu().numpy() for t in (dq, dk, dv)]
+        do64 = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)[1]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            ref = orc.attention_bwd(x.q64, x.k64, x.v64, do64, causal, w.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= a.cpu_seconds:
+                break
+        sec = el / reps
+        cpu = {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(),
+               "kind": "oracle",
+               "sample": f"the full {w.name} backward (all {w.B * w.H * w.T} query rows), "
+                         f"{reps} repeat(s), {sec:.3f} s each",
+               "gpu_vs_oracle_max_abs_err": {n: float(np.max(np.abs(g_ - r_)))
+                                             for n, g_, r_ in zip(("dQ", "dK", "dV"), got, ref)}}
+    elif not a.no_cpu_baseline:
         from oracle import oracle as orc
         torch.cuda.synchronize()
         o_gpu = o.to(torch.float64).cpu().numpy()
@@ -192,15 +239,16 @@ def main():
                                              "L": float(np.max(np.abs(l_gpu - l_ref)))}}
 
     out = {
-        "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_BWD if a.which == "bwd" else METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": f"{w.name}: B={w.B} H={w.H} H_kv={w.H_kv} T={w.T} D={w.D} "
-                               f"BNHD {w.dtype} causal={causal}",
+        "config": {"workload": f"{w.name}{' backward' if a.which == 'bwd' else ''}: B={w.B} "
+                               f"H={w.H} H_kv={w.H_kv} T={w.T} D={w.D} BNHD {w.dtype} "
+                               f"causal={causal}",
                    "B": w.B, "H": w.H, "H_kv": w.H_kv, "T": w.T, "D": w.D,
                    "causal": causal, "layout": "BNHD", "parallelism": "single GPU",
-                   "nsplit": a.nsplit},
+                   "nsplit": a.nsplit, "pass": a.which},
         "flop_per_step": flops,
         "roofline": roof,
         "cpu_baseline": cpu,

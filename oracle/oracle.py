@@ -22,6 +22,11 @@ attention_range(..., lo, hi)             attention over keys [lo, hi) only,
 lse_combine(o_parts, lse_parts)          merge of partials over disjoint key
                                          ranges: L = ln sum exp(L_s),
                                          O = sum exp(L_s - L) O_s (C).
+attention_masked(q, k, v, causal, scale, window, global_tokens)
+                                         sliding-window / local-global mask:
+                                         key j visible to query i iff
+                                         |i - j| <= window or j is a global
+                                         token (and j <= i when causal) (C).
 attention_bwd(q, k, v, dout, causal, scale)
                                          gradients (dq, dk, dv) of the same
                                          definition for upstream gradient dO,
@@ -73,6 +78,9 @@ def _lib():
         lib.oracle_lse_combine_f64.argtypes = [_DP, _DP, ctypes.c_int, ctypes.c_longlong,
                                                ctypes.c_int, _DP, _DP]
         lib.oracle_lse_combine_f64.restype = ctypes.c_int
+        lib.oracle_attn_masked_f64.argtypes = (common + [_DP, _DP] + shape +
+                                               [ctypes.c_int, ctypes.c_void_p])
+        lib.oracle_attn_masked_f64.restype = ctypes.c_int
         lib.oracle_attn_bwd_f64.argtypes = common + [_DP, _DP, _DP, _DP] + shape
         lib.oracle_attn_bwd_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
@@ -180,6 +188,28 @@ def lse_combine(o_parts, lse_parts):
                                        _ptr(o), _ptr(lse))
     if rc:
         raise RuntimeError(f"oracle_lse_combine_f64 failed ({rc})")
+    return o, lse
+
+
+def attention_masked(q, k, v, causal: bool, scale: float, window: int, global_tokens=()):
+    """Attention where key j is visible to query i iff |i - j| <= window or j
+    is in global_tokens (yelogs.com Flash Attention2-in-Triton article,
+    sparse-attention variants: sliding_window_mask, local_global_mask), and
+    j <= i when causal. Returns (o, lse) like attention()."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    flags = np.zeros(T, np.uint8)
+    for j in global_tokens:
+        if not 0 <= int(j) < T:
+            raise ValueError(f"global token {j} outside [0, {T})")
+        flags[int(j)] = 1
+    o = np.empty_like(q)
+    lse = np.empty((B, H, T), np.float64)
+    rc = _lib().oracle_attn_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H,
+                                       H_kv, T, D, int(bool(causal)), float(scale), int(window),
+                                       flags.ctypes.data)
+    if rc:
+        raise RuntimeError(f"oracle_attn_masked_f64 failed ({rc})")
     return o, lse
 
 

@@ -48,6 +48,16 @@
  * same rescale-and-add the online recurrence applies between two chunks, with
  * each chunk's own normaliser folded into exp(L_s).
  *
+ * oracle_attn_masked_f64 is the definition with the visible set cut by the
+ * sparse patterns of the same article ("Flash Attention2 的變體", sparse
+ * attention support): sliding window, key j visible to query i iff
+ * |i - j| <= window; local-global, iff |i - j| <= window or j is one of the
+ * global tokens. The causal flag, when set, also applies (j <= i). Each row's
+ * visible keys are listed explicitly and the row is the plain two-pass
+ * softmax over them; a row with no visible key (possible only when no
+ * window contains the row itself, i.e. never for window >= 0) gets O = 0,
+ * L = -inf.
+ *
  * oracle_attn_bwd_f64 is the gradient of that definition, for a loss whose
  * gradient with respect to O is dO (L is treated as an auxiliary output that
  * the loss does not use). "Flash Attention Memory Optimization Explained",
@@ -321,6 +331,73 @@ int oracle_lse_combine_f64(const double *o_parts, const double *lse_parts, int n
         lse[r] = L;
     }
     return 0;
+}
+
+/* Attention under the sliding-window / local-global mask. is_global: T bytes,
+ * nonzero for the global tokens (NULL: none). window >= 0. */
+int oracle_attn_masked_f64(const double *q, const double *k, const double *v,
+                           double *o, double *lse,
+                           int B, int H, int H_kv, int T, int D, int causal, double scale,
+                           int window, const unsigned char *is_global) {
+    if (bad_args(B, H, H_kv, T, D) || window < 0) return -1;
+    const long long nrows = (long long)B * H * T;
+    const int group = H / H_kv;
+    int fail = 0;
+#pragma omp parallel
+    {
+        int *vis = (int *)malloc(sizeof(int) * (size_t)T);
+        double *s = (double *)malloc(sizeof(double) * (size_t)T);
+        if (!vis || !s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (long long r = 0; r < nrows; ++r) {
+                const int i = (int)(r % T);
+                const int h = (int)((r / T) % H);
+                const int b = (int)(r / ((long long)T * H));
+                const int g = h / group;
+                /* the visible set of row i, from the mask predicates */
+                int n = 0;
+                for (int j = 0; j < T; ++j) {
+                    const int local = (i - j <= window) && (j - i <= window);
+                    const int glob = is_global && is_global[j];
+                    const int causal_ok = !causal || j <= i;
+                    if ((local || glob) && causal_ok) vis[n++] = j;
+                }
+                const double *qi = q + qidx(b, i, h, H, T, D);
+                double *orow = o + qidx(b, i, h, H, T, D);
+                double *lrow = lse + ((size_t)b * H + h) * T + i;
+                for (int d = 0; d < D; ++d) orow[d] = 0.0;
+                if (n == 0) {
+                    *lrow = -INFINITY;
+                    continue;
+                }
+                double m = -INFINITY;
+                for (int t = 0; t < n; ++t) {
+                    const double *kj = k + qidx(b, vis[t], g, H_kv, T, D);
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+                    s[t] = scale * dot;
+                    if (s[t] > m) m = s[t];
+                }
+                double z = 0.0;
+                for (int t = 0; t < n; ++t) {
+                    s[t] = exp(s[t] - m);
+                    z += s[t];
+                }
+                for (int t = 0; t < n; ++t) {
+                    const double *vj = v + qidx(b, vis[t], g, H_kv, T, D);
+                    const double w = s[t] / z;
+                    for (int d = 0; d < D; ++d) orow[d] += w * vj[d];
+                }
+                *lrow = m + log(z);
+            }
+        }
+        free(vis);
+        free(s);
+    }
+    return fail ? -2 : 0;
 }
 
 /* Gradients of full attention. dout, dq: [B, T, H, D]; dk, dv: [B, T, H_kv, D]
