@@ -124,6 +124,19 @@ def main():
             rc = lib.fa_bwd(*bargs)
             if rc:
                 raise RuntimeError(fa.status_str(rc))
+    elif w.window >= 0:
+        if a.nsplit > 1:
+            raise SystemExit("--nsplit does not apply to window workloads")
+        g = torch.tensor(w.global_tokens, dtype=torch.int32, device="cuda")
+        nbytes = int(lib.fa_fwd_window_workspace_bytes(w.T))
+        ws = torch.empty((max(nbytes, 8),), dtype=torch.uint8, device="cuda")
+        wargs = args[:-1] + (w.window, g.data_ptr() if g.numel() else None, g.numel(),
+                             ws.data_ptr(), nbytes, sp)
+
+        def step():
+            rc = lib.fa_fwd_window(*wargs)
+            if rc:
+                raise RuntimeError(fa.status_str(rc))
     elif a.nsplit > 1:
         nbytes = fa.splitk_workspace_bytes(w.B, w.H, w.T, w.D, a.nsplit)
         ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
@@ -189,6 +202,10 @@ def main():
             "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
                        f"{str(a.nsplit > 1).lower()}>" if w.dtype in _ELEM else
                        f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
+    if w.window >= 0:
+        roof["kernel"] = (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
+                          f"false, true> (window)")
+        roof["traffic"] = None
     if a.which == "bwd":
         roof["kernel"] = (f"fa_bwd_pre_kernel + fa_bwd_dkdv_kernel<{_ELEM[w.dtype]}, {w.D}, "
                           f"{str(causal).lower()}> + fa_bwd_dq_kernel (rate over the three)")
@@ -225,7 +242,11 @@ def main():
         l_gpu = lse.to(torch.float64).cpu().numpy()
         reps, t0 = 0, time.perf_counter()
         while True:
-            o_ref, l_ref = orc.attention(x.q64, x.k64, x.v64, causal, w.scale)
+            if w.window >= 0:
+                o_ref, l_ref = orc.attention_masked(x.q64, x.k64, x.v64, causal, w.scale,
+                                                    w.window, w.global_tokens)
+            else:
+                o_ref, l_ref = orc.attention(x.q64, x.k64, x.v64, causal, w.scale)
             reps += 1
             el = time.perf_counter() - t0
             if el >= a.cpu_seconds:
@@ -248,7 +269,9 @@ def main():
                                f"causal={causal}",
                    "B": w.B, "H": w.H, "H_kv": w.H_kv, "T": w.T, "D": w.D,
                    "causal": causal, "layout": "BNHD", "parallelism": "single GPU",
-                   "nsplit": a.nsplit, "pass": a.which},
+                   "nsplit": a.nsplit, "pass": a.which,
+                   **({"window": w.window, "global_tokens": len(w.global_tokens)}
+                      if w.window >= 0 else {})},
         "flop_per_step": flops,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -71,6 +71,11 @@ struct FwdParams {
     // (fp32) and its logsumexp to lpart[s][b][h][t].
     int nsplit;
     float *opart, *lpart;
+    // Sliding-window / local-global mode: key j visible to query i iff
+    // |i - j| <= window (window clamped to T) or bit j%64 of gbits[j/64] is
+    // set (gbits NULL: no global tokens); causal still applies.
+    int window;
+    const unsigned long long *gbits;
 };
 
 template <bool B>
@@ -106,7 +111,7 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 // layout of fa_device.h: K is read as rows (kswz), V transposed for the V^T
 // operand of P.V (vswz).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool SPLIT>
+template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW>
 __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
@@ -161,6 +166,35 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     // Key tiles of this work-group: all of them, or split u.s's share.
     const int jbeg = SPLIT ? u.s * nkt / p.nsplit : 0;
     const int jend = SPLIT ? (u.s + 1) * nkt / p.nsplit : nkt;
+    // Window mode: the key tiles visited are those meeting the band
+    // [q0 - window, q_last + window] of this query tile (tiles blo..bhi) and
+    // those holding a global token; all others are never loaded.
+    int blo = 0, bhi = nkt - 1;
+    if (WINDOW) {
+        const long long q1 = min(u.q0 + kBQ, T) - 1;
+        blo = (int)(max(0LL, (long long)u.q0 - p.window) / BK);
+        bhi = (int)(min((long long)kend - 1, q1 + p.window) / BK);
+    }
+    // The next key tile after j this work-group visits (jend if none).
+    auto next_tile = [&](int j) __attribute__((always_inline)) -> int {
+        int t = j + 1;
+        if (!WINDOW) return t;
+        const unsigned long long *gbits = p.gbits;
+        if (t < blo) {
+            if (!gbits) return blo;
+            while (t < blo && gbits[t] == 0ull) ++t;
+            return t;
+        }
+        if (t <= bhi) return t;
+        if (gbits)
+            while (t < jend && gbits[t] == 0ull) ++t;
+        return min(t, jend);
+    };
+    // Global-token bits of tile t, read between steps (never after a step's
+    // prefetch is issued, whose loads a wait for this read would include).
+    auto tile_bits = [&](int t) __attribute__((always_inline)) -> unsigned long long {
+        return (WINDOW && p.gbits && t < jend) ? p.gbits[t] : 0ull;
+    };
 
     // Staging: this wave issues 1 KB loads wave, wave+4, ... of each tile.
     // Lane slot (row, physical chunk) -> global byte offset within the tile.
@@ -204,7 +238,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
     const bool wave_live = wq0 < T;
 
-    auto tile = [&](bool need_mask, int j, const unsigned char *kt, const unsigned char *vt) {
+    auto tile = [&](bool need_mask, int j, const unsigned char *kt, const unsigned char *vt,
+                    unsigned long long gb) {
         const int key0 = j * BK;
 
         // S^T tile: 64 keys x 32 queries as two 32x32 blocks.
@@ -221,11 +256,27 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
         // Element r of block kb is key key0 + 32kb + 8(r/4) + 4half + r%4.
         if (need_mask) {
             const int lim = (CAUSAL ? min(qrow, T - 1) : T - 1) - key0 - 4 * half;
+            if (WINDOW) {
+                // in the band: lo <= off <= hi; global: bit (off + 4half) of gb
+                const int lo = qrow - p.window - key0 - 4 * half;
+                const int hi = qrow + p.window - key0 - 4 * half;
+                const unsigned long long gl = gb >> (4 * half);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int off = 8 * (r >> 2) + (r & 3);
-                s0[r] = off <= lim ? s0[r] : -INFINITY;
-                s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    const bool v0 = off <= lim && ((off >= lo && off <= hi) || ((gl >> off) & 1ull));
+                    const bool v1 = off + 32 <= lim &&
+                                    ((off + 32 >= lo && off + 32 <= hi) || ((gl >> (off + 32)) & 1ull));
+                    s0[r] = v0 ? s0[r] : -INFINITY;
+                    s1[r] = v1 ? s1[r] : -INFINITY;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    s0[r] = off <= lim ? s0[r] : -INFINITY;
+                    s1[r] = off + 32 <= lim ? s1[r] : -INFINITY;
+                }
             }
         }
 
@@ -292,22 +343,50 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     // One barrier per tile: after it, tile j is in LDS for every wave and every
     // wave has finished reading the buffer that tile j+1 is loaded into. The
     // loop is unrolled by two so each step names its buffers statically.
-    auto step = [&](int j, const unsigned char *kt, const unsigned char *vt, unsigned char *kn,
-                    unsigned char *vn) {
+    auto step = [&](int j, unsigned long long gb, int jn, const unsigned char *kt,
+                    const unsigned char *vt, unsigned char *kn, unsigned char *vn) {
         __builtin_amdgcn_s_waitcnt(0);   // this lane's loads of tile j have landed
         __syncthreads();
-        if (j + 1 < jend)
-            stage_tile<D>(kbase, vbase, ks1, vs1, T, (j + 1) * BK, wave, koff, voff, kn, vn);
+        if (jn < jend)
+            stage_tile<D>(kbase, vbase, ks1, vs1, T, jn * BK, wave, koff, voff, kn, vn);
         const int key0 = j * BK;
-        const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
-        const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
-        if (active) tile(need_mask, j, kt, vt);
+        bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
+        if (WINDOW) {
+            // the band of this wave's 32 rows: [wq0 - window, wq0 + 31 + window]
+            const long long wlo = (long long)wq0 - p.window, whi = (long long)wq0 + 31 + p.window;
+            const bool meets = key0 + BK - 1 >= wlo && key0 <= whi;
+            // every row of the wave sees every key of the tile
+            const bool inside = key0 >= (long long)wq0 + 31 - p.window &&
+                                key0 + BK - 1 <= (long long)wq0 + p.window;
+            active = active && (meets || gb != 0ull);
+            need_mask = need_mask || !inside;
+        }
+        if (active) tile(need_mask, j, kt, vt, gb);
     };
-    if (jbeg < jend)
-        stage_tile<D>(kbase, vbase, ks1, vs1, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
-    for (int j = jbeg; j < jend; j += 2) {
-        step(j, k_lds0, v_lds0, k_lds1, v_lds1);
-        if (j + 1 < jend) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    if (WINDOW) {
+        int j = next_tile(-1);
+        unsigned long long gj = tile_bits(j);
+        if (j < jend)
+            stage_tile<D>(kbase, vbase, ks1, vs1, T, j * BK, wave, koff, voff, k_lds0, v_lds0);
+        while (j < jend) {
+            const int jn = next_tile(j);
+            const unsigned long long gn = tile_bits(jn);
+            step(j, gj, jn, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (jn >= jend) break;
+            const int jnn = next_tile(jn);
+            const unsigned long long gnn = tile_bits(jnn);
+            step(jn, gn, jnn, k_lds1, v_lds1, k_lds0, v_lds0);
+            j = jnn;
+            gj = gnn;
+        }
+    } else {
+        if (jbeg < jend)
+            stage_tile<D>(kbase, vbase, ks1, vs1, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
+        for (int j = jbeg; j < jend; j += 2) {
+            step(j, 0ull, j + 1, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (j + 1 < jend) step(j + 1, 0ull, j + 2, k_lds1, v_lds1, k_lds0, v_lds0);
+        }
     }
 
     if (!wave_live) return;
@@ -586,6 +665,24 @@ __global__ __launch_bounds__(256) void fa_lse_combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Per-key-tile bitmaps of the global tokens: word w has bit t set iff key
+// 64w + t is in the list. One thread per word scans the (short) list, so no
+// zeroing pass or atomics are needed; positions outside [0, T) match no word.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int n,
+                                                             unsigned long long *bits,
+                                                             int nwords) {
+    const int w = blockIdx.x * 256 + threadIdx.x;
+    if (w >= nwords) return;
+    unsigned long long word = 0ull;
+    for (int i = 0; i < n; ++i) {
+        const int j = idx[i];
+        if (j >= 0 && (j >> 6) == w) word |= 1ull << (j & 63);
+    }
+    bits[w] = word;
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation (no HIP calls), dispatch, launch.
 // ---------------------------------------------------------------------------
 constexpr long long kMaxOffset = 1LL << 62;
@@ -604,25 +701,25 @@ long long extent(const long long s[3], int B, int T, int heads, int D) {
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, bool WINDOW>
 void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
     if (dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT>), grid, dim3(kThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW>), grid,
+                           dim3(kThreads), 0, stream, p);
     else if (dtype == FA_DTYPE_F16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT>), grid, dim3(kThreads),
-                           0, stream, p);
-    else if (!SPLIT)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW>), grid,
+                           dim3(kThreads), 0, stream, p);
+    else if (!SPLIT && !WINDOW)
         hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
 }
 
-template <bool CAUSAL, bool SPLIT>
+template <bool CAUSAL, bool SPLIT, bool WINDOW = false>
 void launch_d(const FwdParams &p, int D, int dtype, dim3 grid, hipStream_t stream) {
     switch (D) {
-        case 16: launch<16, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
-        case 32: launch<32, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
-        case 64: launch<64, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
-        default: launch<128, CAUSAL, SPLIT>(p, dtype, grid, stream); break;
+        case 16: launch<16, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
+        case 32: launch<32, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
+        case 64: launch<64, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
+        default: launch<128, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
     }
 }
 
@@ -690,6 +787,8 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
     p.qsign = scale < 0.f ? (half16 ? 0x80008000u : 0x80000000u) : 0u;
     p.nsplit = 1;
     p.opart = p.lpart = nullptr;
+    p.window = 0;
+    p.gbits = nullptr;
     return FA_OK;
 }
 
@@ -833,6 +932,48 @@ extern "C" int fa_lse_combine(const float *o_parts, const float *lse_parts, int 
     contiguous_strides(T, H, D, os);
     return launch_combine(o_parts, lse_parts, n, B, H, T, D, o, os, lse, dtype,
                           (hipStream_t)stream);
+}
+
+extern "C" long long fa_fwd_window_workspace_bytes(int T) {
+    if (T < 0) return -1;
+    return 8LL * ((T + 63LL) / 64);
+}
+
+extern "C" int fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int B, int H, int H_kv, int T, int D, int causal, float scale,
+                             int dtype, int window, const int *global_tokens, int n_global,
+                             void *workspace, long long workspace_bytes, void *stream) {
+    long long qs[3], ks[3];
+    contiguous_strides(T, H, D, qs);
+    contiguous_strides(T, H_kv, D, ks);
+    FwdParams p;
+    bool empty;
+    const int st = prepare(q, k, v, o, lse, B, H, H_kv, T, D, scale, dtype, qs, ks, ks, qs, &p,
+                           &empty);
+    if (st != FA_OK) return st;
+    if (window < 0 || n_global < 0) return FA_ERR_BAD_SHAPE;
+    if (dtype == FA_DTYPE_F32) return FA_ERR_DTYPE;   // the masks run on the 16-bit kernel
+    if (empty) return FA_OK;
+    p.window = window < T ? window : T;   // a window of T already sees every key
+    if (n_global > 0) {
+        if (!global_tokens || !workspace) return FA_ERR_NULL_PTR;
+        if (workspace_bytes < fa_fwd_window_workspace_bytes(T)) return FA_ERR_WORKSPACE;
+        if (!aligned(workspace, 8) || !aligned(global_tokens, 4)) return FA_ERR_ALIGN;
+        p.gbits = (const unsigned long long *)workspace;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (p.gbits) {
+        const int nwords = (int)(fa_fwd_window_workspace_bytes(T) / 8);
+        hipLaunchKernelGGL(fa_global_bits_kernel, dim3((nwords + 255) / 256), dim3(256), 0, s,
+                           global_tokens, n_global, (unsigned long long *)workspace, nwords);
+        if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    }
+    const dim3 grid((unsigned)((long long)p.nbh * p.nq));
+    if (causal)
+        launch_d<true, false, true>(p, D, dtype, grid, s);
+    else
+        launch_d<false, false, true>(p, D, dtype, grid, s);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" const char *fa_status_str(int status) {

@@ -50,6 +50,11 @@ def _lib():
         lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
         lib.fa_lse_combine.restype = _I
+        lib.fa_fwd_window.argtypes = ([_VP] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _I,
+                                                              _VP, ctypes.c_longlong, _VP])
+        lib.fa_fwd_window.restype = _I
+        lib.fa_fwd_window_workspace_bytes.argtypes = [_I]
+        lib.fa_fwd_window_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _VP,
                                                         ctypes.c_longlong, _VP]
         lib.fa_bwd.restype = _I
@@ -215,6 +220,45 @@ def lse_combine(o_parts, lse_parts, dtype=torch.bfloat16):
     rc = _lib().fa_lse_combine(o_parts.data_ptr(), lse_parts.data_ptr(), n, B, H, T, D,
                                o.data_ptr(), lse.data_ptr(), _dtype_code(o), stream)
     _raise(rc, "fa_lse_combine")
+    return o, lse
+
+
+def fwd_window(q, k, v, window: int, global_tokens=None, causal: bool = False, scale=None,
+               workspace=None):
+    """Sliding-window / local-global attention forward (bfloat16 or float16,
+    contiguous BNHD): key j visible to query i iff |i - j| <= window or j is in
+    global_tokens, and j <= i when causal. global_tokens: None, a sequence of
+    ints, or an int32 tensor on q's device. Returns (o, lse) like fwd."""
+    _check(q, k, v)
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"fwd_window takes bfloat16 or float16 inputs, got {q.dtype}")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fwd_window needs contiguous [B,T,H,D] tensors")
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    g = None
+    if global_tokens is not None:
+        g = (global_tokens if isinstance(global_tokens, torch.Tensor)
+             else torch.tensor(list(global_tokens), dtype=torch.int32))
+        if g.dtype != torch.int32 or g.dim() != 1:
+            raise ValueError("global_tokens must be a 1-D int32 tensor or a sequence of ints")
+        g = g.to(q.device).contiguous()
+    n_global = 0 if g is None else g.numel()
+    if n_global and workspace is None:
+        workspace = torch.empty((int(_lib().fa_fwd_window_workspace_bytes(T)) or 8,),
+                                dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib().fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, H_kv, T, D, int(bool(causal)), float(scale),
+                              _dtype_code(q), int(window), g.data_ptr() if n_global else None,
+                              n_global, workspace.data_ptr() if workspace is not None else None,
+                              0 if workspace is None else
+                              workspace.numel() * workspace.element_size(), stream)
+    _raise(rc, "fa_fwd_window")
     return o, lse
 
 

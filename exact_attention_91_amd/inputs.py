@@ -22,6 +22,8 @@ attention layer of "Flash Attention Memory Optimization Explained"):
   gpt2_f16          the gpt2 workload in IEEE half (seed 1006)
   gpt2_b2, long_b1  gpt2 at B=2 and long at B=1 (one GPU's share of a batch
                     split over 8 GPUs), seeds 1007 and 1008
+  window            B=2 H=12 T=8192 D=64 bf16 causal, window 256 and global
+                    tokens 0..15 (seed 1009)
 Seeds: 1001, 1020+D, 1003, 1004, 1005 respectively. The backward pass takes an
 upstream gradient dO drawn the same way from the fourth child of the same seed.
 """
@@ -44,15 +46,34 @@ class Workload:
     causal: tuple       # mask settings this workload is run with
     seed: int
     qk_sigma: float = 1.0
+    window: int = -1            # >= 0: sliding-window / local-global mask
+    global_tokens: tuple = ()   # global key positions of that mask
 
     @property
     def scale(self) -> float:
         return default_scale(self.D)
 
     def flops(self, causal: bool) -> float:
-        """Counted FLOP: 4*B*H*T^2*D, halved when causal."""
+        """Counted FLOP: 4*B*H*T^2*D, halved when causal; under a window mask,
+        4*D per visible (query, key) pair."""
+        if self.window >= 0:
+            return 4.0 * self.B * self.H * self.D * visible_pairs(
+                self.T, self.window, self.global_tokens, causal)
         f = 4.0 * self.B * self.H * self.T * self.T * self.D
         return f / 2.0 if causal else f
+
+
+def visible_pairs(T: int, window: int, global_tokens, causal: bool) -> int:
+    """Number of (i, j) with |i - j| <= window or j global, and j <= i if causal."""
+    i = np.arange(T, dtype=np.int64)
+    lo = np.maximum(0, i - window)
+    hi = i if causal else np.minimum(T - 1, i + window)
+    hi = np.minimum(hi, i + window)
+    n = int(np.sum(hi - lo + 1))
+    for g in sorted(set(int(x) for x in global_tokens if 0 <= int(x) < T)):
+        rows = i[(np.abs(i - g) > window) & ((g <= i) if causal else True)]
+        n += len(rows)
+    return n
 
 
 def default_scale(D: int) -> float:
@@ -72,6 +93,10 @@ WORKLOADS = {
     # 8 GPUs: fewer work-groups than compute units (the key-split regime).
     "gpt2_b2": Workload("gpt2_b2", 2, 12, 12, 1024, 64, "bf16", (True,), 1007),
     "long_b1": Workload("long_b1", 1, 1, 1, 8192, 128, "bf16", (True,), 1008),
+    # Sliding window of 256 plus the first 16 tokens global, over an 8192-token
+    # sequence (the local-global pattern of the sparse-attention variants).
+    "window": Workload("window", 2, 12, 12, 8192, 64, "bf16", (True,), 1009, window=256,
+                       global_tokens=tuple(range(16))),
 }
 
 

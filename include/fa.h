@@ -156,6 +156,35 @@ int fa_lse_combine(const float *o_parts, const float *lse_parts, int n, int B, i
                    int T, int D, void *o, float *lse, int dtype, void *stream);
 
 /*
+ * Sparse-pattern forward (bf16 or fp16): the same computation with key j
+ * visible to query i iff
+ *   |i - j| <= window  or  j is one of the global tokens,
+ * and j <= i when causal -- the sliding-window and local-global masks of the
+ * yelogs.com Flash Attention2-in-Triton article (sparse-attention variants;
+ * the causal flag is applied on top). Key tiles that meet neither the band of
+ * a query tile nor a global token are skipped (never loaded).
+ *   window          >= 0 (FA_ERR_BAD_SHAPE otherwise); window >= T - 1 with
+ *                   no global tokens is fa_fwd.
+ *   global_tokens   device int32 array of n_global key positions (any order,
+ *                   duplicates allowed; positions outside [0, T) are
+ *                   ignored); may be NULL when n_global == 0.
+ *   workspace       device memory, 8-byte aligned, at least
+ *                   fa_fwd_window_workspace_bytes(T) bytes when n_global > 0
+ *                   (unused otherwise): per-64-key bitmaps of the global
+ *                   tokens, rebuilt by each call (calls sharing it must be
+ *                   ordered on one stream).
+ * Every row sees at least itself, so L is finite. Tensors, dtype (bf16 or
+ * fp16; fp32 returns FA_ERR_DTYPE), errors and precision as fa_fwd.
+ */
+int fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int B, int H, int H_kv, int T, int D, int causal, float scale,
+                  int dtype, int window, const int *global_tokens, int n_global,
+                  void *workspace, long long workspace_bytes, void *stream);
+
+/* Workspace bytes of fa_fwd_window: 8 * ceil(T / 64); -1 for T < 0. */
+long long fa_fwd_window_workspace_bytes(int T);
+
+/*
  * Attention backward: the gradients of the forward above for an upstream
  * gradient dO = dLoss/dO (the loss is taken not to depend on lse). The
  * forward's intermediates are recomputed from q, k and the stored lse instead
