@@ -30,7 +30,9 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s and % of MFMA peak (GPT-2 causal bf16 shape)"
 METRIC_BWD = "attention bwd TFLOP/s (5 contractions counted) and % of MFMA peak"
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA, TFLOP/s
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_91_amd", "csrc", "fa_fwd.hip")
+# the forward kernel's sources (its traffic figures are tied to their hash)
+KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_91_amd", "csrc", n)
+               for n in ("fa_fwd.hip", "fa_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_gpt2_traffic.json")
 _ELEM = {"bf16": "__bf16", "f16": "_Float16"}   # element type of the 16-bit kernel
 
@@ -60,8 +62,11 @@ def parse():
 
 
 def source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_for(workload_name):

@@ -666,20 +666,27 @@ __global__ __launch_bounds__(256) void fa_lse_combine_kernel(CombineParams p) {
 
 // ---------------------------------------------------------------------------
 // Per-key-tile bitmaps of the global tokens: word w has bit t set iff key
-// 64w + t is in the list. One thread per word scans the (short) list, so no
-// zeroing pass or atomics are needed; positions outside [0, T) match no word.
+// 64w + t is in the list. One thread per word scans the list, staged through
+// LDS 256 positions at a time (one coalesced load per chunk), so no zeroing
+// pass or atomics are needed; positions outside [0, T) match no word.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int n,
                                                              unsigned long long *bits,
                                                              int nwords) {
+    __shared__ int chunk[256];
     const int w = blockIdx.x * 256 + threadIdx.x;
-    if (w >= nwords) return;
     unsigned long long word = 0ull;
-    for (int i = 0; i < n; ++i) {
-        const int j = idx[i];
-        if (j >= 0 && (j >> 6) == w) word |= 1ull << (j & 63);
+    for (int base = 0; base < n; base += 256) {
+        const int m = min(256, n - base);
+        __syncthreads();                  // the previous chunk has been read
+        if ((int)threadIdx.x < m) chunk[threadIdx.x] = idx[base + threadIdx.x];
+        __syncthreads();
+        for (int i = 0; i < m; ++i) {
+            const int j = chunk[i];
+            if (j >= 0 && (j >> 6) == w) word |= 1ull << (j & 63);
+        }
     }
-    bits[w] = word;
+    if (w < nwords) bits[w] = word;
 }
 
 // ---------------------------------------------------------------------------

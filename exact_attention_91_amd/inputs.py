@@ -23,7 +23,8 @@ attention layer of "Flash Attention Memory Optimization Explained"):
   gpt2_b2, long_b1  gpt2 at B=2 and long at B=1 (one GPU's share of a batch
                     split over 8 GPUs), seeds 1007 and 1008
   window            B=2 H=12 T=8192 D=64 bf16 causal, window 256 and global
-                    tokens 0..15 (seed 1009)
+                    tokens 0..15 (seed 1009); window_dense: the same without
+                    the mask
 Seeds: 1001, 1020+D, 1003, 1004, 1005 respectively. The backward pass takes an
 upstream gradient dO drawn the same way from the fourth child of the same seed.
 """
@@ -97,6 +98,8 @@ WORKLOADS = {
     # sequence (the local-global pattern of the sparse-attention variants).
     "window": Workload("window", 2, 12, 12, 8192, 64, "bf16", (True,), 1009, window=256,
                        global_tokens=tuple(range(16))),
+    # the window workload's shape without the mask (plain causal attention)
+    "window_dense": Workload("window_dense", 2, 12, 12, 8192, 64, "bf16", (True,), 1009),
 }
 
 

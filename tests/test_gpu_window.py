@@ -47,6 +47,7 @@ CASES = [  # T, window, global tokens
     (1000, 257, (5, 500, 999)),
     (1000, 2000, ()),
     (777, 31, tuple(range(0, 777, 97))),
+    (1000, 20, tuple(range(1, 1000, 3))),      # 333 tokens: the list is staged in chunks
 ]
 
 
