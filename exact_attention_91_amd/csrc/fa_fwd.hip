@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256) void fa_lse_combine_kernel(CombineParams p) {
 // LDS 256 positions at a time (one coalesced load per chunk), so no zeroing
 // pass or atomics are needed; positions outside [0, T) match no word.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int n,
+__global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int n, int T,
                                                              unsigned long long *bits,
                                                              int nwords) {
     __shared__ int chunk[256];
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int
         __syncthreads();
         for (int i = 0; i < m; ++i) {
             const int j = chunk[i];
-            if (j >= 0 && (j >> 6) == w) word |= 1ull << (j & 63);
+            if (j >= 0 && j < T && (j >> 6) == w) word |= 1ull << (j & 63);
         }
     }
     if (w < nwords) bits[w] = word;
@@ -941,15 +941,29 @@ extern "C" int fa_lse_combine(const float *o_parts, const float *lse_parts, int 
                           (hipStream_t)stream);
 }
 
-extern "C" long long fa_fwd_window_workspace_bytes(int T) {
+extern "C" long long fa_window_bitmap_bytes(int T) {
     if (T < 0) return -1;
     return 8LL * ((T + 63LL) / 64);
 }
 
+extern "C" int fa_window_bitmap(const int *global_tokens, int n_global, int T, void *bits,
+                                long long bits_bytes, void *stream) {
+    if (n_global < 0 || T < 0) return FA_ERR_BAD_SHAPE;
+    if (T == 0) return FA_OK;
+    if (!bits || (n_global > 0 && !global_tokens)) return FA_ERR_NULL_PTR;
+    if (!aligned(bits, 8) || !aligned(global_tokens, 4)) return FA_ERR_ALIGN;
+    const long long need = fa_window_bitmap_bytes(T);
+    if (bits_bytes < need) return FA_ERR_WORKSPACE;
+    const int nwords = (int)(need / 8);
+    hipLaunchKernelGGL(fa_global_bits_kernel, dim3((nwords + 255) / 256), dim3(256), 0,
+                       (hipStream_t)stream, global_tokens, n_global, T,
+                       (unsigned long long *)bits, nwords);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 extern "C" int fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse,
                              int B, int H, int H_kv, int T, int D, int causal, float scale,
-                             int dtype, int window, const int *global_tokens, int n_global,
-                             void *workspace, long long workspace_bytes, void *stream) {
+                             int dtype, int window, const void *global_bits, void *stream) {
     long long qs[3], ks[3];
     contiguous_strides(T, H, D, qs);
     contiguous_strides(T, H_kv, D, ks);
@@ -958,24 +972,14 @@ extern "C" int fa_fwd_window(const void *q, const void *k, const void *v, void *
     const int st = prepare(q, k, v, o, lse, B, H, H_kv, T, D, scale, dtype, qs, ks, ks, qs, &p,
                            &empty);
     if (st != FA_OK) return st;
-    if (window < 0 || n_global < 0) return FA_ERR_BAD_SHAPE;
+    if (window < 0) return FA_ERR_BAD_SHAPE;
     if (dtype == FA_DTYPE_F32) return FA_ERR_DTYPE;   // the masks run on the 16-bit kernel
     if (empty) return FA_OK;
+    if (!aligned(global_bits, 8)) return FA_ERR_ALIGN;
     p.window = window < T ? window : T;   // a window of T already sees every key
-    if (n_global > 0) {
-        if (!global_tokens || !workspace) return FA_ERR_NULL_PTR;
-        if (workspace_bytes < fa_fwd_window_workspace_bytes(T)) return FA_ERR_WORKSPACE;
-        if (!aligned(workspace, 8) || !aligned(global_tokens, 4)) return FA_ERR_ALIGN;
-        p.gbits = (const unsigned long long *)workspace;
-    }
-    hipStream_t s = (hipStream_t)stream;
-    if (p.gbits) {
-        const int nwords = (int)(fa_fwd_window_workspace_bytes(T) / 8);
-        hipLaunchKernelGGL(fa_global_bits_kernel, dim3((nwords + 255) / 256), dim3(256), 0, s,
-                           global_tokens, n_global, (unsigned long long *)workspace, nwords);
-        if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
-    }
+    p.gbits = (const unsigned long long *)global_bits;
     const dim3 grid((unsigned)((long long)p.nbh * p.nq));
+    hipStream_t s = (hipStream_t)stream;
     if (causal)
         launch_d<true, false, true>(p, D, dtype, grid, s);
     else

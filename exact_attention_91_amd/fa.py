@@ -50,11 +50,12 @@ def _lib():
         lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
         lib.fa_lse_combine.restype = _I
-        lib.fa_fwd_window.argtypes = ([_VP] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _I,
-                                                              _VP, ctypes.c_longlong, _VP])
+        lib.fa_fwd_window.argtypes = ([_VP] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _VP])
         lib.fa_fwd_window.restype = _I
-        lib.fa_fwd_window_workspace_bytes.argtypes = [_I]
-        lib.fa_fwd_window_workspace_bytes.restype = ctypes.c_longlong
+        lib.fa_window_bitmap.argtypes = [_VP, _I, _I, _VP, ctypes.c_longlong, _VP]
+        lib.fa_window_bitmap.restype = _I
+        lib.fa_window_bitmap_bytes.argtypes = [_I]
+        lib.fa_window_bitmap_bytes.restype = ctypes.c_longlong
         lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _VP,
                                                         ctypes.c_longlong, _VP]
         lib.fa_bwd.restype = _I
@@ -223,12 +224,34 @@ def lse_combine(o_parts, lse_parts, dtype=torch.bfloat16):
     return o, lse
 
 
+def window_bitmap(global_tokens, T: int, device):
+    """Bitmap of the global tokens for fwd_window (uint8 tensor of
+    8*ceil(T/64) bytes on `device`), built by the library's kernel.
+    global_tokens: a sequence of ints or a 1-D int32 tensor."""
+    g = (global_tokens if isinstance(global_tokens, torch.Tensor)
+         else torch.tensor(list(global_tokens), dtype=torch.int32))
+    if g.dtype != torch.int32 or g.dim() != 1:
+        raise ValueError("global_tokens must be a 1-D int32 tensor or a sequence of ints")
+    g = g.to(device).contiguous()
+    nbytes = int(_lib().fa_window_bitmap_bytes(T))
+    if nbytes < 0:
+        raise ValueError(f"bad T {T}")
+    bits = torch.empty((max(nbytes, 8),), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    rc = _lib().fa_window_bitmap(g.data_ptr() if g.numel() else None, g.numel(), T,
+                                 bits.data_ptr(), bits.numel(), stream)
+    _raise(rc, "fa_window_bitmap")
+    return bits
+
+
 def fwd_window(q, k, v, window: int, global_tokens=None, causal: bool = False, scale=None,
-               workspace=None):
+               global_bits=None):
     """Sliding-window / local-global attention forward (bfloat16 or float16,
-    contiguous BNHD): key j visible to query i iff |i - j| <= window or j is in
-    global_tokens, and j <= i when causal. global_tokens: None, a sequence of
-    ints, or an int32 tensor on q's device. Returns (o, lse) like fwd."""
+    contiguous BNHD): key j visible to query i iff |i - j| <= window or j is a
+    global token, and j <= i when causal. The global tokens are given either
+    as `global_tokens` (a sequence of ints or an int32 tensor; the bitmap is
+    built for this call) or as a prebuilt `global_bits` from window_bitmap.
+    Returns (o, lse) like fwd."""
     _check(q, k, v)
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(f"fwd_window takes bfloat16 or float16 inputs, got {q.dtype}")
@@ -238,26 +261,20 @@ def fwd_window(q, k, v, window: int, global_tokens=None, causal: bool = False, s
     H_kv = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    g = None
+    if global_tokens is not None and global_bits is not None:
+        raise ValueError("give global_tokens or global_bits, not both")
     if global_tokens is not None:
-        g = (global_tokens if isinstance(global_tokens, torch.Tensor)
-             else torch.tensor(list(global_tokens), dtype=torch.int32))
-        if g.dtype != torch.int32 or g.dim() != 1:
-            raise ValueError("global_tokens must be a 1-D int32 tensor or a sequence of ints")
-        g = g.to(q.device).contiguous()
-    n_global = 0 if g is None else g.numel()
-    if n_global and workspace is None:
-        workspace = torch.empty((int(_lib().fa_fwd_window_workspace_bytes(T)) or 8,),
-                                dtype=torch.uint8, device=q.device)
+        global_bits = window_bitmap(global_tokens, T, q.device)
+    if global_bits is not None and global_bits.numel() * global_bits.element_size() < \
+            int(_lib().fa_window_bitmap_bytes(T)):
+        raise ValueError("global_bits is smaller than window_bitmap builds for this T")
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = _lib().fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                               lse.data_ptr(), B, H, H_kv, T, D, int(bool(causal)), float(scale),
-                              _dtype_code(q), int(window), g.data_ptr() if n_global else None,
-                              n_global, workspace.data_ptr() if workspace is not None else None,
-                              0 if workspace is None else
-                              workspace.numel() * workspace.element_size(), stream)
+                              _dtype_code(q), int(window),
+                              None if global_bits is None else global_bits.data_ptr(), stream)
     _raise(rc, "fa_fwd_window")
     return o, lse
 

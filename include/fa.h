@@ -163,26 +163,33 @@ int fa_lse_combine(const float *o_parts, const float *lse_parts, int n, int B, i
  * yelogs.com Flash Attention2-in-Triton article (sparse-attention variants;
  * the causal flag is applied on top). Key tiles that meet neither the band of
  * a query tile nor a global token are skipped (never loaded).
- *   window          >= 0 (FA_ERR_BAD_SHAPE otherwise); window >= T - 1 with
- *                   no global tokens is fa_fwd.
- *   global_tokens   device int32 array of n_global key positions (any order,
- *                   duplicates allowed; positions outside [0, T) are
- *                   ignored); may be NULL when n_global == 0.
- *   workspace       device memory, 8-byte aligned, at least
- *                   fa_fwd_window_workspace_bytes(T) bytes when n_global > 0
- *                   (unused otherwise): per-64-key bitmaps of the global
- *                   tokens, rebuilt by each call (calls sharing it must be
- *                   ordered on one stream).
+ *   window        >= 0 (FA_ERR_BAD_SHAPE otherwise); window >= T - 1 with no
+ *                 global tokens is fa_fwd.
+ *   global_bits   device bitmap of the global tokens as built by
+ *                 fa_window_bitmap for this T (bit j%64 of 64-bit word j/64
+ *                 set iff key j is global), 8-byte aligned; NULL = none. It
+ *                 is read only, so one bitmap serves every call (layer, head
+ *                 group, batch) with the same global tokens.
  * Every row sees at least itself, so L is finite. Tensors, dtype (bf16 or
  * fp16; fp32 returns FA_ERR_DTYPE), errors and precision as fa_fwd.
  */
 int fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse,
                   int B, int H, int H_kv, int T, int D, int causal, float scale,
-                  int dtype, int window, const int *global_tokens, int n_global,
-                  void *workspace, long long workspace_bytes, void *stream);
+                  int dtype, int window, const void *global_bits, void *stream);
 
-/* Workspace bytes of fa_fwd_window: 8 * ceil(T / 64); -1 for T < 0. */
-long long fa_fwd_window_workspace_bytes(int T);
+/*
+ * Build the global-token bitmap of fa_fwd_window: global_tokens is a device
+ * int32 array of n_global key positions (any order, duplicates allowed;
+ * positions outside [0, T) are ignored; NULL allowed when n_global == 0);
+ * bits is device memory of at least fa_window_bitmap_bytes(T) bytes, 8-byte
+ * aligned, fully overwritten. One kernel on `stream`. FA_ERR_WORKSPACE if
+ * bits_bytes is too small.
+ */
+int fa_window_bitmap(const int *global_tokens, int n_global, int T, void *bits,
+                     long long bits_bytes, void *stream);
+
+/* Bytes of the bitmap: 8 * ceil(T / 64); -1 for T < 0. */
+long long fa_window_bitmap_bytes(int T);
 
 /*
  * Attention backward: the gradients of the forward above for an upstream

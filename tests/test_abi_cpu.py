@@ -40,9 +40,9 @@ DT = _enum_values("fa_dtype_t")
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd",
                                      "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
-                                     "fa_fwd_strided", "fa_fwd_window",
-                                     "fa_fwd_window_workspace_bytes", "fa_lse_combine",
-                                     "fa_status_str", "fa_version"]
+                                     "fa_fwd_strided", "fa_fwd_window", "fa_lse_combine",
+                                     "fa_status_str", "fa_version", "fa_window_bitmap",
+                                     "fa_window_bitmap_bytes"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -295,31 +295,26 @@ def test_bwd_empty_call_is_a_noop(lib, kw):
 def call_window(lib, **kw):
     _host_only()
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=4, H_kv=2, T=100, D=64, causal=1, scale=0.125,
-             dtype=DT["FA_DTYPE_BF16"], window=16, g=P, ng=3, ws=P, ws_bytes=1 << 20)
+             dtype=DT["FA_DTYPE_BF16"], window=16, bits=P)
     a.update(kw)
     return lib.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"],
                              a["T"], a["D"], a["causal"], a["scale"], a["dtype"], a["window"],
-                             a["g"], a["ng"], a["ws"], a["ws_bytes"], None)
+                             a["bits"], None)
 
 
-def test_window_workspace_bytes(lib):
-    f = lib.fa_fwd_window_workspace_bytes
+def test_window_bitmap_bytes(lib):
+    f = lib.fa_window_bitmap_bytes
     assert f(100) == 16 and f(64) == 8 and f(65) == 16 and f(0) == 0 and f(-1) == -1
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(window=-1), "FA_ERR_BAD_SHAPE"),
-    (dict(ng=-1), "FA_ERR_BAD_SHAPE"),
     (dict(dtype=DT["FA_DTYPE_F32"]), "FA_ERR_DTYPE"),
     (dict(D=40), "FA_ERR_HEAD_DIM"),
     (dict(H=3, H_kv=2), "FA_ERR_HEADS"),
     (dict(scale=math.nan), "FA_ERR_SCALE"),
     (dict(q=None), "FA_ERR_NULL_PTR"),
-    (dict(g=None), "FA_ERR_NULL_PTR"),
-    (dict(ws=None), "FA_ERR_NULL_PTR"),
-    (dict(ws_bytes=15), "FA_ERR_WORKSPACE"),
-    (dict(ws=P + 4), "FA_ERR_ALIGN"),
-    (dict(g=P + 2), "FA_ERR_ALIGN"),
+    (dict(bits=P + 4), "FA_ERR_ALIGN"),
     (dict(o=P + 8), "FA_ERR_ALIGN"),
 ])
 def test_window_rejects(lib, kw, code):
@@ -327,5 +322,20 @@ def test_window_rejects(lib, kw, code):
 
 
 def test_window_empty_call_is_a_noop(lib):
-    assert call_window(lib, T=0, q=None, k=None, v=None, o=None, lse=None, g=None,
-                       ws=None) == ST["FA_OK"]
+    assert call_window(lib, T=0, q=None, k=None, v=None, o=None, lse=None,
+                       bits=None) == ST["FA_OK"]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, -1, 100, P, 16), "FA_ERR_BAD_SHAPE"),
+    ((P, 3, -1, P, 16), "FA_ERR_BAD_SHAPE"),
+    ((None, 3, 100, P, 16), "FA_ERR_NULL_PTR"),
+    ((P, 3, 100, None, 16), "FA_ERR_NULL_PTR"),
+    ((P, 3, 100, P + 4, 16), "FA_ERR_ALIGN"),
+    ((P + 2, 3, 100, P, 16), "FA_ERR_ALIGN"),
+    ((P, 3, 100, P, 15), "FA_ERR_WORKSPACE"),
+    ((None, 0, 0, None, 0), "FA_OK"),
+])
+def test_window_bitmap_rejects(lib, args, code):
+    _host_only()
+    assert lib.fa_window_bitmap(*args, None) == ST[code]

@@ -118,3 +118,36 @@ def test_workload_window():
     x = generate_workload(w)
     o, lse = run_window(x, True, w.scale, w.window, w.global_tokens)
     check(x, w.dtype, True, w.scale, w.window, w.global_tokens, o, lse, w.name)
+
+
+@pytest.mark.parametrize("T,tokens", [(1, [0]), (64, [63, 0, 63]), (65, [64]),
+                                      (1000, list(range(3, 1000, 7)) + [-1, 1000, 5000]),
+                                      (300, [])])
+def test_window_bitmap_bits(T, tokens):
+    """Bit j % 64 of word j // 64 is set iff j is a listed position in [0, T)."""
+    from exact_attention_91_amd import fa
+    bits = fa.window_bitmap(tokens, T, torch.device("cuda"))
+    torch.cuda.synchronize()
+    words = bits.cpu().numpy().view(np.uint64)
+    expect = np.zeros((T + 63) // 64, np.uint64)
+    for j in tokens:
+        if 0 <= j < T:
+            expect[j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    assert np.array_equal(words[:len(expect)], expect)
+
+
+def test_window_prebuilt_bitmap_reused():
+    """One bitmap serves several calls (two head groups, both masks) with the
+    same result as building it per call."""
+    from exact_attention_91_amd import fa
+    glob = (0, 1, 200, 511)
+    bits = fa.window_bitmap(glob, 512, torch.device("cuda"))
+    for seed, causal in ((9904, True), (9905, False)):
+        x = generate(1, 4, 2, 512, 64, "bf16", seed)
+        q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+        o1, l1 = fa.fwd_window(q, k, v, 33, global_bits=bits, causal=causal, scale=0.125)
+        o2, l2 = fa.fwd_window(q, k, v, 33, glob, causal=causal, scale=0.125)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        check(x, "bf16", causal, 0.125, 33, glob, o1.double().cpu().numpy(),
+              l1.double().cpu().numpy(), f"prebuilt causal={causal}")
