@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="bwd: time fa_bwd (gradients for a seeded dO, from the "
                          "forward's o and lse computed once before timing)")
+    ap.add_argument("--head-split", type=int, default=0,
+                    help="bwd: query-head parts of the dK/dV kernel (0: library choice)")
     ap.add_argument("--nsplit", type=int, default=1,
                     help="> 1: time fa_fwd_splitk (key split into this many parts "
                          "plus the logsumexp combine) instead of fa_fwd")
@@ -118,11 +120,11 @@ def main():
             raise RuntimeError(fa.status_str(rc))
         do = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)[0].cuda()
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        nbytes = fa.bwd_workspace_bytes(w.B, w.H, w.T)
+        nbytes = fa.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.T, w.D, a.head_split)
         ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
         bargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.H_kv,
-                 w.T, w.D, int(causal), w.scale, dcode, ws.data_ptr(), nbytes, sp)
+                 w.T, w.D, int(causal), w.scale, dcode, a.head_split, ws.data_ptr(), nbytes, sp)
 
         def step():
             rc = lib.fa_bwd(*bargs)

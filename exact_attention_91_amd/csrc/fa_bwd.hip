@@ -52,6 +52,12 @@ struct BwdParams {
     int nblk;               // 128-row tiles per sequence
     float c;                // scale * log2(e) (signed)
     float scale;
+    // Head split of the dK/dV kernel: work-group (key tile, b, g, part s)
+    // takes query heads [s*group/hsplit, (s+1)*group/hsplit) of kv head g.
+    // With hsplit > 1 each part writes fp32 sums (dK unscaled) to
+    // dkpart/dvpart [s][b][t][g][d], added in part order by the reduce kernel.
+    int hsplit;
+    float *dkpart, *dvpart;
 };
 
 // ---------------------------------------------------------------------------
@@ -123,8 +129,10 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
     const int nbg = p.B * p.H_kv;
-    const int tk = blockIdx.x / nbg;          // key tile; tile 0 (most work) first
-    const int bg = blockIdx.x - tk * nbg;
+    const int hs = blockIdx.x % p.hsplit;     // head part
+    const int id = blockIdx.x / p.hsplit;
+    const int tk = id / nbg;                  // key tile; tile 0 (most work) first
+    const int bg = id - tk * nbg;
     const int b = bg / p.H_kv, g = bg - b * p.H_kv;
     const int k0 = tk * kBlk;
     const int wk0 = k0 + 32 * wave;
@@ -193,11 +201,13 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     const int nqt_all = (T + BQ - 1) / BQ;
     const int i_beg = CAUSAL ? k0 / BQ : 0;
     const int nqt = nqt_all - i_beg;
-    const int nit = p.group * nqt;
+    const int h0 = g * p.group + hs * p.group / p.hsplit;      // this part's query heads
+    const int nh = g * p.group + (hs + 1) * p.group / p.hsplit - h0;
+    const int nit = nh * nqt;
 
     auto stage = [&](int it, unsigned char *qd, unsigned char *od, float *sd)
         __attribute__((always_inline)) {
-        const int h = g * p.group + it / nqt;
+        const int h = h0 + it / nqt;
         const int q0 = (i_beg + it % nqt) * BQ;
         const long long hoff = (long long)b * T * qrs + (long long)h * D;
         stage_tile<D>((const unsigned short *)p.q + hoff, (const unsigned short *)p.dout + hoff,
@@ -299,6 +309,27 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     if (!wave_live || key >= T) return;
     // dK^T / dV^T register r of block n is dim 32n + 8(r/4) + 4half + r%4.
     const long long off = ((long long)b * T + key) * krs + (long long)g * D;
+    if (p.hsplit > 1) {
+        // this part's fp32 sums; the reduce kernel adds the parts and scales dK
+        const long long poff = (long long)hs * p.B * T * krs + off;
+#pragma unroll
+        for (int n = 0; n < ND; ++n)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d = 32 * n + 8 * rg + 4 * half;
+                if (D >= 32 || d < D) {
+                    f32x4_t k4, v4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        k4[e] = dkacc[n][4 * rg + e];
+                        v4[e] = dvacc[n][4 * rg + e];
+                    }
+                    *(f32x4_t *)(p.dkpart + poff + d) = k4;
+                    *(f32x4_t *)(p.dvpart + poff + d) = v4;
+                }
+            }
+        return;
+    }
     unsigned short *dkrow = (unsigned short *)p.dk + off;
     unsigned short *dvrow = (unsigned short *)p.dv + off;
     const float sc = p.scale;
@@ -517,6 +548,32 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV from the head-split parts: dK = scale * sum_s dkpart[s], dV =
+// sum_s dvpart[s], parts added in order s = 0, 1, ... (deterministic). Each
+// thread handles four consecutive elements of the [B][T][H_kv][D] arrays.
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(BwdParams p, long long n) {
+    typedef E e4v __attribute__((ext_vector_type(4)));
+    // n = B * T * H_kv * D elements per part, a multiple of 4
+    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    f32x4_t k = {0.f, 0.f, 0.f, 0.f}, v = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.hsplit; ++s) {
+        k += *(const f32x4_t *)(p.dkpart + s * n + i);
+        v += *(const f32x4_t *)(p.dvpart + s * n + i);
+    }
+    e4v k4, v4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        k4[e] = (E)(k[e] * p.scale);
+        v4[e] = (E)v[e];
+    }
+    *(e4v *)((E *)p.dk + i) = k4;
+    *(e4v *)((E *)p.dv + i) = v4;
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation (no HIP calls), launch.
 // ---------------------------------------------------------------------------
 constexpr long long kMaxElems = 1LL << 62;
@@ -524,12 +581,34 @@ constexpr long long kMaxGridB = (1LL << 24) - 1;
 
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr % 16) == 0; }
 
-long long bwd_ws_bytes(int B, int H, int T) {
-    long long r;
-    if (__builtin_mul_overflow((long long)B * H, (long long)T, &r) ||
-        __builtin_mul_overflow(r, 8LL, &r))
+constexpr long long kTargetWG = 1024;   // dK/dV work-groups aimed for (4 per CU)
+
+// Head parts of the dK/dV kernel: the requested count (capped at the group
+// size) or, for 0, enough parts to bring the launch to kTargetWG work-groups.
+int head_parts(int B, int H, int H_kv, int T, int requested) {
+    const int group = H / H_kv;
+    if (requested > 0) return requested < group ? requested : group;
+    const long long nwg = (long long)B * H_kv * (((long long)T + kBlk - 1) / kBlk);
+    if (nwg <= 0) return 1;
+    const long long want = (kTargetWG + nwg - 1) / nwg;
+    return (int)(want < group ? want : group);
+}
+
+// Workspace: Delta and L2 (B*H*T floats each, padded to 16 bytes), then, with
+// hs > 1 head parts, the fp32 dK and dV parts (hs * B*T*H_kv*D floats each).
+// Sets *stat_bytes to the size of the first region; -1 on overflow.
+long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, long long *stat_bytes) {
+    long long rows, part, total;
+    if (__builtin_mul_overflow((long long)B * H, (long long)T, &rows) || rows > (1LL << 58))
         return -1;
-    return r;
+    const long long stat = (rows * 8 + 15) / 16 * 16;
+    if (stat_bytes) *stat_bytes = stat;
+    if (hs <= 1) return stat;
+    if (__builtin_mul_overflow((long long)B * T, (long long)H_kv * D, &part) ||
+        __builtin_mul_overflow(part, (long long)hs * 8, &part) ||
+        __builtin_add_overflow(stat, part, &total))
+        return -1;
+    return total;
 }
 
 template <typename E, int D, bool CAUSAL>
@@ -539,7 +618,13 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
     hipLaunchKernelGGL((fa_bwd_pre_kernel<E, D>), dim3((unsigned)((rows + rpb - 1) / rpb)),
                        dim3(256), 0, s, p);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL>),
-                       dim3((unsigned)((long long)p.B * p.H_kv * p.nblk)), dim3(kThreads), 0, s, p);
+                       dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit)),
+                       dim3(kThreads), 0, s, p);
+    if (p.hsplit > 1) {
+        const long long n = (long long)p.B * p.T * p.H_kv * D;
+        hipLaunchKernelGGL((fa_bwd_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
+                           dim3(256), 0, s, p, n);
+    }
     hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL>),
                        dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s, p);
 }
@@ -556,19 +641,22 @@ void launch_bwd_d(const BwdParams &p, int D, hipStream_t s) {
 
 }  // namespace
 
-extern "C" long long fa_bwd_workspace_bytes(int B, int H, int T) {
-    if (B < 0 || H < 1 || T < 0) return -1;
-    return bwd_ws_bytes(B, H, T);
+extern "C" long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D,
+                                            int head_split) {
+    if (B < 0 || H < 1 || H_kv < 1 || T < 0 || H % H_kv != 0 || head_split < 0 ||
+        (D != 16 && D != 32 && D != 64 && D != 128))
+        return -1;
+    return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split), nullptr);
 }
 
 extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
                       const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
                       int H, int H_kv, int T, int D, int causal, float scale, int dtype,
-                      void *workspace, long long workspace_bytes, void *stream) {
+                      int head_split, void *workspace, long long workspace_bytes, void *stream) {
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
         return FA_ERR_DTYPE;
     if (dtype == FA_DTYPE_F32) return FA_ERR_DTYPE;   // 16-bit MFMA kernels only
-    if (B < 0 || T < 0 || H < 1 || H_kv < 1) return FA_ERR_BAD_SHAPE;
+    if (B < 0 || T < 0 || H < 1 || H_kv < 1 || head_split < 0) return FA_ERR_BAD_SHAPE;
     if (H % H_kv != 0) return FA_ERR_HEADS;
     if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
     if (!isfinite(scale) || !isfinite(scale * kLog2e)) return FA_ERR_SCALE;
@@ -579,7 +667,9 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
     for (const void *ptr : ptrs)
         if (!aligned16(ptr)) return FA_ERR_ALIGN;
     if (((uintptr_t)lse % 4) != 0) return FA_ERR_ALIGN;
-    const long long need = bwd_ws_bytes(B, H, T);
+    const int hs = head_parts(B, H, H_kv, T, head_split);
+    long long stat_bytes = 0;
+    const long long need = bwd_ws_bytes(B, H, H_kv, T, D, hs, &stat_bytes);
     if (need < 0) return FA_ERR_OVERFLOW;
     if (workspace_bytes < need) return FA_ERR_WORKSPACE;
     // element counts, 32-bit staging ranges (64 rows of a tile) and grids
@@ -588,8 +678,11 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
         return FA_ERR_OVERFLOW;
     if ((63LL * H * D + D) * 2 >= (1LL << 31)) return FA_ERR_OVERFLOW;
     const long long nblk = ((long long)T + kBlk - 1) / kBlk;
-    if ((long long)B * H * nblk > kMaxGridB) return FA_ERR_OVERFLOW;
-    if ((long long)B * H * T / (256 / (D / 8)) + 1 > kMaxGridB) return FA_ERR_OVERFLOW;
+    if ((long long)B * H * nblk > kMaxGridB || (long long)B * H_kv * nblk * hs > kMaxGridB)
+        return FA_ERR_OVERFLOW;
+    if ((long long)B * H * T / (256 / (D / 8)) + 1 > kMaxGridB ||
+        (long long)B * T * H_kv * D / 1024 + 1 > kMaxGridB)
+        return FA_ERR_OVERFLOW;
 
     BwdParams p;
     p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
@@ -601,6 +694,12 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
     p.nblk = (int)nblk;
     p.c = scale * kLog2e;
     p.scale = scale;
+    p.hsplit = hs;
+    p.dkpart = p.dvpart = nullptr;
+    if (hs > 1) {
+        p.dkpart = (float *)((char *)workspace + stat_bytes);
+        p.dvpart = p.dkpart + (long long)hs * B * T * H_kv * D;
+    }
     hipStream_t s = (hipStream_t)stream;
     if (dtype == FA_DTYPE_BF16) {
         if (causal) launch_bwd_d<__bf16, true>(p, D, s);

@@ -56,10 +56,10 @@ def _lib():
         lib.fa_window_bitmap.restype = _I
         lib.fa_window_bitmap_bytes.argtypes = [_I]
         lib.fa_window_bitmap_bytes.restype = ctypes.c_longlong
-        lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _VP,
+        lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP,
                                                         ctypes.c_longlong, _VP]
         lib.fa_bwd.restype = _I
-        lib.fa_bwd_workspace_bytes.argtypes = [_I] * 3
+        lib.fa_bwd_workspace_bytes.argtypes = [_I] * 6
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_status_str.argtypes = [_I]
         lib.fa_status_str.restype = ctypes.c_char_p
@@ -279,19 +279,21 @@ def fwd_window(q, k, v, window: int, global_tokens=None, causal: bool = False, s
     return o, lse
 
 
-def bwd_workspace_bytes(B: int, H: int, T: int) -> int:
+def bwd_workspace_bytes(B: int, H: int, H_kv: int, T: int, D: int, head_split: int = 0) -> int:
     """Bytes of device workspace bwd needs (-1 for invalid sizes)."""
-    return int(_lib().fa_bwd_workspace_bytes(B, H, T))
+    return int(_lib().fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split))
 
 
-def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None):
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None,
+        head_split: int = 0):
     """Attention backward on contiguous BNHD tensors (bfloat16 or float16).
 
     q, o, dout: [B, T, H, D]; k, v: [B, T, H_kv, D]; lse: float32 [B, H, T]
     -- o and lse as returned by fwd for the same q, k, v, causal, scale.
     Returns (dq, dk, dv) shaped like q, k, v. `workspace` (optional): a
-    device tensor of at least bwd_workspace_bytes(B, H, T) bytes; allocated
-    here when None."""
+    device tensor of at least bwd_workspace_bytes(B, H, H_kv, T, D, head_split)
+    bytes; allocated here when None. head_split: parts the query heads of a
+    kv head are split into for the dK/dV kernel (0: the library's choice)."""
     _check(q, k, v)
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(f"bwd takes bfloat16 or float16 inputs, got {q.dtype}")
@@ -309,7 +311,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None)
     H_kv = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = bwd_workspace_bytes(B, H, T)
+    need = bwd_workspace_bytes(B, H, H_kv, T, D, head_split)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q)
@@ -319,7 +321,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None)
     rc = _lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H,
                        H_kv, T, D, int(bool(causal)), float(scale), _dtype_code(q),
-                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                       stream)
+                       int(head_split), workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), stream)
     _raise(rc, "fa_bwd")
     return dq, dk, dv

@@ -212,21 +212,29 @@ long long fa_window_bitmap_bytes(int T);
  * All contiguous, 16-byte aligned (lse 4-byte). Precision: P and dS are
  * rounded to the input type only as MFMA operands, everything else is fp32;
  * the outputs are rounded to nearest even. fp32 inputs return FA_ERR_DTYPE.
+ * head_split: the dK/dV kernel works per (128-key tile, kv head); with
+ * several query heads per kv head it can also split the group's heads into
+ * head_split parts (capped at H / H_kv) whose fp32 sums a reduce kernel adds
+ * in a fixed order (still deterministic). 0 lets the library choose (enough
+ * parts to occupy the GPU); 1 means no split; < 0 is FA_ERR_BAD_SHAPE.
  * workspace: caller-owned device memory, 16-byte aligned, at least
- * fa_bwd_workspace_bytes(B, H, T) bytes: float32 Delta [B][H][T] followed by
- * float32 lse * log2(e) [B][H][T]; overwritten (calls sharing a workspace
- * must be ordered on one stream); FA_ERR_WORKSPACE if too small. dq, dk, dv
- * must not overlap any input, the workspace or each other. Three kernels
- * are enqueued on `stream`.
+ * fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split) bytes: float32 Delta
+ * [B][H][T], float32 lse * log2(e) [B][H][T] (padded to 16 bytes), then with
+ * a head split the fp32 dK and dV parts; overwritten (calls sharing a
+ * workspace must be ordered on one stream); FA_ERR_WORKSPACE if too small.
+ * dq, dk, dv must not overlap any input, the workspace or each other. Three
+ * or four kernels are enqueued on `stream`.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
            const void *dout, void *dq, void *dk, void *dv, int B, int H, int H_kv, int T,
-           int D, int causal, float scale, int dtype, void *workspace,
+           int D, int causal, float scale, int dtype, int head_split, void *workspace,
            long long workspace_bytes, void *stream);
 
-/* Workspace bytes fa_bwd needs: 2 * B * H * T * 4; -1 for invalid sizes or
- * overflow. */
-long long fa_bwd_workspace_bytes(int B, int H, int T);
+/* Workspace bytes fa_bwd needs for these sizes and head_split (0 = the
+ * library's choice, as in fa_bwd): 8 * B * H * T rounded up to 16, plus
+ * 8 * parts * B * T * H_kv * D when the group's heads are split into parts > 1;
+ * -1 for invalid sizes or overflow. */
+long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D, int head_split);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_str(int status);

@@ -244,20 +244,31 @@ def test_lse_combine_rejects(lib, kw, code):
 def call_bwd(lib, **kw):
     _host_only()
     a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=2, H=4, H_kv=2, T=100,
-             D=64, causal=1, scale=0.125, dtype=DT["FA_DTYPE_BF16"], ws=P, ws_bytes=1 << 40)
+             D=64, causal=1, scale=0.125, dtype=DT["FA_DTYPE_BF16"], hsplit=1, ws=P,
+             ws_bytes=1 << 40)
     a.update(kw)
     return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
                       a["dv"], a["B"], a["H"], a["H_kv"], a["T"], a["D"], a["causal"],
-                      a["scale"], a["dtype"], a["ws"], a["ws_bytes"], None)
+                      a["scale"], a["dtype"], a["hsplit"], a["ws"], a["ws_bytes"], None)
 
 
 def test_bwd_workspace_bytes(lib):
     f = lib.fa_bwd_workspace_bytes
-    assert f(2, 4, 100) == 2 * 2 * 4 * 100 * 4
-    assert f(0, 4, 100) == 0
-    assert f(2, 0, 100) == -1
-    assert f(-1, 4, 100) == -1
-    assert f(1 << 30, 1 << 30, 1 << 30) == -1
+    stat = (2 * 4 * 100 * 8 + 15) // 16 * 16
+    assert f(2, 4, 2, 100, 64, 1) == stat                    # no head split
+    assert f(2, 4, 4, 100, 64, 0) == stat                    # one query head per kv head
+    # two parts: plus fp32 dK and dV parts of [2][B][T][H_kv][D]
+    assert f(2, 4, 2, 100, 64, 2) == stat + 2 * 2 * 100 * 2 * 64 * 8
+    assert f(2, 4, 2, 100, 64, 9) == f(2, 4, 2, 100, 64, 2)  # capped at the group size
+    # the library's choice for 2 key tiles x 2 kv heads x B=2: 8 work-groups -> all 2 parts
+    assert f(2, 4, 2, 200, 64, 0) == f(2, 4, 2, 200, 64, 2)
+    assert f(0, 4, 2, 100, 64, 0) == 0
+    assert f(2, 0, 1, 100, 64, 0) == -1
+    assert f(2, 4, 3, 100, 64, 0) == -1                      # H % H_kv
+    assert f(2, 4, 2, 100, 48, 0) == -1                      # head dim
+    assert f(2, 4, 2, 100, 64, -1) == -1
+    assert f(-1, 4, 2, 100, 64, 0) == -1
+    assert f(1 << 30, 1 << 30, 1, 1 << 30, 64, 1) == -1
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -265,6 +276,7 @@ def test_bwd_workspace_bytes(lib):
     (dict(dtype=5), "FA_ERR_DTYPE"),
     (dict(B=-1), "FA_ERR_BAD_SHAPE"),
     (dict(H_kv=0), "FA_ERR_BAD_SHAPE"),
+    (dict(hsplit=-1), "FA_ERR_BAD_SHAPE"),
     (dict(H=6, H_kv=4), "FA_ERR_HEADS"),
     (dict(D=48), "FA_ERR_HEAD_DIM"),
     (dict(scale=math.inf), "FA_ERR_SCALE"),
@@ -278,6 +290,7 @@ def test_bwd_workspace_bytes(lib):
     (dict(ws=P + 4), "FA_ERR_ALIGN"),
     (dict(lse=P + 2), "FA_ERR_ALIGN"),
     (dict(ws_bytes=2 * 2 * 4 * 100 * 4 - 1), "FA_ERR_WORKSPACE"),
+    (dict(hsplit=2, ws_bytes=2 * 2 * 4 * 100 * 4 + 1000), "FA_ERR_WORKSPACE"),
     (dict(B=1 << 20, H=1 << 10, H_kv=1, T=1 << 12, ws_bytes=1 << 62), "FA_ERR_OVERFLOW"),
     (dict(B=1, H=1 << 18, H_kv=1, T=64, D=128), "FA_ERR_OVERFLOW"),   # 64-row tile > 2 GiB
 ])
