@@ -212,8 +212,9 @@ def main():
                           f"false, true> (window)")
         roof["traffic"] = None
     if a.which == "bwd":
-        roof["kernel"] = (f"fa_bwd_pre_kernel + fa_bwd_dkdv_kernel<{_ELEM[w.dtype]}, {w.D}, "
-                          f"{str(causal).lower()}> + fa_bwd_dq_kernel (rate over the three)")
+        roof["kernel"] = (f"fa_bwd_dq_kernel + fa_bwd_dkdv_kernel<{_ELEM[w.dtype]}, {w.D}, "
+                          f"{str(causal).lower()}> (+ fa_bwd_reduce_kernel with a head split; "
+                          f"rate over the step)")
         roof["traffic"] = None
     if a.nsplit > 1:
         # one step = the split kernel plus the combine kernel; the rate is over both

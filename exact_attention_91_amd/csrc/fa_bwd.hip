@@ -9,9 +9,8 @@
 //   P = exp(scale QK^T - L),  dV = P^T dO,  dP = dO V^T,
 //   dS = P o (dP - Delta),  Delta_i = dO_i . O_i,  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// gfx950 design (three kernels on one stream, no atomics, deterministic):
-//  * fa_bwd_pre_kernel: Delta = rowsum(dO o O) and L2 = L log2(e) per row,
-//    into the caller's workspace (HBM-bound, one pass over O and dO).
+// gfx950 design (two kernels on one stream, three with a head split; no
+// atomics, deterministic):
 //  * fa_bwd_dkdv_kernel: one work-group per 128-key tile of one (batch, kv
 //    head); each wave keeps its 32 keys' K and V rows in registers as MFMA
 //    operands and its dK, dV accumulators in registers for the whole loop,
@@ -20,11 +19,13 @@
 //    S = Q K^T, so a lane owns one key column: P and dS feed the B operand of
 //    dV^T += dO^T P and dK^T += Q^T dS straight from registers, with dO^T and
 //    Q^T read from the same LDS tiles by transposing reads.
-//  * fa_bwd_dq_kernel: the forward's decomposition (one work-group per
-//    128-row query tile, heaviest causal tiles first); each wave keeps its 32
-//    query rows of Q and dO in registers, streams K and V tiles, computes
-//    S^T = K Q^T and dP^T = V dO^T, and accumulates dQ^T += K^T dS^T with K^T
-//    from transposing reads of the K tile.
+//  * fa_bwd_dq_kernel (first): the forward's decomposition (one work-group
+//    per 128-row query tile, heaviest causal tiles first); each wave keeps
+//    its 32 query rows of Q and dO in registers, forms Delta = rowsum(dO o O)
+//    and L2 = L log2(e) for them (stored in the workspace for the dK/dV
+//    kernel), streams K and V tiles, computes S^T = K Q^T and dP^T = V dO^T,
+//    and accumulates dQ^T += K^T dS^T with K^T from transposing reads of the
+//    K tile.
 //  Tiles read both as rows and transposed use the dual swizzle (dswz) of
 //  fa_device.h. Causal: key tiles wholly after a query tile are never loaded;
 //  query tiles wholly before a key tile are never loaded; waves skip the math
@@ -59,39 +60,6 @@ struct BwdParams {
     int hsplit;
     float *dkpart, *dvpart;
 };
-
-// ---------------------------------------------------------------------------
-// Delta_i = sum_d dO[i,d] O[i,d] (fp32) and L2_i = L_i log2(e), per row
-// (b, h, t), stored at (b*H + h)*T + t. D/8 threads per row, 8 elements each.
-// ---------------------------------------------------------------------------
-template <typename E, int D>
-__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
-    using H16 = Half16<E>;
-    typedef typename H16::v8 e8_t;
-    constexpr int TPR = D / 8;
-    const long long rows = (long long)p.B * p.H * p.T;
-    const long long row = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-    const int part = threadIdx.x % TPR;
-    float acc = 0.f;
-    if (row < rows) {
-        const int t = (int)(row % p.T);
-        const long long bh = row / p.T;
-        const int h = (int)(bh % p.H), b = (int)(bh / p.H);
-        const long long off = (((long long)b * p.T + t) * p.H + h) * D + 8 * part;
-        const e8_t ov = __builtin_bit_cast(e8_t, *(const u32x4_t *)((const unsigned short *)p.o + off));
-        const e8_t dv =
-            __builtin_bit_cast(e8_t, *(const u32x4_t *)((const unsigned short *)p.dout + off));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)ov[e], (float)dv[e], acc);
-    }
-    // TPR consecutive lanes hold one row (TPR divides the wave size).
-#pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (row < rows && part == 0) {
-        p.delta[row] = acc;
-        p.l2[row] = p.lse[row] * kLog2e;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // dK, dV. Work-group: keys [k0, k0 + 128) of kv head g of batch b, wave w
@@ -411,11 +379,31 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
             df[ks] = __builtin_bit_cast(e8_t, y);
         }
     }
+    // Delta = dO . O of this lane's row (the two halves of the row live in
+    // lanes col and col + 32) and L2 = L log2(e): used here and stored in the
+    // workspace for the dK/dV kernel, which runs after this one.
     float l2 = 0.f, dl = 0.f;
-    if (qrow < T) {
-        const long long r = ((long long)b * p.H + h) * T + qrow;
-        l2 = p.l2[r];
-        dl = p.delta[r];
+    {
+        const long long off = ((long long)b * T + qrow) * qrs + (long long)h * D + 8 * half;
+        float part = 0.f;
+        if (qrow < T) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const e8_t ov = __builtin_bit_cast(
+                    e8_t, *(const u32x4_t *)((const unsigned short *)p.o + off + 16 * ks));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part = fmaf((float)ov[e], (float)df[ks][e], part);
+            }
+        }
+        dl = half_swap_sum(part);
+        if (qrow < T) {
+            const long long r = ((long long)b * p.H + h) * T + qrow;
+            l2 = p.lse[r] * kLog2e;
+            if (half == 0) {
+                p.delta[r] = dl;
+                p.l2[r] = l2;
+            }
+        }
     }
 
     const int kend = CAUSAL ? min(T, q0 + kBlk) : T;
@@ -611,12 +599,11 @@ long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, long long *
     return total;
 }
 
+// dQ first: it also writes Delta and L2, which the dK/dV kernel reads.
 template <typename E, int D, bool CAUSAL>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
-    const long long rows = (long long)p.B * p.H * p.T;
-    const long long rpb = 256 / (D / 8);
-    hipLaunchKernelGGL((fa_bwd_pre_kernel<E, D>), dim3((unsigned)((rows + rpb - 1) / rpb)),
-                       dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL>),
+                       dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL>),
                        dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit)),
                        dim3(kThreads), 0, s, p);
@@ -625,8 +612,6 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
         hipLaunchKernelGGL((fa_bwd_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
                            dim3(256), 0, s, p, n);
     }
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL>),
-                       dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s, p);
 }
 
 template <typename E, bool CAUSAL>
@@ -680,8 +665,7 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
     const long long nblk = ((long long)T + kBlk - 1) / kBlk;
     if ((long long)B * H * nblk > kMaxGridB || (long long)B * H_kv * nblk * hs > kMaxGridB)
         return FA_ERR_OVERFLOW;
-    if ((long long)B * H * T / (256 / (D / 8)) + 1 > kMaxGridB ||
-        (long long)B * T * H_kv * D / 1024 + 1 > kMaxGridB)
+    if ((long long)B * T * H_kv * D / 1024 + 1 > kMaxGridB)
         return FA_ERR_OVERFLOW;
 
     BwdParams p;

@@ -222,8 +222,8 @@ long long fa_window_bitmap_bytes(int T);
  * [B][H][T], float32 lse * log2(e) [B][H][T] (padded to 16 bytes), then with
  * a head split the fp32 dK and dV parts; overwritten (calls sharing a
  * workspace must be ordered on one stream); FA_ERR_WORKSPACE if too small.
- * dq, dk, dv must not overlap any input, the workspace or each other. Three
- * or four kernels are enqueued on `stream`.
+ * dq, dk, dv must not overlap any input, the workspace or each other. Two
+ * kernels (three with a head split) are enqueued on `stream`.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
            const void *dout, void *dq, void *dk, void *dv, int B, int H, int H_kv, int T,
