@@ -31,6 +31,8 @@ attention_bwd(q, k, v, dout, causal, scale)
                                          gradients (dq, dk, dv) of the same
                                          definition for upstream gradient dO,
                                          every intermediate recomputed (C).
+attention_bwd_masked(q, k, v, dout, causal, scale, window, global_tokens)
+                                         gradients of attention_masked (C).
 brute_force(q, k, v, causal, scale)      pure Python, hand-expanded exponentials
                                          summed with math.fsum, no max
                                          subtraction; for T <= 8 only.
@@ -83,6 +85,9 @@ def _lib():
         lib.oracle_attn_masked_f64.restype = ctypes.c_int
         lib.oracle_attn_bwd_f64.argtypes = common + [_DP, _DP, _DP, _DP] + shape
         lib.oracle_attn_bwd_f64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_masked_f64.argtypes = (common + [_DP, _DP, _DP, _DP] + shape +
+                                                   [ctypes.c_int, ctypes.c_void_p])
+        lib.oracle_attn_bwd_masked_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         _LIB = lib
@@ -228,6 +233,29 @@ def attention_bwd(q, k, v, dout, causal: bool, scale: float):
                                     _ptr(dv), B, H, H_kv, T, D, int(bool(causal)), float(scale))
     if rc:
         raise RuntimeError(f"oracle_attn_bwd_f64 failed ({rc})")
+    return dq, dk, dv
+
+
+def attention_bwd_masked(q, k, v, dout, causal: bool, scale: float, window: int,
+                         global_tokens=()):
+    """Gradients of attention_masked (same visible sets) for upstream gradient
+    dout. Returns (dq, dk, dv) like attention_bwd."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    flags = np.zeros(T, np.uint8)
+    for j in global_tokens:
+        if not 0 <= int(j) < T:
+            raise ValueError(f"global token {j} outside [0, {T})")
+        flags[int(j)] = 1
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    rc = _lib().oracle_attn_bwd_masked_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+                                           _ptr(dk), _ptr(dv), B, H, H_kv, T, D,
+                                           int(bool(causal)), float(scale), int(window),
+                                           flags.ctypes.data)
+    if rc:
+        raise RuntimeError(f"oracle_attn_bwd_masked_f64 failed ({rc})")
     return dq, dk, dv
 
 

@@ -71,6 +71,8 @@
  *     dQ_i  = scale sum_j dS_ij k_j      dK_j += scale dS_ij q_i
  * with dK and dV of a kv head summed over the query heads that share it. It
  * uses neither L nor the identity sum_k P_ik dP_ik = dO_i . O_i.
+ * oracle_attn_bwd_masked_f64 is the same over the visible sets of the
+ * sliding-window / local-global masks.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math, no BLAS).
  */
@@ -400,20 +402,24 @@ int oracle_attn_masked_f64(const double *q, const double *k, const double *v,
     return fail ? -2 : 0;
 }
 
-/* Gradients of full attention. dout, dq: [B, T, H, D]; dk, dv: [B, T, H_kv, D]
- * (overwritten). Parallel over (batch, kv head); each task owns the dk/dv rows
- * of its kv head, so no two tasks write the same element. */
-int oracle_attn_bwd_f64(const double *q, const double *k, const double *v, const double *dout,
-                        double *dq, double *dk, double *dv,
-                        int B, int H, int H_kv, int T, int D, int causal, double scale) {
+/* Gradients of attention over each row's visible keys: j <= i when causal
+ * and, when window >= 0, |i - j| <= window or is_global[j] (is_global may be
+ * NULL). dout, dq: [B, T, H, D]; dk, dv: [B, T, H_kv, D] (overwritten).
+ * Parallel over (batch, kv head); each task owns the dk/dv rows of its kv
+ * head, so no two tasks write the same element. A row with no visible key
+ * (impossible for window >= 0) contributes nothing. */
+static int attn_bwd(const double *q, const double *k, const double *v, const double *dout,
+                    double *dq, double *dk, double *dv, int B, int H, int H_kv, int T, int D,
+                    int causal, double scale, int window, const unsigned char *is_global) {
     if (bad_args(B, H, H_kv, T, D)) return -1;
     const int group = H / H_kv;
     int fail = 0;
 #pragma omp parallel
     {
+        int *vis = (int *)malloc(sizeof(int) * (size_t)T);
         double *p = (double *)malloc(sizeof(double) * (size_t)T);
         double *dp = (double *)malloc(sizeof(double) * (size_t)T);
-        if (!p || !dp) {
+        if (!vis || !p || !dp) {
 #pragma omp atomic write
             fail = 1;
         } else {
@@ -427,53 +433,81 @@ int oracle_attn_bwd_f64(const double *q, const double *k, const double *v, const
                     }
                 for (int h = g * group; h < (g + 1) * group; ++h)
                     for (int i = 0; i < T; ++i) {
-                        const int nvis = causal ? i + 1 : T;
+                        /* the visible keys of row i */
+                        int n = 0;
+                        for (int j = 0; j < T; ++j) {
+                            const int causal_ok = !causal || j <= i;
+                            const int local = window < 0 ||
+                                              ((i - j <= window) && (j - i <= window));
+                            const int glob = window >= 0 && is_global && is_global[j];
+                            if (causal_ok && (local || glob)) vis[n++] = j;
+                        }
                         const double *qi = q + qidx(b, i, h, H, T, D);
                         const double *doi = dout + qidx(b, i, h, H, T, D);
-                        /* forward recomputed: scores, max, normaliser, P */
-                        double m = -INFINITY;
-                        for (int j = 0; j < nvis; ++j) {
-                            const double *kj = k + qidx(b, j, g, H_kv, T, D);
-                            double dot = 0.0;
-                            for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
-                            p[j] = scale * dot;
-                            if (p[j] > m) m = p[j];
-                        }
-                        double z = 0.0;
-                        for (int j = 0; j < nvis; ++j) {
-                            p[j] = exp(p[j] - m);
-                            z += p[j];
-                        }
-                        for (int j = 0; j < nvis; ++j) p[j] /= z;
-                        /* dP and the softmax Jacobian's row term */
-                        double rowdot = 0.0;
-                        for (int j = 0; j < nvis; ++j) {
-                            const double *vj = v + qidx(b, j, g, H_kv, T, D);
-                            double dot = 0.0;
-                            for (int d = 0; d < D; ++d) dot += doi[d] * vj[d];
-                            dp[j] = dot;
-                            rowdot += p[j] * dot;
-                        }
                         double *dqi = dq + qidx(b, i, h, H, T, D);
                         for (int d = 0; d < D; ++d) dqi[d] = 0.0;
-                        for (int j = 0; j < nvis; ++j) {
-                            const double ds = p[j] * (dp[j] - rowdot);
-                            const double *kj = k + qidx(b, j, g, H_kv, T, D);
-                            double *dkj = dk + qidx(b, j, g, H_kv, T, D);
-                            double *dvj = dv + qidx(b, j, g, H_kv, T, D);
+                        if (n == 0) continue;
+                        /* forward recomputed: scores, max, normaliser, P */
+                        double m = -INFINITY;
+                        for (int t = 0; t < n; ++t) {
+                            const double *kj = k + qidx(b, vis[t], g, H_kv, T, D);
+                            double dot = 0.0;
+                            for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+                            p[t] = scale * dot;
+                            if (p[t] > m) m = p[t];
+                        }
+                        double z = 0.0;
+                        for (int t = 0; t < n; ++t) {
+                            p[t] = exp(p[t] - m);
+                            z += p[t];
+                        }
+                        for (int t = 0; t < n; ++t) p[t] /= z;
+                        /* dP and the softmax Jacobian's row term */
+                        double rowdot = 0.0;
+                        for (int t = 0; t < n; ++t) {
+                            const double *vj = v + qidx(b, vis[t], g, H_kv, T, D);
+                            double dot = 0.0;
+                            for (int d = 0; d < D; ++d) dot += doi[d] * vj[d];
+                            dp[t] = dot;
+                            rowdot += p[t] * dot;
+                        }
+                        for (int t = 0; t < n; ++t) {
+                            const double ds = p[t] * (dp[t] - rowdot);
+                            const double *kj = k + qidx(b, vis[t], g, H_kv, T, D);
+                            double *dkj = dk + qidx(b, vis[t], g, H_kv, T, D);
+                            double *dvj = dv + qidx(b, vis[t], g, H_kv, T, D);
                             for (int d = 0; d < D; ++d) {
                                 dqi[d] += scale * ds * kj[d];
                                 dkj[d] += scale * ds * qi[d];
-                                dvj[d] += p[j] * doi[d];
+                                dvj[d] += p[t] * doi[d];
                             }
                         }
                     }
             }
         }
+        free(vis);
         free(p);
         free(dp);
     }
     return fail ? -2 : 0;
+}
+
+/* Gradients of full attention (causal or not). */
+int oracle_attn_bwd_f64(const double *q, const double *k, const double *v, const double *dout,
+                        double *dq, double *dk, double *dv,
+                        int B, int H, int H_kv, int T, int D, int causal, double scale) {
+    return attn_bwd(q, k, v, dout, dq, dk, dv, B, H, H_kv, T, D, causal, scale, -1, NULL);
+}
+
+/* Gradients of the sliding-window / local-global attention of
+ * oracle_attn_masked_f64 (window >= 0). */
+int oracle_attn_bwd_masked_f64(const double *q, const double *k, const double *v,
+                               const double *dout, double *dq, double *dk, double *dv,
+                               int B, int H, int H_kv, int T, int D, int causal, double scale,
+                               int window, const unsigned char *is_global) {
+    if (window < 0) return -1;
+    return attn_bwd(q, k, v, dout, dq, dk, dv, B, H, H_kv, T, D, causal, scale, window,
+                    is_global);
 }
 
 int oracle_num_threads(void) {

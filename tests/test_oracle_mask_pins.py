@@ -108,3 +108,93 @@ def test_m7_bad_arguments(oracle):
         oracle.attention_masked(q, k, v, False, 1.0, 2, global_tokens=(8,))
     with pytest.raises(RuntimeError):
         oracle.attention_masked(q, k, v, False, 1.0, -1)
+
+
+# ------------------------------------------------- gradients under the masks
+
+def _rand_do(q, seed):
+    return np.random.default_rng(seed).standard_normal(q.shape)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mb1_wide_window_is_plain_backward(oracle, causal):
+    q, k, v = _rand(2, 4, 2, 37, 8, seed=1201)
+    do = _rand_do(q, 1202)
+    a = oracle.attention_bwd_masked(q, k, v, do, causal, 0.3, 36)
+    b = oracle.attention_bwd(q, k, v, do, causal, 0.3)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window,glob", [(1, ()), (2, (0, 6)), (0, (3,))])
+def test_mb2_finite_differences(oracle, causal, window, glob):
+    """Central differences of loss = sum(O * dO) through the pinned masked
+    forward."""
+    B, H, T, D = 1, 2, 7, 3
+    q, k, v = _rand(B, H, 1, T, D, seed=1203 + window)
+    do = _rand_do(q, 1204)
+    scale = 0.8
+    grads = oracle.attention_bwd_masked(q, k, v, do, causal, scale, window, glob)
+
+    def loss(q, k, v):
+        o, _ = oracle.attention_masked(q, k, v, causal, scale, window, glob)
+        return float(np.sum(o * do))
+
+    h = 1e-5
+    for name, g in zip(("q", "k", "v"), grads):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*g.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = args[name].copy(), args[name].copy()
+            xp[idx] += h
+            xm[idx] -= h
+            num[idx] = (loss(**dict(args, **{name: xp})) -
+                        loss(**dict(args, **{name: xm}))) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=0, atol=2e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mb3_torch_autograd_with_explicit_mask(oracle, causal):
+    """torch float64 autograd through the naive module with the mask built
+    from the pages' predicates (|i - j| <= w or isin(j, globals), and j <= i
+    when causal) as a masked_fill of -inf."""
+    import torch
+    B, H, H_kv, T, D = 2, 4, 2, 41, 16
+    window, glob = 5, (0, 20, 40)
+    q, k, v = _rand(B, H, H_kv, T, D, seed=1205, sigma=1.5)
+    do = _rand_do(q, 1206)
+    scale = 0.25
+    dq, dk, dv = oracle.attention_bwd_masked(q, k, v, do, causal, scale, window, glob)
+    g = H // H_kv
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    qh = tq.permute(0, 2, 1, 3)
+    kh = tk.permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    vh = tv.permute(0, 2, 1, 3).repeat_interleave(g, dim=1)
+    s = scale * torch.matmul(qh, kh.transpose(-1, -2).contiguous())
+    qi = torch.arange(T)[:, None]
+    kj = torch.arange(T)[None, :]
+    visible = (torch.abs(qi - kj) <= window) | torch.isin(kj, torch.tensor(glob))
+    if causal:
+        visible = visible & (kj <= qi)
+    p = torch.softmax(s.masked_fill(~visible, float("-inf")), dim=-1)
+    o = torch.matmul(p, vh).permute(0, 2, 1, 3)
+    o.backward(torch.tensor(do))
+    for name, a, b in (("dq", dq, tq.grad.numpy()), ("dk", dk, tk.grad.numpy()),
+                       ("dv", dv, tv.grad.numpy())):
+        np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mb4_invariants(oracle, causal):
+    """Each row's softmax over its visible keys is shift invariant and sums to
+    1: dK of a kv head sums to zero, dV sums to the group's dO."""
+    B, H, H_kv, T, D = 1, 4, 2, 50, 8
+    q, k, v = _rand(B, H, H_kv, T, D, seed=1207)
+    do = _rand_do(q, 1208)
+    dq, dk, dv = oracle.attention_bwd_masked(q, k, v, do, causal, 0.4, 4, (0, 25))
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, rtol=0, atol=1e-12)
+    do_groups = do.reshape(B, T, H_kv, H // H_kv, D).sum(axis=3).sum(axis=1)
+    np.testing.assert_allclose(dv.sum(axis=1), do_groups, rtol=0, atol=1e-12)
