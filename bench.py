@@ -115,7 +115,15 @@ def main():
         from exact_attention_91_amd.inputs import generate_dout
         if a.nsplit > 1:
             raise SystemExit("--nsplit applies to the forward only")
-        rc = lib.fa_fwd(*args)
+        bits = None
+        if w.window >= 0:
+            # o and lse from the window forward; the token bitmap is built once
+            bits = (fa.window_bitmap(w.global_tokens, w.T, q.device) if w.global_tokens
+                    else None)
+            rc = lib.fa_fwd_window(*(args[:-1] + (w.window, None if bits is None
+                                                  else bits.data_ptr(), sp)))
+        else:
+            rc = lib.fa_fwd(*args)
         if rc:
             raise RuntimeError(fa.status_str(rc))
         do = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)[0].cuda()
@@ -124,12 +132,22 @@ def main():
         ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
         bargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.H_kv,
-                 w.T, w.D, int(causal), w.scale, dcode, a.head_split, ws.data_ptr(), nbytes, sp)
+                 w.T, w.D, int(causal), w.scale, dcode)
+        tail = (a.head_split, ws.data_ptr(), nbytes, sp)
+        if w.window >= 0:
+            wargs = bargs + (w.window, None if bits is None else bits.data_ptr()) + tail
 
-        def step():
-            rc = lib.fa_bwd(*bargs)
-            if rc:
-                raise RuntimeError(fa.status_str(rc))
+            def step():
+                rc = lib.fa_bwd_window(*wargs)
+                if rc:
+                    raise RuntimeError(fa.status_str(rc))
+        else:
+            bargs = bargs + tail
+
+            def step():
+                rc = lib.fa_bwd(*bargs)
+                if rc:
+                    raise RuntimeError(fa.status_str(rc))
     elif w.window >= 0:
         if a.nsplit > 1:
             raise SystemExit("--nsplit does not apply to window workloads")
@@ -207,7 +225,7 @@ def main():
             "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
                        f"{str(a.nsplit > 1).lower()}>" if w.dtype in _ELEM else
                        f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
-    if w.window >= 0:
+    if w.window >= 0 and a.which == "fwd":
         roof["kernel"] = (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
                           f"false, true> (window)")
         roof["traffic"] = None
@@ -229,7 +247,11 @@ def main():
         do64 = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)[1]
         reps, t0 = 0, time.perf_counter()
         while True:
-            ref = orc.attention_bwd(x.q64, x.k64, x.v64, do64, causal, w.scale)
+            if w.window >= 0:
+                ref = orc.attention_bwd_masked(x.q64, x.k64, x.v64, do64, causal, w.scale,
+                                               w.window, w.global_tokens)
+            else:
+                ref = orc.attention_bwd(x.q64, x.k64, x.v64, do64, causal, w.scale)
             reps += 1
             el = time.perf_counter() - t0
             if el >= a.cpu_seconds:

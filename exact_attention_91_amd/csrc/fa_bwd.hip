@@ -59,6 +59,12 @@ struct BwdParams {
     // dkpart/dvpart [s][b][t][g][d], added in part order by the reduce kernel.
     int hsplit;
     float *dkpart, *dvpart;
+    // Window mode (as the window forward): key j visible to query i iff
+    // |i - j| <= window (clamped to T) or bit j%64 of gbits[j/64] is set
+    // (gbits NULL: no global tokens); causal still applies.
+    int window;
+    const unsigned long long *gbits;
+    int nwords;             // 64-bit words of gbits: ceil(T / 64)
 };
 
 // ---------------------------------------------------------------------------
@@ -72,7 +78,7 @@ struct BwdParams {
 // registers 8 s2 .. 8 s2 + 7, whose queries 16 s2 + 8(e/4) + 4half + e%4 are
 // exactly the rows the transposing reads of dO^T / Q^T hand lane (d, half).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
@@ -168,7 +174,26 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     // tile (causal: rows >= k0).
     const int nqt_all = (T + BQ - 1) / BQ;
     const int i_beg = CAUSAL ? k0 / BQ : 0;
-    const int nqt = nqt_all - i_beg;
+    // Window mode: the global bits of this work-group's 128 keys (two words)
+    // and of this lane's key; a key tile holding no global token sees only the
+    // query tiles meeting its band [k0 - window, k0 + 127 + window].
+    unsigned long long gw0 = 0ull, gw1 = 0ull;
+    if (WINDOW && p.gbits) {
+        gw0 = p.gbits[k0 / 64];
+        if (k0 / 64 + 1 < p.nwords) gw1 = p.gbits[k0 / 64 + 1];
+    }
+    const bool kglob = WINDOW && key < T &&
+                       (((key - k0 < 64 ? gw0 : gw1) >> ((key - k0) & 63)) & 1ull);
+    const bool wave_glob = WINDOW && (((wave < 2 ? gw0 : gw1) >> (32 * (wave & 1))) &
+                                      0xffffffffull) != 0ull;
+    int qlo = i_beg, qhi = nqt_all - 1;
+    if (WINDOW && (gw0 | gw1) == 0ull) {
+        const long long lo = max(0LL, (long long)k0 - p.window) / BQ;
+        const long long hi = ((long long)k0 + kBlk - 1 + p.window) / BQ;
+        qlo = max(qlo, (int)lo);
+        qhi = (int)min((long long)qhi, hi);
+    }
+    const int nqt = qhi - qlo + 1;
     const int h0 = g * p.group + hs * p.group / p.hsplit;      // this part's query heads
     const int nh = g * p.group + (hs + 1) * p.group / p.hsplit - h0;
     const int nit = nh * nqt;
@@ -176,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     auto stage = [&](int it, unsigned char *qd, unsigned char *od, float *sd)
         __attribute__((always_inline)) {
         const int h = h0 + it / nqt;
-        const int q0 = (i_beg + it % nqt) * BQ;
+        const int q0 = (qlo + it % nqt) * BQ;
         const long long hoff = (long long)b * T * qrs + (long long)h * D;
         stage_tile<D>((const unsigned short *)p.q + hoff, (const unsigned short *)p.dout + hoff,
                       qrs, qrs, T, q0, wave, qoff, qoff, qd, od);
@@ -192,12 +217,19 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
 
     auto compute = [&](int it, const unsigned char *qt, const unsigned char *ot, const float *st)
         __attribute__((always_inline)) {
-        const int q0 = (i_beg + it % nqt) * BQ;
+        const int q0 = (qlo + it % nqt) * BQ;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int n0 = q0 + 32 * sub;
             if (n0 >= T || (CAUSAL && n0 + 31 < wk0)) continue;   // wave-uniform
-            const bool need_mask = (CAUSAL && n0 < wk0 + 31) || (wk0 + 31 >= T);
+            bool need_mask = (CAUSAL && n0 < wk0 + 31) || (wk0 + 31 >= T);
+            if (WINDOW) {
+                // rows n0..n0+31 against this wave's keys wk0..wk0+31
+                const bool meets = n0 + 31 >= wk0 - p.window && n0 <= wk0 + 31 + p.window;
+                if (!meets && !wave_glob) continue;
+                const bool inside = n0 + 31 - wk0 <= p.window && wk0 + 31 - n0 <= p.window;
+                need_mask = need_mask || !inside;
+            }
             f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -225,7 +257,9 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int qn = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const bool ok = key < T && (!CAUSAL || key <= qn);
+                    bool ok = key < T && (!CAUSAL || key <= qn);
+                    if (WINDOW)
+                        ok = ok && ((qn - key <= p.window && key - qn <= p.window) || kglob);
                     s[r] = ok ? s[r] : 0.f;
                     dp[r] = ok ? dp[r] : 0.f;
                 }
@@ -328,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
 // L2 and Delta are per-lane scalars; register r of block kb is key
 // key0 + 32 kb + 8(r/4) + 4half + r%4.
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
@@ -408,6 +442,32 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
 
     const int kend = CAUSAL ? min(T, q0 + kBlk) : T;
     const int nkt = (kend + BK - 1) / BK;
+    // Window mode: key tiles meeting the band of this query tile (blo..bhi)
+    // or holding a global token; the others are never loaded.
+    int blo = 0, bhi = nkt - 1;
+    if (WINDOW) {
+        const long long q1 = min(q0 + kBlk, T) - 1;
+        blo = (int)(max(0LL, (long long)q0 - p.window) / BK);
+        bhi = (int)(min((long long)kend - 1, q1 + p.window) / BK);
+    }
+    auto next_tile = [&](int j) __attribute__((always_inline)) -> int {
+        int t = j + 1;
+        if (!WINDOW) return t;
+        const unsigned long long *gbits = p.gbits;
+        if (t < blo) {
+            if (!gbits) return blo;
+            while (t < blo && gbits[t] == 0ull) ++t;
+            return t;
+        }
+        if (t <= bhi) return t;
+        if (gbits)
+            while (t < nkt && gbits[t] == 0ull) ++t;
+        return min(t, nkt);
+    };
+    // read between steps, never after a step's prefetch is issued
+    auto tile_bits = [&](int t) __attribute__((always_inline)) -> unsigned long long {
+        return (WINDOW && p.gbits && t < nkt) ? p.gbits[t] : 0ull;
+    };
 
     int koff[NI], voff[NI];
 #pragma unroll
@@ -443,8 +503,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
     float c;
     asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
 
-    auto tile = [&](bool need_mask, int j, const unsigned char *kt, const unsigned char *vt)
-        __attribute__((always_inline)) {
+    auto tile = [&](bool need_mask, int j, const unsigned char *kt, const unsigned char *vt,
+                    unsigned long long gb) __attribute__((always_inline)) {
         const int key0 = j * BK;
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{}, d0 = f32x16_t{}, d1 = f32x16_t{};
 #pragma unroll
@@ -470,11 +530,27 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
         }
         if (need_mask) {
             const int lim = (CAUSAL ? min(qrow, T - 1) : T - 1) - key0 - 4 * half;
+            if (WINDOW) {
+                // in the band: lo <= off <= hi; global: bit (off + 4half) of gb
+                const int lo = qrow - p.window - key0 - 4 * half;
+                const int hi = qrow + p.window - key0 - 4 * half;
+                const unsigned long long gl = gb >> (4 * half);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int off = 8 * (r >> 2) + (r & 3);
-                s0[r] = off <= lim ? s0[r] : 0.f;
-                s1[r] = off + 32 <= lim ? s1[r] : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    const bool v0 = off <= lim && ((off >= lo && off <= hi) || ((gl >> off) & 1ull));
+                    const bool v1 = off + 32 <= lim &&
+                                    ((off + 32 >= lo && off + 32 <= hi) || ((gl >> (off + 32)) & 1ull));
+                    s0[r] = v0 ? s0[r] : 0.f;
+                    s1[r] = v1 ? s1[r] : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    s0[r] = off <= lim ? s0[r] : 0.f;
+                    s1[r] = off + 32 <= lim ? s1[r] : 0.f;
+                }
             }
         }
         // dS^T as the B operand: k-step s4 covers keys 16 s4 + 8(e/4) + 4half + e%4.
@@ -501,21 +577,42 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
         }
     };
 
-    auto step = [&](int j, const unsigned char *kt, const unsigned char *vt, unsigned char *kn,
-                    unsigned char *vn) __attribute__((always_inline)) {
+    auto step = [&](int j, unsigned long long gb, int jn, const unsigned char *kt,
+                    const unsigned char *vt, unsigned char *kn, unsigned char *vn)
+        __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (j + 1 < nkt)
-            stage_tile<D>(kbase, vbase, krs, krs, T, (j + 1) * BK, wave, koff, voff, kn, vn);
+        if (jn < nkt)
+            stage_tile<D>(kbase, vbase, krs, krs, T, jn * BK, wave, koff, voff, kn, vn);
         const int key0 = j * BK;
-        const bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
-        const bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
-        if (active) tile(need_mask, j, kt, vt);
+        bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
+        if (WINDOW) {
+            const long long wlo = (long long)wq0 - p.window, whi = (long long)wq0 + 31 + p.window;
+            const bool meets = key0 + BK - 1 >= wlo && key0 <= whi;
+            const bool inside = key0 >= (long long)wq0 + 31 - p.window &&
+                                key0 + BK - 1 <= (long long)wq0 + p.window;
+            active = active && (meets || gb != 0ull);
+            need_mask = need_mask || !inside;
+        }
+        if (active) tile(need_mask, j, kt, vt, gb);
     };
-    stage_tile<D>(kbase, vbase, krs, krs, T, 0, wave, koff, voff, k_lds0, v_lds0);
-    for (int j = 0; j < nkt; j += 2) {
-        step(j, k_lds0, v_lds0, k_lds1, v_lds1);
-        if (j + 1 < nkt) step(j + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+    {
+        int j = next_tile(-1);
+        unsigned long long gj = tile_bits(j);
+        if (j < nkt)
+            stage_tile<D>(kbase, vbase, krs, krs, T, j * BK, wave, koff, voff, k_lds0, v_lds0);
+        while (j < nkt) {
+            const int jn = next_tile(j);
+            const unsigned long long gn = tile_bits(jn);
+            step(j, gj, jn, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (jn >= nkt) break;
+            const int jnn = next_tile(jn);
+            const unsigned long long gnn = tile_bits(jnn);
+            step(jn, gn, jnn, k_lds1, v_lds1, k_lds0, v_lds0);
+            j = jnn;
+            gj = gnn;
+        }
     }
 
     if (!wave_live || qrow >= T) return;
@@ -600,11 +697,11 @@ long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, long long *
 }
 
 // dQ first: it also writes Delta and L2, which the dK/dV kernel reads.
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool WINDOW>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL>),
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
                        dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL>),
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW>),
                        dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit)),
                        dim3(kThreads), 0, s, p);
     if (p.hsplit > 1) {
@@ -614,14 +711,20 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
     }
 }
 
-template <typename E, bool CAUSAL>
+template <typename E, bool CAUSAL, bool WINDOW>
 void launch_bwd_d(const BwdParams &p, int D, hipStream_t s) {
     switch (D) {
-        case 16: launch_bwd<E, 16, CAUSAL>(p, s); break;
-        case 32: launch_bwd<E, 32, CAUSAL>(p, s); break;
-        case 64: launch_bwd<E, 64, CAUSAL>(p, s); break;
-        default: launch_bwd<E, 128, CAUSAL>(p, s); break;
+        case 16: launch_bwd<E, 16, CAUSAL, WINDOW>(p, s); break;
+        case 32: launch_bwd<E, 32, CAUSAL, WINDOW>(p, s); break;
+        case 64: launch_bwd<E, 64, CAUSAL, WINDOW>(p, s); break;
+        default: launch_bwd<E, 128, CAUSAL, WINDOW>(p, s); break;
     }
+}
+
+template <typename E, bool WINDOW>
+void launch_bwd_c(const BwdParams &p, int D, int causal, hipStream_t s) {
+    if (causal) launch_bwd_d<E, true, WINDOW>(p, D, s);
+    else launch_bwd_d<E, false, WINDOW>(p, D, s);
 }
 
 }  // namespace
@@ -634,10 +737,13 @@ extern "C" long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D
     return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split), nullptr);
 }
 
-extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
-                      const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
-                      int H, int H_kv, int T, int D, int causal, float scale, int dtype,
-                      int head_split, void *workspace, long long workspace_bytes, void *stream) {
+namespace {
+
+// Validation and launch shared by fa_bwd (window < 0) and fa_bwd_window.
+int bwd_impl(const void *q, const void *k, const void *v, const void *o, const float *lse,
+             const void *dout, void *dq, void *dk, void *dv, int B, int H, int H_kv, int T,
+             int D, int causal, float scale, int dtype, int window, const void *global_bits,
+             int head_split, void *workspace, long long workspace_bytes, void *stream) {
     if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16)
         return FA_ERR_DTYPE;
     if (dtype == FA_DTYPE_F32) return FA_ERR_DTYPE;   // 16-bit MFMA kernels only
@@ -651,7 +757,7 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
     const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
     for (const void *ptr : ptrs)
         if (!aligned16(ptr)) return FA_ERR_ALIGN;
-    if (((uintptr_t)lse % 4) != 0) return FA_ERR_ALIGN;
+    if (((uintptr_t)lse % 4) != 0 || ((uintptr_t)global_bits % 8) != 0) return FA_ERR_ALIGN;
     const int hs = head_parts(B, H, H_kv, T, head_split);
     long long stat_bytes = 0;
     const long long need = bwd_ws_bytes(B, H, H_kv, T, D, hs, &stat_bytes);
@@ -684,13 +790,37 @@ extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o
         p.dkpart = (float *)((char *)workspace + stat_bytes);
         p.dvpart = p.dkpart + (long long)hs * B * T * H_kv * D;
     }
+    p.window = window < 0 ? -1 : (window < T ? window : T);
+    p.gbits = window < 0 ? nullptr : (const unsigned long long *)global_bits;
+    p.nwords = (int)(((long long)T + 63) / 64);
     hipStream_t s = (hipStream_t)stream;
+    const bool win = window >= 0;
     if (dtype == FA_DTYPE_BF16) {
-        if (causal) launch_bwd_d<__bf16, true>(p, D, s);
-        else launch_bwd_d<__bf16, false>(p, D, s);
+        if (win) launch_bwd_c<__bf16, true>(p, D, causal, s);
+        else launch_bwd_c<__bf16, false>(p, D, causal, s);
     } else {
-        if (causal) launch_bwd_d<_Float16, true>(p, D, s);
-        else launch_bwd_d<_Float16, false>(p, D, s);
+        if (win) launch_bwd_c<_Float16, true>(p, D, causal, s);
+        else launch_bwd_c<_Float16, false>(p, D, causal, s);
     }
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                      int H, int H_kv, int T, int D, int causal, float scale, int dtype,
+                      int head_split, void *workspace, long long workspace_bytes, void *stream) {
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, T, D, causal, scale, dtype,
+                    -1, nullptr, head_split, workspace, workspace_bytes, stream);
+}
+
+extern "C" int fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
+                             const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                             int B, int H, int H_kv, int T, int D, int causal, float scale,
+                             int dtype, int window, const void *global_bits, int head_split,
+                             void *workspace, long long workspace_bytes, void *stream) {
+    if (window < 0) return FA_ERR_BAD_SHAPE;
+    return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, T, D, causal, scale, dtype,
+                    window, global_bits, head_split, workspace, workspace_bytes, stream);
 }

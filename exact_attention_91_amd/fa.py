@@ -59,6 +59,9 @@ def _lib():
         lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP,
                                                         ctypes.c_longlong, _VP]
         lib.fa_bwd.restype = _I
+        lib.fa_bwd_window.argtypes = ([_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _I,
+                                                              _VP, ctypes.c_longlong, _VP])
+        lib.fa_bwd_window.restype = _I
         lib.fa_bwd_workspace_bytes.argtypes = [_I] * 6
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_status_str.argtypes = [_I]
@@ -284,19 +287,10 @@ def bwd_workspace_bytes(B: int, H: int, H_kv: int, T: int, D: int, head_split: i
     return int(_lib().fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split))
 
 
-def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None,
-        head_split: int = 0):
-    """Attention backward on contiguous BNHD tensors (bfloat16 or float16).
-
-    q, o, dout: [B, T, H, D]; k, v: [B, T, H_kv, D]; lse: float32 [B, H, T]
-    -- o and lse as returned by fwd for the same q, k, v, causal, scale.
-    Returns (dq, dk, dv) shaped like q, k, v. `workspace` (optional): a
-    device tensor of at least bwd_workspace_bytes(B, H, H_kv, T, D, head_split)
-    bytes; allocated here when None. head_split: parts the query heads of a
-    kv head are split into for the dK/dV kernel (0: the library's choice)."""
+def _bwd_args(q, k, v, o, lse, dout, scale, head_split, workspace):
     _check(q, k, v)
     if q.dtype not in (torch.bfloat16, torch.float16):
-        raise TypeError(f"bwd takes bfloat16 or float16 inputs, got {q.dtype}")
+        raise TypeError(f"the backward takes bfloat16 or float16 inputs, got {q.dtype}")
     B, T, H, D = q.shape
     for name, t, shape, dt in (("o", o, q.shape, q.dtype), ("dout", dout, q.shape, q.dtype),
                                ("lse", lse, (B, H, T), torch.float32)):
@@ -307,21 +301,53 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None,
                              f"{t.dtype} {tuple(t.shape)}")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout)):
         if not t.is_contiguous():
-            raise ValueError(f"bwd needs contiguous tensors ({name} is not)")
+            raise ValueError(f"the backward needs contiguous tensors ({name} is not)")
     H_kv = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = bwd_workspace_bytes(B, H, H_kv, T, D, head_split)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ptrs = [t.data_ptr() for t in (q, k, v, o, lse, dout) + grads]
+    return (ptrs, (B, H, H_kv, T, D), float(scale), workspace, grads)
+
+
+def bwd_window(q, k, v, o, lse, dout, window: int, global_tokens=None, causal: bool = False,
+               scale=None, global_bits=None, workspace=None, head_split: int = 0):
+    """Backward of fwd_window (same window, global tokens, causal, scale; o and
+    lse from fwd_window). Returns (dq, dk, dv)."""
+    ptrs, dims, scale, workspace, grads = _bwd_args(q, k, v, o, lse, dout, scale, head_split,
+                                                    workspace)
+    if global_tokens is not None and global_bits is not None:
+        raise ValueError("give global_tokens or global_bits, not both")
+    if global_tokens is not None:
+        global_bits = window_bitmap(global_tokens, dims[3], q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = _lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H,
-                       H_kv, T, D, int(bool(causal)), float(scale), _dtype_code(q),
-                       int(head_split), workspace.data_ptr(),
-                       workspace.numel() * workspace.element_size(), stream)
+    rc = _lib().fa_bwd_window(*ptrs, *dims, int(bool(causal)), scale, _dtype_code(q),
+                              int(window),
+                              None if global_bits is None else global_bits.data_ptr(),
+                              int(head_split), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), stream)
+    _raise(rc, "fa_bwd_window")
+    return grads
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale=None, workspace=None,
+        head_split: int = 0):
+    """Attention backward on contiguous BNHD tensors (bfloat16 or float16).
+
+    q, o, dout: [B, T, H, D]; k, v: [B, T, H_kv, D]; lse: float32 [B, H, T]
+    -- o and lse as returned by fwd for the same q, k, v, causal, scale.
+    Returns (dq, dk, dv) shaped like q, k, v. `workspace` (optional): a
+    device tensor of at least bwd_workspace_bytes(B, H, H_kv, T, D, head_split)
+    bytes; allocated here when None. head_split: parts the query heads of a
+    kv head are split into for the dK/dV kernel (0: the library's choice)."""
+    ptrs, dims, scale, workspace, grads = _bwd_args(q, k, v, o, lse, dout, scale, head_split,
+                                                    workspace)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib().fa_bwd(*ptrs, *dims, int(bool(causal)), scale, _dtype_code(q), int(head_split),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       stream)
     _raise(rc, "fa_bwd")
-    return dq, dk, dv
+    return grads

@@ -230,6 +230,22 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
            int D, int causal, float scale, int dtype, int head_split, void *workspace,
            long long workspace_bytes, void *stream);
 
+/*
+ * Backward of fa_fwd_window: the gradients above with P restricted to the
+ * sliding-window / local-global visible set (|i - j| <= window or j global,
+ * and j <= i when causal). o and lse must come from fa_fwd_window with the
+ * same window, global_bits, causal and scale. Key tiles that no query sees
+ * (outside every band and holding no global token) are skipped on both
+ * sides. window >= 0 (FA_ERR_BAD_SHAPE otherwise); global_bits as in
+ * fa_fwd_window (NULL = none); everything else as fa_bwd, with the same
+ * workspace size.
+ */
+int fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
+                  const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
+                  int H, int H_kv, int T, int D, int causal, float scale, int dtype, int window,
+                  const void *global_bits, int head_split, void *workspace,
+                  long long workspace_bytes, void *stream);
+
 /* Workspace bytes fa_bwd needs for these sizes and head_split (0 = the
  * library's choice, as in fa_bwd): 8 * B * H * T rounded up to 16, plus
  * 8 * parts * B * T * H_kv * D when the group's heads are split into parts > 1;

@@ -38,7 +38,7 @@ DT = _enum_values("fa_dtype_t")
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_fwd",
                                      "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
                                      "fa_fwd_strided", "fa_fwd_window", "fa_lse_combine",
                                      "fa_status_str", "fa_version", "fa_window_bitmap",
@@ -352,3 +352,24 @@ def test_window_empty_call_is_a_noop(lib):
 def test_window_bitmap_rejects(lib, args, code):
     _host_only()
     assert lib.fa_window_bitmap(*args, None) == ST[code]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), "FA_ERR_BAD_SHAPE"),
+    (dict(bits=P + 4), "FA_ERR_ALIGN"),
+    (dict(dtype=DT["FA_DTYPE_F32"]), "FA_ERR_DTYPE"),
+    (dict(dq=None), "FA_ERR_NULL_PTR"),
+    (dict(ws_bytes=10), "FA_ERR_WORKSPACE"),
+    (dict(B=0), "FA_OK"),
+])
+def test_bwd_window_rejects(lib, kw, code):
+    _host_only()
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=2, H=4, H_kv=2, T=100,
+             D=64, causal=1, scale=0.125, dtype=DT["FA_DTYPE_BF16"], window=8, bits=P, hsplit=1,
+             ws=P, ws_bytes=1 << 40)
+    a.update(kw)
+    rc = lib.fa_bwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                           a["dv"], a["B"], a["H"], a["H_kv"], a["T"], a["D"], a["causal"],
+                           a["scale"], a["dtype"], a["window"], a["bits"], a["hsplit"], a["ws"],
+                           a["ws_bytes"], None)
+    assert rc == ST[code]

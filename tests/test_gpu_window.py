@@ -151,3 +151,91 @@ def test_window_prebuilt_bitmap_reused():
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
         check(x, "bf16", causal, 0.125, 33, glob, o1.double().cpu().numpy(),
               l1.double().cpu().numpy(), f"prebuilt causal={causal}")
+
+
+# ---------------------------------------------------------------- backward
+
+BWD_RTOL = {"bf16": 2e-2, "f16": 3e-3}   # as the plain backward (tests/test_gpu_bwd.py)
+
+
+def run_bwd_window(x, do, causal, scale, window, glob, head_split=0):
+    from exact_attention_91_amd import fa
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    bits = fa.window_bitmap(glob, q.shape[1], q.device)
+    o, lse = fa.fwd_window(q, k, v, window, causal=causal, scale=scale, global_bits=bits)
+    g = fa.bwd_window(q, k, v, o, lse, do.cuda(), window, causal=causal, scale=scale,
+                      global_bits=bits, head_split=head_split)
+    torch.cuda.synchronize()
+    return tuple(t.double().cpu().numpy() for t in g)
+
+
+def check_bwd(x, do64, dtype, causal, scale, window, glob, got, label=""):
+    from oracle import oracle as orc
+    valid = [int(g) for g in glob if 0 <= int(g) < x.q64.shape[1]]
+    ref = orc.attention_bwd_masked(x.q64, x.k64, x.v64, do64, causal, scale, window, valid)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(g)), name
+        err = float(np.max(np.abs(g - r)))
+        tol = BWD_RTOL[dtype] * max(1.0, float(np.max(np.abs(r))))
+        say(f"  {label} {name}: max|err|={err:.3e} (tol {tol:.3e})")
+        assert err <= tol, (name, err, tol)
+
+
+BWD_CASES = [(65, 0, ()), (300, 63, (0, 64, 299)), (300, 1, ()), (1000, 100, (0, 1, 2, 3)),
+             (777, 31, tuple(range(0, 777, 97))), (1000, 2000, ())]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T,window,glob", BWD_CASES)
+def test_bwd_window_small(dtype, D, causal, T, window, glob):
+    from exact_attention_91_amd.inputs import generate_dout
+    B, H, H_kv = (2, 3, 1) if T < 500 else (1, 2, 2)
+    seed = 9950 + T + window + D
+    say(f"case bwd window dtype={dtype} D={D} causal={causal} T={T} window={window} "
+        f"globals={len(glob)} seed={seed}")
+    x = generate(B, H, H_kv, T, D, dtype, seed)
+    do, do64 = generate_dout(B, H, T, D, dtype, seed)
+    scale = default_scale(D)
+    got = run_bwd_window(x, do, causal, scale, window, glob)
+    check_bwd(x, do64, dtype, causal, scale, window, glob, got, "small")
+
+
+@pytest.mark.parametrize("head_split", [1, 4, 0])
+def test_bwd_window_head_split(head_split):
+    from exact_attention_91_amd.inputs import generate_dout
+    x = generate(2, 8, 1, 500, 64, "bf16", 9990)
+    do, do64 = generate_dout(2, 8, 500, 64, "bf16", 9990)
+    for causal in (False, True):
+        got = run_bwd_window(x, do, causal, 0.125, 70, (3, 250), head_split=head_split)
+        check_bwd(x, do64, "bf16", causal, 0.125, 70, (3, 250), got, f"split={head_split}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_window_covering_everything_is_bwd_bitwise(causal):
+    """A window covering every key without global tokens: the same tiles and
+    arithmetic as fa_bwd, bitwise the same gradients."""
+    from exact_attention_91_amd import fa
+    from exact_attention_91_amd.inputs import generate_dout
+    x = generate(2, 4, 2, 300, 64, "bf16", 9991)
+    do = generate_dout(2, 4, 300, 64, "bf16", 9991)[0].cuda()
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=0.125)
+    a = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=0.125, head_split=1)
+    b = fa.bwd_window(q, k, v, o, lse, do, 299, causal=causal, scale=0.125, head_split=1)
+    torch.cuda.synchronize()
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)
+
+
+def test_bwd_workload_window():
+    """The window workload's backward (B=2 H=12 T=8192 D=64, window 256, tokens
+    0..15 global, causal), compared in full."""
+    from exact_attention_91_amd.inputs import generate_dout
+    w = WORKLOADS["window"]
+    say(f"workload bwd {w.name}")
+    x = generate_workload(w)
+    do, do64 = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)
+    got = run_bwd_window(x, do, True, w.scale, w.window, w.global_tokens)
+    check_bwd(x, do64, w.dtype, True, w.scale, w.window, w.global_tokens, got, w.name)
