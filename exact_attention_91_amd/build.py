@@ -23,11 +23,25 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    cmd = [HIPCC, *FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
-           "-o", LIB + ".tmp", *SRCS]
+    """Compile each source to an object in parallel, then link the library."""
+    objs = [os.path.join(HERE, "csrc", os.path.basename(src) + ".o") for src in SRCS]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs = []
+    for src, obj in zip(SRCS, objs):
+        cmd = [HIPCC, *compile_flags, *extra, "-I", os.path.join(ROOT, "include"), "-c",
+               "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+    failed = [p.args for p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    cmd = [HIPCC, *FLAGS, *extra, "-o", LIB + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    for obj in objs:
+        os.remove(obj)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 
