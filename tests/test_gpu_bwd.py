@@ -207,3 +207,25 @@ def test_bwd_head_split(H, H_kv, head_split):
             assert torch.equal(a, b)
         got = tuple(t.double().cpu().numpy() for t in g1)
         check_grads(x, do64, "bf16", causal, 0.125, got, f"split={head_split}")
+
+
+def test_bwd_workload_long_full():
+    """The long workload (B=8 H=1 T=8192 D=128, causal) backward, compared in
+    full (the oracle takes about a minute on the host)."""
+    w = WORKLOADS["long"]
+    say(f"workload bwd {w.name}")
+    x = generate_workload(w)
+    do, do64 = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)
+    got = run_bwd(x, do, True, w.scale)
+    check_grads(x, do64, w.dtype, True, w.scale, got, w.name)
+
+
+def test_bwd_workload_mqa_full():
+    """The MQA workload (q [8,12,4096,64], one kv head, q,k ~ N(0,4^2), causal)
+    backward with the library's head split, compared in full."""
+    w = WORKLOADS["mqa"]
+    say(f"workload bwd {w.name}")
+    x = generate_workload(w)
+    do, do64 = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)
+    got = run_bwd(x, do, True, w.scale)
+    check_grads(x, do64, w.dtype, True, w.scale, got, w.name)
