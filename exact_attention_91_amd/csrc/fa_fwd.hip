@@ -76,6 +76,11 @@ struct FwdParams {
     // set (gbits NULL: no global tokens); causal still applies.
     int window;
     const unsigned long long *gbits;
+    // Paired causal mode: work-group t runs query tiles nq-1-t, then t, so every
+    // work-group has the same number of key tiles (used when all work-groups
+    // are resident at once and rows are long, where the heaviest tile would
+    // otherwise set the launch's length).
+    int pair;
 };
 
 template <bool B>
@@ -111,7 +116,7 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 // layout of fa_device.h: K is read as rows (kswz), V transposed for the V^T
 // operand of P.V (vswz).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW>
+template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW, bool PAIR>
 __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
@@ -136,7 +141,26 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
-    const Unit u = unit_of(p);
+    constexpr bool paired = PAIR && CAUSAL && !SPLIT && !WINDOW;
+    for (int pass = 0; pass < (paired ? 2 : 1); ++pass) {
+    Unit u;
+    if (paired) {
+        const int id = blockIdx.x;
+        const int t = id / p.nbh;
+        const int bh = id - t * p.nbh;
+        u.b = bh / p.H;
+        u.h = bh - u.b * p.H;
+        u.g = u.h / p.group;
+        u.s = 0;
+        const int qt = pass == 0 ? p.nq - 1 - t : t;
+        if (pass == 1 && qt == p.nq - 1 - t) break;   // odd count: the middle tile is done
+        u.q0 = qt * kBQ;
+        // every wave starts each pass together (before the second pass this is
+        // also what keeps its first tile's staging off buffers still being read)
+        __syncthreads();
+    } else {
+        u = unit_of(p);
+    }
     const int wq0 = u.q0 + wave * 32;       // first query row of this wave
     const int qrow = wq0 + col;             // this lane's query row
 
@@ -389,9 +413,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
         }
     }
 
-    if (!wave_live) return;
+    if (!wave_live) continue;
     const float lt = half_swap_sum(lsum);
-    if (qrow >= T) return;
+    if (qrow >= T) continue;
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
     const float lse_row = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     if (SPLIT) {
@@ -411,7 +435,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
                 }
             }
         if (half == 0) p.lpart[row] = lse_row;
-        return;
+        continue;
     }
     unsigned short *orow = (unsigned short *)p.o + u.b * p.os[0] + (long long)qrow * p.os[1] +
                            u.h * p.os[2];
@@ -429,6 +453,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
             }
         }
     if (half == 0) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
+    }   // pass
 }
 // ---------------------------------------------------------------------------
 // fp32 kernel: fp32 operands on fp32 MFMA (32x32x2), 32-key tiles. Weights stay
@@ -693,6 +718,7 @@ __global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int
 // Host side: validation (no HIP calls), dispatch, launch.
 // ---------------------------------------------------------------------------
 constexpr long long kMaxOffset = 1LL << 62;
+constexpr long long kNumCU = 256;   // MI355X compute units
 constexpr long long kMaxGrid = (1LL << 24) - 1;
 
 // Largest element offset + 1 of a [B, T, heads, D] view; -1 on overflow.
@@ -710,11 +736,18 @@ bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 template <int D, bool CAUSAL, bool SPLIT, bool WINDOW>
 void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
-    if (dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW>), grid,
+    constexpr bool CAN_PAIR = CAUSAL && !SPLIT && !WINDOW;
+    if (CAN_PAIR && p.pair && dtype == FA_DTYPE_BF16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_PAIR>), grid,
+                           dim3(kThreads), 0, stream, p);
+    else if (CAN_PAIR && p.pair && dtype == FA_DTYPE_F16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_PAIR>), grid,
+                           dim3(kThreads), 0, stream, p);
+    else if (dtype == FA_DTYPE_BF16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>), grid,
                            dim3(kThreads), 0, stream, p);
     else if (dtype == FA_DTYPE_F16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW>), grid,
+        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>), grid,
                            dim3(kThreads), 0, stream, p);
     else if (!SPLIT && !WINDOW)
         hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
@@ -796,6 +829,7 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
     p.opart = p.lpart = nullptr;
     p.window = 0;
     p.gbits = nullptr;
+    p.pair = 0;
     return FA_OK;
 }
 
@@ -860,7 +894,14 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     const int st = prepare(q, k, v, o, lse, B, H, H_kv, T, D, scale, dtype, q_strides, k_strides,
                            v_strides, o_strides, &p, &empty);
     if (st != FA_OK || empty) return st;
-    const dim3 grid((unsigned)((long long)p.nbh * p.nq));
+    // Pair causal query tiles when rows are long and every work-group is
+    // resident at once (work-group slots: 256 CUs x 4, or x 2 at D = 128 by
+    // registers), so the heaviest tile would set the launch's length.
+    const long long units = (long long)p.nbh * p.nq;
+    const long long slots = kNumCU * (D >= 128 ? 2 : 4);
+    if (causal && dtype != FA_DTYPE_F32 && T >= 4096 && units <= slots && 2 * units >= slots)
+        p.pair = 1;
+    const dim3 grid((unsigned)(p.pair ? (long long)p.nbh * ((p.nq + 1) / 2) : units));
     hipStream_t s = (hipStream_t)stream;
     if (causal)
         launch_d<true, false>(p, D, dtype, grid, s);

@@ -126,3 +126,15 @@ def test_workload_mqa_sampled_rows():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     # O is a convex combination of V rows
     assert np.max(np.abs(o)) <= np.max(np.abs(x.v64)) + TOL["bf16"][0]
+
+
+@pytest.mark.parametrize("B,T,D", [(5, 8000, 128), (4, 8192, 128), (16, 4200, 64)])
+def test_paired_query_tiles(B, T, D):
+    """Long causal rows with every work-group resident at once: the library
+    runs query tiles in heavy/light pairs (nq-1-t, then t). Odd tile counts
+    (T = 8000 and 4200) leave the middle tile unpaired. Compared in full."""
+    say(f"case paired B={B} T={T} D={D}")
+    x = generate(B, 1, 1, T, D, "bf16", 9700 + T + D)
+    scale = default_scale(D)
+    o, lse = run_gpu(x, True, scale)
+    check_full(x, "bf16", True, scale, o, lse, "paired")
