@@ -1,0 +1,86 @@
+"""The entry points under HIP graph capture: the library allocates nothing,
+sets no memory and never synchronises, so a captured call replays like the
+eager one. Each graph is replayed several times with the inputs rewritten
+eagerly between replays (and the program's own work and synchronisation in
+between); every replay must equal an eager call on the same inputs bitwise."""
+import pytest
+import torch
+
+from exact_attention_91_amd.inputs import generate, generate_dout
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _fresh(q, k, v, seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for t in (q, k, v):
+        t.copy_(torch.randn(t.shape, device="cuda", generator=g).to(t.dtype))
+
+
+def _capture(fn):
+    """Capture fn() on a side stream (warmed up first); return (graph, outputs)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()                     # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = fn()
+    torch.cuda.synchronize()
+    return graph, out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_graph_replays(causal):
+    from exact_attention_91_amd import fa
+    x = generate(2, 4, 2, 300, 64, "bf16", 12001)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    graph, (o, lse) = _capture(lambda: fa.fwd(q, k, v, causal=causal, scale=0.125))
+    for rep in range(4):
+        _fresh(q, k, v, 500 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eo, el = fa.fwd(q, k, v, causal=causal, scale=0.125)
+        torch.cuda.synchronize()
+        assert torch.equal(o, eo) and torch.equal(lse, el), f"replay {rep}"
+
+
+def test_bwd_and_splitk_and_window_graph_replays():
+    from exact_attention_91_amd import fa
+    B, H, H_kv, T, D = 1, 8, 2, 400, 64
+    x = generate(B, H, H_kv, T, D, "bf16", 12002)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    do = generate_dout(B, H, T, D, "bf16", 12002)[0].cuda()
+    bits = fa.window_bitmap((0, 7, 399), T, q.device)
+    ws_b = torch.empty((fa.bwd_workspace_bytes(B, H, H_kv, T, D, 0),), dtype=torch.uint8,
+                       device="cuda")
+    ws_s = torch.empty((fa.splitk_workspace_bytes(B, H, T, D, 3),), dtype=torch.uint8,
+                       device="cuda")
+
+    def step():
+        o, lse = fa.fwd(q, k, v, causal=True, scale=0.125)
+        g = fa.bwd(q, k, v, o, lse, do, causal=True, scale=0.125, workspace=ws_b)
+        os_, ls_ = fa.fwd_splitk(q, k, v, causal=True, scale=0.125, nsplit=3, workspace=ws_s)
+        ow, lw = fa.fwd_window(q, k, v, 33, causal=True, scale=0.125, global_bits=bits)
+        return (o, lse) + tuple(g) + (os_, ls_, ow, lw)
+
+    graph, outs = _capture(step)
+    for rep in range(3):
+        _fresh(q, k, v, 600 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = step()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a, b), f"replay {rep} output {i}"
