@@ -239,3 +239,17 @@ def test_bwd_workload_window():
     do, do64 = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)
     got = run_bwd_window(x, do, True, w.scale, w.window, w.global_tokens)
     check_bwd(x, do64, w.dtype, True, w.scale, w.window, w.global_tokens, got, w.name)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_window_scale_values(scale):
+    """Negative scale (q's sign flipped in registers) and zero scale (uniform
+    weights over each row's visible keys), forward and backward."""
+    from exact_attention_91_amd.inputs import generate_dout
+    x = generate(1, 4, 2, 300, 64, "bf16", 9995)
+    do, do64 = generate_dout(1, 4, 300, 64, "bf16", 9995)
+    for causal in (False, True):
+        o, lse = run_window(x, causal, scale, 20, (0, 150))
+        check(x, "bf16", causal, scale, 20, (0, 150), o, lse, f"scale={scale}")
+        got = run_bwd_window(x, do, causal, scale, 20, (0, 150))
+        check_bwd(x, do64, "bf16", causal, scale, 20, (0, 150), got, f"scale={scale}")
