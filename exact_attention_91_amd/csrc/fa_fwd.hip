@@ -1,5 +1,8 @@
-// fa_fwd.hip -- exact, IO-aware, tiled attention forward for MI355X (gfx950),
-// and the C ABI declared in include/fa.h.
+// fa_fwd.hip -- exact, IO-aware, tiled attention forward for MI355X (gfx950):
+// the plain forward (fa_fwd, fa_fwd_strided), its key-split form with the
+// logsumexp combine (fa_fwd_splitk, fa_lse_combine), the sliding-window /
+// local-global forward and its token bitmap (fa_fwd_window, fa_window_bitmap),
+// and their C ABI (include/fa.h).
 //
 // Method (pages by title and section):
 //  * "Flash Attention Memory Optimization Explained" (lzwjava.github.io),
@@ -41,7 +44,15 @@
 //  * Causal: key tiles past the query tile are never loaded; a wave skips the
 //    math of tiles wholly in its future; only tiles that touch the diagonal or
 //    the ragged end T are masked element-wise. Query tiles are issued
-//    heaviest-first.
+//    heaviest-first; for long rows with every work-group resident, heavy and
+//    light tiles are paired in one work-group (the PAIR instantiation).
+//  * Variants of the same 16-bit kernel (template flags): SPLIT runs a range
+//    of each query tile's key tiles and writes an fp32 partial result that
+//    fa_lse_combine_kernel merges by the logsumexps (the online-softmax update
+//    of "Softmax 的在線計算" applied across ranges); WINDOW visits only the key
+//    tiles that meet the query tile's band or hold a global token (the
+//    sparse-attention variants of the same article) and masks by band, token
+//    bitmap and causality.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
