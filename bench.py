@@ -223,11 +223,12 @@ def main():
     roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
             "frac": tflops / peak, "traffic": traffic_for(w.name),
             "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
-                       f"{str(a.nsplit > 1).lower()}>" if w.dtype in _ELEM else
+                       f"{str(a.nsplit > 1).lower()}, false, PAIR> (PAIR as the library picks)"
+                       if w.dtype in _ELEM else
                        f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
     if w.window >= 0 and a.which == "fwd":
         roof["kernel"] = (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
-                          f"false, true> (window)")
+                          f"false, true, false> (window)")
         roof["traffic"] = None
     if a.which == "bwd":
         roof["kernel"] = (f"fa_bwd_dq_kernel + fa_bwd_dkdv_kernel<{_ELEM[w.dtype]}, {w.D}, "
