@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--nsplit", type=int, default=1,
                     help="> 1: time fa_fwd_splitk (key split into this many parts "
                          "plus the logsumexp combine) instead of fa_fwd")
+    ap.add_argument("--no-global-split", action="store_true",
+                    help="window backward: workspace without room for the global keys' "
+                         "partial sums (each global key tile walks every query tile itself)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle until this much wall time has passed")
@@ -129,6 +132,10 @@ def main():
         do = generate_dout(w.B, w.H, w.T, w.D, w.dtype, w.seed)[0].cuda()
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         nbytes = fa.bwd_workspace_bytes(w.B, w.H, w.H_kv, w.T, w.D, a.head_split)
+        if w.window >= 0 and w.global_tokens and not a.no_global_split:
+            # room for the global keys' partial sums: their far queries are split
+            nbytes = fa.bwd_window_workspace_bytes(w.B, w.H, w.H_kv, w.T, w.D, w.window,
+                                                   len(set(w.global_tokens)), a.head_split)
         ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
         bargs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.H_kv,

@@ -7,4 +7,5 @@ the functions below are a thin ctypes binding that marshals torch device
 tensors into it.
 """
 from .fa import (fwd, fwd_strided, fwd_splitk, lse_combine, splitk_workspace_bytes,  # noqa: F401
-                 fwd_window, window_bitmap, bwd, bwd_window, bwd_workspace_bytes, version, status_str, lib_path)
+                 fwd_window, window_bitmap, bwd, bwd_window, bwd_workspace_bytes,
+                 bwd_window_workspace_bytes, version, status_str, lib_path)

@@ -65,7 +65,102 @@ struct BwdParams {
     int window;
     const unsigned long long *gbits;
     int nwords;             // 64-bit words of gbits: ceil(T / 64)
+    // Window split of the global key tiles (nslots > 0). A key tile holding
+    // a global token is seen by every query (causal: every later one), not
+    // only by its band. Its main work-group then walks the band alone, like
+    // every other tile, and the far query tiles (outside the band: there only
+    // the global keys are visible) go to nfar = B * H_kv * nchunk extra
+    // work-groups, chunk c taking run c of the (query head, far tile) list.
+    // For each global key, every part writes its fp32 sums (dK unscaled) to
+    // the key's slot, its rank among the global keys:
+    //   gpk / gpv [slot][part][b][g][D],  part = head part hs (band) or
+    //   hsplit + c (far chunk c),  nparts = hsplit + nchunk,
+    // gmeta[0] = number of slots in use, gmeta[4 + slot] = the slot's key;
+    // fa_bwd_gsum_kernel adds the parts in order. Only the first kMaxSplit
+    // global tiles whose keys all have slots (rank < nslots) are split; the
+    // others keep the full walk.
+    int nslots, nchunk, nparts, nfar;
+    int *gmeta;
+    float *gpk, *gpv;
 };
+
+constexpr int kMaxSplit = 64;   // global key tiles that can be split
+
+// Global key tiles in key order, from a scan of the bitmap (two words per
+// 128-key tile, bits at or past T ignored) by the whole work-group.
+struct SplitLds {
+    int tile[kMaxSplit];     // the r-th tile holding a global token
+    int before[kMaxSplit];   // global keys in the tiles before it
+    int end[kMaxSplit];      // ... and in it
+    int wsum[4][2];
+    int nelig;               // eligible tiles: a prefix of the list
+    int mine;                // rank of tile tk among the global tiles (-1: none)
+};
+
+__device__ __forceinline__ unsigned long long gword(const BwdParams &p, int w) {
+    if (w >= p.nwords) return 0ull;
+    unsigned long long x = p.gbits[w];
+    const int tail = p.T - 64 * w;
+    if (tail < 64) x &= (1ull << tail) - 1ull;
+    return x;
+}
+
+// Called by every thread of the work-group (it synchronises).
+__device__ void scan_global_tiles(const BwdParams &p, int tk, SplitLds &sl) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) sl.mine = -1;
+    int nt = 0, nk = 0;   // global tiles / keys before this chunk (uniform)
+    for (int c0 = 0; c0 < p.nblk && nt < kMaxSplit; c0 += kThreads) {
+        const int t = c0 + tid;
+        unsigned long long w0 = 0ull, w1 = 0ull;
+        if (t < p.nblk) {
+            w0 = gword(p, 2 * t);
+            w1 = gword(p, 2 * t + 1);
+        }
+        const int f = (w0 | w1) != 0ull;
+        const int kc = __popcll(w0) + __popcll(w1);
+        int sf = f, sk = kc;   // inclusive scans within the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int xf = __shfl_up(sf, o), xk = __shfl_up(sk, o);
+            if (lane >= o) {
+                sf += xf;
+                sk += xk;
+            }
+        }
+        if (lane == 63) {
+            sl.wsum[wave][0] = sf;
+            sl.wsum[wave][1] = sk;
+        }
+        __syncthreads();
+        int pf = nt, pk = nk;
+        for (int w = 0; w < 4; ++w) {
+            if (w < wave) {
+                pf += sl.wsum[w][0];
+                pk += sl.wsum[w][1];
+            }
+        }
+        for (int w = 0; w < 4; ++w) {
+            nt += sl.wsum[w][0];
+            nk += sl.wsum[w][1];
+        }
+        const int rank = pf + sf - f;
+        if (f && rank < kMaxSplit) {
+            sl.tile[rank] = t;
+            sl.before[rank] = pk + sk - kc;
+            sl.end[rank] = pk + sk;
+        }
+        if (f && t == tk) sl.mine = rank;
+        __syncthreads();   // wsum is rewritten by the next chunk
+    }
+    if (tid == 0) {
+        const int nl = min(nt, kMaxSplit);
+        int n = 0;
+        while (n < nl && sl.end[n] <= p.nslots) ++n;
+        sl.nelig = n;
+    }
+    __syncthreads();
+}
 
 // ---------------------------------------------------------------------------
 // dK, dV. Work-group: keys [k0, k0 + 128) of kv head g of batch b, wave w
@@ -96,6 +191,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char o_lds1[L::TILEB];
     __shared__ __attribute__((aligned(16))) float st_lds0[2 * BQ];   // L2 then Delta
     __shared__ __attribute__((aligned(16))) float st_lds1[2 * BQ];
+    __shared__ SplitLds sl;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -103,34 +199,25 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
     const int nbg = p.B * p.H_kv;
-    const int hs = blockIdx.x % p.hsplit;     // head part
-    const int id = blockIdx.x / p.hsplit;
-    const int tk = id / nbg;                  // key tile; tile 0 (most work) first
-    const int bg = id - tk * nbg;
+    // Work-group: with the window split the first nfar work-groups are far
+    // parts (b, g, chunk); the others are (key tile, b, g, head part), key
+    // tile 0 (most work) first.
+    int blk = blockIdx.x;
+    const bool far = WINDOW && blk < p.nfar;
+    int hs = 0, chunk = 0, tk0 = 0, bg;
+    if (far) {
+        chunk = blk % p.nchunk;
+        bg = blk / p.nchunk;
+    } else {
+        if (WINDOW) blk -= p.nfar;
+        hs = blk % p.hsplit;
+        const int id = blk / p.hsplit;
+        tk0 = id / nbg;
+        bg = id - tk0 * nbg;
+    }
     const int b = bg / p.H_kv, g = bg - b * p.H_kv;
-    const int k0 = tk * kBlk;
-    const int wk0 = k0 + 32 * wave;
-    const int key = wk0 + col;
-    const bool wave_live = wk0 < T;
     const long long qrs = (long long)p.H * D;      // row stride of q, o, dout, dq
     const long long krs = (long long)p.H_kv * D;   // row stride of k, v, dk, dv
-
-    // K and V rows of this lane's key as B operands: lane (col, half) holds
-    // dims 16 ks + 8 half + 0..7.
-    e8_t kf[KS], vf[KS];
-    {
-        const long long off = ((long long)b * T + key) * krs + (long long)g * D + 8 * half;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-            if (key < T) {
-                x = *(const u32x4_t *)((const unsigned short *)p.k + off + 16 * ks);
-                y = *(const u32x4_t *)((const unsigned short *)p.v + off + 16 * ks);
-            }
-            kf[ks] = __builtin_bit_cast(e8_t, x);
-            vf[ks] = __builtin_bit_cast(e8_t, y);
-        }
-    }
 
     // Staging offsets: row within the tile and physical chunk of each lane.
     int qoff[NI];
@@ -160,197 +247,304 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
         }
     }
     const bool tzero = D < 32 && col >= D;   // D=16: rows 16..31 of dO^T / Q^T are zero
-
-    f32x16_t dkacc[ND], dvacc[ND];
-#pragma unroll
-    for (int n = 0; n < ND; ++n) {
-        dkacc[n] = f32x16_t{};
-        dvacc[n] = f32x16_t{};
-    }
     float c;
     asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
 
-    // Query tiles: every query head of the group, tiles that reach this key
-    // tile (causal: rows >= k0).
-    const int nqt_all = (T + BQ - 1) / BQ;
-    const int i_beg = CAUSAL ? k0 / BQ : 0;
-    // Window mode: the global bits of this work-group's 128 keys (two words)
-    // and of this lane's key; a key tile holding no global token sees only the
-    // query tiles meeting its band [k0 - window, k0 + 127 + window].
-    unsigned long long gw0 = 0ull, gw1 = 0ull;
-    if (WINDOW && p.gbits) {
-        gw0 = p.gbits[k0 / 64];
-        if (k0 / 64 + 1 < p.nwords) gw1 = p.gbits[k0 / 64 + 1];
-    }
-    const bool kglob = WINDOW && key < T &&
-                       (((key - k0 < 64 ? gw0 : gw1) >> ((key - k0) & 63)) & 1ull);
-    const bool wave_glob = WINDOW && (((wave < 2 ? gw0 : gw1) >> (32 * (wave & 1))) &
-                                      0xffffffffull) != 0ull;
-    int qlo = i_beg, qhi = nqt_all - 1;
-    if (WINDOW && (gw0 | gw1) == 0ull) {
-        const long long lo = max(0LL, (long long)k0 - p.window) / BQ;
-        const long long hi = ((long long)k0 + kBlk - 1 + p.window) / BQ;
-        qlo = max(qlo, (int)lo);
-        qhi = (int)min((long long)qhi, hi);
-    }
-    const int nqt = qhi - qlo + 1;
-    const int h0 = g * p.group + hs * p.group / p.hsplit;      // this part's query heads
-    const int nh = g * p.group + (hs + 1) * p.group / p.hsplit - h0;
-    const int nit = nh * nqt;
-
-    auto stage = [&](int it, unsigned char *qd, unsigned char *od, float *sd)
-        __attribute__((always_inline)) {
-        const int h = h0 + it / nqt;
-        const int q0 = (qlo + it % nqt) * BQ;
-        const long long hoff = (long long)b * T * qrs + (long long)h * D;
-        stage_tile<D>((const unsigned short *)p.q + hoff, (const unsigned short *)p.dout + hoff,
-                      qrs, qrs, T, q0, wave, qoff, qoff, qd, od);
-        if (wave < 2) {
-            const long long r = ((long long)b * p.H + h) * T + q0;
-            const float *src = (wave == 0 ? p.l2 : p.delta) + r;
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<float *>(src), (short)0, min(T - q0, BQ) * 4, kRsrcWord3);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sd + BQ * wave), 4,
-                                                     lane * 4, 0, 0, 0);
+    // Window split (nslots > 0): which global key tiles this work-group
+    // serves. A main work-group scans only when its own tile holds a global
+    // token; a far work-group serves every eligible tile, one job each.
+    int njobs = 1, elig = 0, mine = -1;
+    if (WINDOW && p.nslots > 0) {
+        bool scan = far;
+        if (!far) {
+            unsigned long long x = p.gbits[2 * tk0];
+            if (2 * tk0 + 1 < p.nwords) x |= p.gbits[2 * tk0 + 1];
+            scan = x != 0ull;
         }
-    };
+        if (scan) {
+            scan_global_tiles(p, far ? -1 : tk0, sl);
+            elig = sl.nelig;
+            mine = sl.mine;
+        }
+        if (far) {
+            njobs = elig;
+            if (bg == 0 && chunk == 0 && tid == 0) p.gmeta[0] = elig > 0 ? sl.end[elig - 1] : 0;
+        }
+    }
+    const bool split_tile = !far && mine >= 0 && mine < elig;
 
-    auto compute = [&](int it, const unsigned char *qt, const unsigned char *ot, const float *st)
-        __attribute__((always_inline)) {
-        const int q0 = (qlo + it % nqt) * BQ;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int n0 = q0 + 32 * sub;
-            if (n0 >= T || (CAUSAL && n0 + 31 < wk0)) continue;   // wave-uniform
-            bool need_mask = (CAUSAL && n0 < wk0 + 31) || (wk0 + 31 >= T);
-            if (WINDOW) {
-                // rows n0..n0+31 against this wave's keys wk0..wk0+31
-                const bool meets = n0 + 31 >= wk0 - p.window && n0 <= wk0 + 31 + p.window;
-                if (!meets && !wave_glob) continue;
-                const bool inside = n0 + 31 - wk0 <= p.window && wk0 + 31 - n0 <= p.window;
-                need_mask = need_mask || !inside;
-            }
-            f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+    for (int job = 0; job < njobs; ++job) {
+        if (job > 0) __syncthreads();    // every wave is done with the previous job's tiles
+        const int tk = far ? sl.tile[job] : tk0;
+        const int kbefore = far ? sl.before[job] : (split_tile ? sl.before[mine] : 0);
+        const int k0 = tk * kBlk;
+        const int wk0 = k0 + 32 * wave;
+        const int key = wk0 + col;
+        const bool wave_live = wk0 < T;
+
+        // K and V rows of this lane's key as B operands: lane (col, half) holds
+        // dims 16 ks + 8 half + 0..7.
+        e8_t kf[KS], vf[KS];
+        {
+            const long long off = ((long long)b * T + key) * krs + (long long)g * D + 8 * half;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const e8_t a = __builtin_bit_cast(
-                    e8_t, *(const lds_bf16x8_t *)(qt + raddr[ks] + 32 * sub * L::ROWB));
-                const e8_t a2 = __builtin_bit_cast(
-                    e8_t, *(const lds_bf16x8_t *)(ot + raddr[ks] + 32 * sub * L::ROWB));
-                s = H16::mfma(a, kf[ks], s);
-                dp = H16::mfma(a2, vf[ks], dp);
-            }
-            // P and dS; register r is query n0 + 8(r/4) + 4half + r%4.
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4_t l4 = *(const lds_f32x4_t *)(st + 32 * sub + 8 * gq + 4 * half);
-                const f32x4_t d4 = *(const lds_f32x4_t *)(st + BQ + 32 * sub + 8 * gq + 4 * half);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 4 * gq + e;
-                    const float pr = fast_exp2(fmaf(s[r], c, -l4[e]));
-                    s[r] = pr;
-                    dp[r] = pr * (dp[r] - d4[e]);
+                u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+                if (key < T) {
+                    x = *(const u32x4_t *)((const unsigned short *)p.k + off + 16 * ks);
+                    y = *(const u32x4_t *)((const unsigned short *)p.v + off + 16 * ks);
                 }
-            }
-            if (need_mask) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qn = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    bool ok = key < T && (!CAUSAL || key <= qn);
-                    if (WINDOW)
-                        ok = ok && ((qn - key <= p.window && key - qn <= p.window) || kglob);
-                    s[r] = ok ? s[r] : 0.f;
-                    dp[r] = ok ? dp[r] : 0.f;
-                }
-            }
-            e8_t pb[2], sb[2];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[0][e] = (E)s[e];
-                pb[1][e] = (E)s[8 + e];
-                sb[0][e] = (E)dp[e];
-                sb[1][e] = (E)dp[8 + e];
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int ro = (32 * sub + 16 * s2) * L::ROWB;
-#pragma unroll
-                for (int n = 0; n < ND; ++n) {
-                    const int tn = D >= 32 ? n : 0;
-                    e8_t ao = __builtin_shufflevector(H16::read_tr(ot + taddr[tn] + ro),
-                                                      H16::read_tr(ot + taddr8[tn] + ro), 0, 1, 2,
-                                                      3, 4, 5, 6, 7);
-                    e8_t aq = __builtin_shufflevector(H16::read_tr(qt + taddr[tn] + ro),
-                                                      H16::read_tr(qt + taddr8[tn] + ro), 0, 1, 2,
-                                                      3, 4, 5, 6, 7);
-                    if (tzero) {
-                        ao = e8_t{};
-                        aq = e8_t{};
-                    }
-                    dvacc[n] = H16::mfma(ao, pb[s2], dvacc[n]);
-                    dkacc[n] = H16::mfma(aq, sb[s2], dkacc[n]);
-                }
+                kf[ks] = __builtin_bit_cast(e8_t, x);
+                vf[ks] = __builtin_bit_cast(e8_t, y);
             }
         }
-    };
 
-    auto step = [&](int it, const unsigned char *qt, const unsigned char *ot, const float *st,
-                    unsigned char *qn, unsigned char *on, float *sn) __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of tile `it` have landed
-        __syncthreads();
-        if (it + 1 < nit) stage(it + 1, qn, on, sn);
-        if (wave_live) compute(it, qt, ot, st);
-    };
-    stage(0, q_lds0, o_lds0, st_lds0);
-    for (int it = 0; it < nit; it += 2) {
-        step(it, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1);
-        if (it + 1 < nit) step(it + 1, q_lds1, o_lds1, st_lds1, q_lds0, o_lds0, st_lds0);
-    }
+        f32x16_t dkacc[ND], dvacc[ND];
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+            dkacc[n] = f32x16_t{};
+            dvacc[n] = f32x16_t{};
+        }
 
-    if (!wave_live || key >= T) return;
-    // dK^T / dV^T register r of block n is dim 32n + 8(r/4) + 4half + r%4.
-    const long long off = ((long long)b * T + key) * krs + (long long)g * D;
-    if (p.hsplit > 1) {
-        // this part's fp32 sums; the reduce kernel adds the parts and scales dK
-        const long long poff = (long long)hs * p.B * T * krs + off;
+        // Window mode: the global bits of this tile's 128 keys (two words) and
+        // of this lane's key.
+        unsigned long long gw0 = 0ull, gw1 = 0ull;
+        if (WINDOW && p.gbits) {
+            gw0 = p.gbits[k0 / 64];
+            if (k0 / 64 + 1 < p.nwords) gw1 = p.gbits[k0 / 64 + 1];
+        }
+        const bool kglob = WINDOW && key < T &&
+                           (((key - k0 < 64 ? gw0 : gw1) >> ((key - k0) & 63)) & 1ull);
+        const bool wave_glob = WINDOW && (((wave < 2 ? gw0 : gw1) >> (32 * (wave & 1))) &
+                                          0xffffffffull) != 0ull;
+
+        // Query tiles visited, as iterations it in [itb, ite) of a list of
+        // (query head, query tile) pairs: head hbase + it / nper, tile index
+        // f = it % nper mapped to i_beg + f (f < nleft) or a2 + f - nleft.
+        // Main work-group: the heads of its part, tiles that reach this key
+        // tile (causal: rows >= k0); in window mode only those meeting the
+        // band [k0 - window, k0 + 127 + window], unless the tile holds a
+        // global token and is not split. Far work-group: chunk `chunk` of all
+        // heads x the tiles outside the band (there only global keys are
+        // visible).
+        const int nqt_all = (T + BQ - 1) / BQ;
+        const int i_beg = CAUSAL ? k0 / BQ : 0;
+        int lo = i_beg, hi = nqt_all - 1;
+        if (WINDOW && ((gw0 | gw1) == 0ull || split_tile || far)) {
+            lo = (int)(max(0LL, (long long)k0 - p.window) / BQ);
+            hi = (int)min((long long)nqt_all - 1, ((long long)k0 + kBlk - 1 + p.window) / BQ);
+        }
+        int hbase, nper, nleft = 0, a2, itb, ite;
+        if (far) {
+            nleft = max(0, min(lo, nqt_all) - i_beg);
+            a2 = max(hi + 1, i_beg);
+            nper = nleft + max(0, nqt_all - a2);
+            hbase = g * p.group;
+            const long long n = (long long)p.group * nper;
+            itb = (int)(chunk * n / p.nchunk);
+            ite = (int)((chunk + 1) * n / p.nchunk);
+        } else {
+            a2 = max(lo, i_beg);
+            nper = hi - a2 + 1;
+            hbase = g * p.group + hs * p.group / p.hsplit;     // this part's query heads
+            const int nh = g * p.group + (hs + 1) * p.group / p.hsplit - hbase;
+            itb = 0;
+            ite = nh * nper;
+        }
+        auto qtile0 = [&](int it, int &h) __attribute__((always_inline)) -> int {
+            const int hq = it / nper;
+            const int f = it - hq * nper;
+            h = hbase + hq;
+            return (f < nleft ? i_beg + f : a2 + (f - nleft)) * BQ;
+        };
+
+        auto stage = [&](int it, unsigned char *qd, unsigned char *od, float *sd)
+            __attribute__((always_inline)) {
+            int h;
+            const int q0 = qtile0(it, h);
+            const long long hoff = (long long)b * T * qrs + (long long)h * D;
+            stage_tile<D>((const unsigned short *)p.q + hoff, (const unsigned short *)p.dout + hoff,
+                          qrs, qrs, T, q0, wave, qoff, qoff, qd, od);
+            if (wave < 2) {
+                const long long r = ((long long)b * p.H + h) * T + q0;
+                const float *src = (wave == 0 ? p.l2 : p.delta) + r;
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float *>(src), (short)0, min(T - q0, BQ) * 4, kRsrcWord3);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sd + BQ * wave), 4,
+                                                         lane * 4, 0, 0, 0);
+            }
+        };
+
+        auto compute = [&](int it, const unsigned char *qt, const unsigned char *ot,
+                           const float *st) __attribute__((always_inline)) {
+            int h;
+            const int q0 = qtile0(it, h);
 #pragma unroll
-        for (int n = 0; n < ND; ++n)
+            for (int sub = 0; sub < 2; ++sub) {
+                const int n0 = q0 + 32 * sub;
+                if (n0 >= T || (CAUSAL && n0 + 31 < wk0)) continue;   // wave-uniform
+                bool need_mask = (CAUSAL && n0 < wk0 + 31) || (wk0 + 31 >= T);
+                if (WINDOW) {
+                    // rows n0..n0+31 against this wave's keys wk0..wk0+31
+                    const bool meets = n0 + 31 >= wk0 - p.window && n0 <= wk0 + 31 + p.window;
+                    if (!meets && !wave_glob) continue;
+                    const bool inside = n0 + 31 - wk0 <= p.window && wk0 + 31 - n0 <= p.window;
+                    need_mask = need_mask || !inside;
+                }
+                f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d = 32 * n + 8 * rg + 4 * half;
-                if (D >= 32 || d < D) {
-                    f32x4_t k4, v4;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const e8_t a = __builtin_bit_cast(
+                        e8_t, *(const lds_bf16x8_t *)(qt + raddr[ks] + 32 * sub * L::ROWB));
+                    const e8_t a2v = __builtin_bit_cast(
+                        e8_t, *(const lds_bf16x8_t *)(ot + raddr[ks] + 32 * sub * L::ROWB));
+                    s = H16::mfma(a, kf[ks], s);
+                    dp = H16::mfma(a2v, vf[ks], dp);
+                }
+                // P and dS; register r is query n0 + 8(r/4) + 4half + r%4.
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4_t l4 = *(const lds_f32x4_t *)(st + 32 * sub + 8 * gq + 4 * half);
+                    const f32x4_t d4 =
+                        *(const lds_f32x4_t *)(st + BQ + 32 * sub + 8 * gq + 4 * half);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        k4[e] = dkacc[n][4 * rg + e];
-                        v4[e] = dvacc[n][4 * rg + e];
+                        const int r = 4 * gq + e;
+                        const float pr = fast_exp2(fmaf(s[r], c, -l4[e]));
+                        s[r] = pr;
+                        dp[r] = pr * (dp[r] - d4[e]);
                     }
-                    *(f32x4_t *)(p.dkpart + poff + d) = k4;
-                    *(f32x4_t *)(p.dvpart + poff + d) = v4;
+                }
+                if (need_mask) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qn = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                        bool ok = key < T && (!CAUSAL || key <= qn);
+                        if (WINDOW)
+                            ok = ok && ((qn - key <= p.window && key - qn <= p.window) || kglob);
+                        s[r] = ok ? s[r] : 0.f;
+                        dp[r] = ok ? dp[r] : 0.f;
+                    }
+                }
+                e8_t pb[2], sb[2];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pb[0][e] = (E)s[e];
+                    pb[1][e] = (E)s[8 + e];
+                    sb[0][e] = (E)dp[e];
+                    sb[1][e] = (E)dp[8 + e];
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int ro = (32 * sub + 16 * s2) * L::ROWB;
+#pragma unroll
+                    for (int n = 0; n < ND; ++n) {
+                        const int tn = D >= 32 ? n : 0;
+                        e8_t ao = __builtin_shufflevector(H16::read_tr(ot + taddr[tn] + ro),
+                                                          H16::read_tr(ot + taddr8[tn] + ro), 0,
+                                                          1, 2, 3, 4, 5, 6, 7);
+                        e8_t aq = __builtin_shufflevector(H16::read_tr(qt + taddr[tn] + ro),
+                                                          H16::read_tr(qt + taddr8[tn] + ro), 0,
+                                                          1, 2, 3, 4, 5, 6, 7);
+                        if (tzero) {
+                            ao = e8_t{};
+                            aq = e8_t{};
+                        }
+                        dvacc[n] = H16::mfma(ao, pb[s2], dvacc[n]);
+                        dkacc[n] = H16::mfma(aq, sb[s2], dkacc[n]);
+                    }
                 }
             }
-        return;
-    }
-    unsigned short *dkrow = (unsigned short *)p.dk + off;
-    unsigned short *dvrow = (unsigned short *)p.dv + off;
-    const float sc = p.scale;
+        };
+
+        auto step = [&](int it, const unsigned char *qt, const unsigned char *ot, const float *st,
+                        unsigned char *qn, unsigned char *on, float *sn)
+            __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of tile `it` have landed
+            __syncthreads();
+            if (it + 1 < ite) stage(it + 1, qn, on, sn);
+            if (wave_live) compute(it, qt, ot, st);
+        };
+        if (itb < ite) stage(itb, q_lds0, o_lds0, st_lds0);
+        for (int it = itb; it < ite; it += 2) {
+            step(it, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1);
+            if (it + 1 < ite) step(it + 1, q_lds1, o_lds1, st_lds1, q_lds0, o_lds0, st_lds0);
+        }
+
+        if (wave_live && key < T) {
+            // dK^T / dV^T register r of block n is dim 32n + 8(r/4) + 4half + r%4.
+            const long long off = ((long long)b * T + key) * krs + (long long)g * D;
+            if (far) {
+                // nothing for the tile's other keys: they see no far query
+            } else if (p.hsplit > 1) {
+                // this part's fp32 sums; the reduce kernel adds the parts and scales dK
+                const long long poff = (long long)hs * p.B * T * krs + off;
 #pragma unroll
-    for (int n = 0; n < ND; ++n)
+                for (int n = 0; n < ND; ++n)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const int d = 32 * n + 8 * rg + 4 * half;
-            if (D >= 32 || d < D) {
-                e4_t k4, v4;
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int d = 32 * n + 8 * rg + 4 * half;
+                        if (D >= 32 || d < D) {
+                            f32x4_t k4, v4;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    k4[e] = (E)(dkacc[n][4 * rg + e] * sc);
-                    v4[e] = (E)dvacc[n][4 * rg + e];
-                }
-                *(u32x2_t *)(dkrow + d) = __builtin_bit_cast(u32x2_t, k4);
-                *(u32x2_t *)(dvrow + d) = __builtin_bit_cast(u32x2_t, v4);
+                            for (int e = 0; e < 4; ++e) {
+                                k4[e] = dkacc[n][4 * rg + e];
+                                v4[e] = dvacc[n][4 * rg + e];
+                            }
+                            *(f32x4_t *)(p.dkpart + poff + d) = k4;
+                            *(f32x4_t *)(p.dvpart + poff + d) = v4;
+                        }
+                    }
+            } else {
+                unsigned short *dkrow = (unsigned short *)p.dk + off;
+                unsigned short *dvrow = (unsigned short *)p.dv + off;
+                const float sc = p.scale;
+#pragma unroll
+                for (int n = 0; n < ND; ++n)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int d = 32 * n + 8 * rg + 4 * half;
+                        if (D >= 32 || d < D) {
+                            e4_t k4, v4;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                k4[e] = (E)(dkacc[n][4 * rg + e] * sc);
+                                v4[e] = (E)dvacc[n][4 * rg + e];
+                            }
+                            *(u32x2_t *)(dkrow + d) = __builtin_bit_cast(u32x2_t, k4);
+                            *(u32x2_t *)(dvrow + d) = __builtin_bit_cast(u32x2_t, v4);
+                        }
+                    }
+            }
+            if (WINDOW && kglob && (far || split_tile)) {
+                // A global key of a split tile: this part's fp32 sums (dK
+                // unscaled) go to its slot, rank = global keys before it.
+                const int kk = key - k0;
+                const int rank = kbefore + (kk < 64 ? __popcll(gw0 & ((1ull << kk) - 1ull))
+                                                    : __popcll(gw0) +
+                                                          __popcll(gw1 & ((1ull << (kk - 64)) - 1ull)));
+                const int part = far ? p.hsplit + chunk : hs;
+                const long long goff = (((long long)rank * p.nparts + part) * nbg + bg) * D;
+#pragma unroll
+                for (int n = 0; n < ND; ++n)
+#pragma unroll
+                    for (int rg = 0; rg < 4; ++rg) {
+                        const int d = 32 * n + 8 * rg + 4 * half;
+                        if (D >= 32 || d < D) {
+                            f32x4_t k4, v4;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                k4[e] = dkacc[n][4 * rg + e];
+                                v4[e] = dvacc[n][4 * rg + e];
+                            }
+                            *(f32x4_t *)(p.gpk + goff + d) = k4;
+                            *(f32x4_t *)(p.gpv + goff + d) = v4;
+                        }
+                    }
+                if (far && bg == 0 && chunk == 0 && half == 0) p.gmeta[4 + rank] = key;
             }
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -454,15 +648,9 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
         int t = j + 1;
         if (!WINDOW) return t;
         const unsigned long long *gbits = p.gbits;
-        if (t < blo) {
-            if (!gbits) return blo;
-            while (t < blo && gbits[t] == 0ull) ++t;
-            return t;
-        }
+        if (t < blo) return gbits ? first_nonzero_word(gbits, t, blo) : blo;
         if (t <= bhi) return t;
-        if (gbits)
-            while (t < nkt && gbits[t] == 0ull) ++t;
-        return min(t, nkt);
+        return gbits ? first_nonzero_word(gbits, t, nkt) : max(t, nkt);
     };
     // read between steps, never after a step's prefetch is issued
     auto tile_bits = [&](int t) __attribute__((always_inline)) -> unsigned long long {
@@ -659,6 +847,42 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(BwdParams p, long lo
 }
 
 // ---------------------------------------------------------------------------
+// Global keys of split tiles: dK = scale * sum_part gpk[slot][part], dV =
+// sum_part gpv[slot][part], parts in order (deterministic), over the rows the
+// other kernels wrote for those keys. Thread: (slot, b, g, 4 dims).
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(256) void fa_bwd_gsum_kernel(BwdParams p, int D) {
+    typedef E e4v __attribute__((ext_vector_type(4)));
+    const int nbg = p.B * p.H_kv;
+    const long long per = (long long)nbg * (D / 4);
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long r = i / per;
+    if (r >= p.gmeta[0] || r >= p.nslots) return;
+    const int key = p.gmeta[4 + r];
+    if (key < 0 || key >= p.T) return;
+    const int rest = (int)(i - r * per);
+    const int bg = rest / (D / 4);
+    const int d = 4 * (rest - bg * (D / 4));
+    const int b = bg / p.H_kv, g = bg - b * p.H_kv;
+    f32x4_t k = {0.f, 0.f, 0.f, 0.f}, v = {0.f, 0.f, 0.f, 0.f};
+    for (int part = 0; part < p.nparts; ++part) {
+        const long long off = ((r * p.nparts + part) * nbg + bg) * D + d;
+        k += *(const f32x4_t *)(p.gpk + off);
+        v += *(const f32x4_t *)(p.gpv + off);
+    }
+    e4v k4, v4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        k4[e] = (E)(k[e] * p.scale);
+        v4[e] = (E)v[e];
+    }
+    const long long o = (((long long)b * p.T + key) * p.H_kv + g) * D + d;
+    *(e4v *)((E *)p.dk + o) = k4;
+    *(e4v *)((E *)p.dv + o) = v4;
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation (no HIP calls), launch.
 // ---------------------------------------------------------------------------
 constexpr long long kMaxElems = 1LL << 62;
@@ -696,18 +920,49 @@ long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, long long *
     return total;
 }
 
-// dQ first: it also writes Delta and L2, which the dK/dV kernel reads.
+// Far parts per split global tile: runs of about the main work-group's
+// iteration count (its heads x the band's query tiles) over all heads x all
+// query tiles.
+int far_chunks(int T, int window, int group, int hs) {
+    const long long nqt = ((long long)T + 63) / 64;
+    const long long nband = ((long long)kBlk + 2LL * window) / 64 + 2;
+    const long long nh = (group + hs - 1) / hs;
+    long long run = nh * nband;
+    if (run < 4) run = 4;
+    long long n = ((long long)group * nqt + run - 1) / run;
+    if (n < 1) n = 1;
+    return (int)(n < 256 ? n : 256);
+}
+
+// Bytes of the window split region for `slots` global-key slots: a 16-byte
+// header, the slot -> key map (padded to 16 bytes), then gpk and gpv.
+long long split_bytes(long long slots, int nparts, int B, int H_kv, int D) {
+    if (slots <= 0) return 0;
+    long long per, map = (slots * 4 + 15) / 16 * 16, total;
+    if (__builtin_mul_overflow((long long)nparts * B, (long long)H_kv * D * 8, &per) ||
+        __builtin_mul_overflow(per, slots, &total) || __builtin_add_overflow(total, 16 + map, &total))
+        return -1;
+    return total;
+}
+
+// dQ first: it also writes Delta and L2, which the dK/dV kernel reads. The
+// global-key sums go last, over the rows the dK/dV (or reduce) kernel wrote.
 template <typename E, int D, bool CAUSAL, bool WINDOW>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
     hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
                        dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW>),
-                       dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit)),
+                       dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit + p.nfar)),
                        dim3(kThreads), 0, s, p);
     if (p.hsplit > 1) {
         const long long n = (long long)p.B * p.T * p.H_kv * D;
         hipLaunchKernelGGL((fa_bwd_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
                            dim3(256), 0, s, p, n);
+    }
+    if (WINDOW && p.nslots > 0) {
+        const long long n = (long long)p.nslots * p.B * p.H_kv * (D / 4);
+        hipLaunchKernelGGL((fa_bwd_gsum_kernel<E>), dim3((unsigned)((n + 255) / 256)),
+                           dim3(256), 0, s, p, D);
     }
 }
 
@@ -735,6 +990,21 @@ extern "C" long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D
         (D != 16 && D != 32 && D != 64 && D != 128))
         return -1;
     return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split), nullptr);
+}
+
+extern "C" long long fa_bwd_window_workspace_bytes(int B, int H, int H_kv, int T, int D,
+                                                   int window, int n_global, int head_split) {
+    const long long base = fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split);
+    if (base < 0 || window < 0 || n_global < 0) return -1;
+    if (n_global == 0 || T == 0 || B == 0) return base;
+    const int hs = head_parts(B, H, H_kv, T, head_split);
+    const int w = window < T ? window : T;
+    const long long slots = n_global < T ? n_global : T;
+    const long long extra =
+        split_bytes(slots, hs + far_chunks(T, w, H / H_kv, hs), B, H_kv, D);
+    long long total;
+    if (extra < 0 || __builtin_add_overflow(base, extra, &total)) return -1;
+    return total;
 }
 
 namespace {
@@ -793,6 +1063,36 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     p.window = window < 0 ? -1 : (window < T ? window : T);
     p.gbits = window < 0 ? nullptr : (const unsigned long long *)global_bits;
     p.nwords = (int)(((long long)T + 63) / 64);
+    // Window split: as many global-key slots as the workspace holds past
+    // what fa_bwd needs (none: every global tile keeps the full walk).
+    p.nslots = p.nchunk = p.nfar = 0;
+    p.nparts = hs;
+    p.gmeta = nullptr;
+    p.gpk = p.gpv = nullptr;
+    if (window >= 0 && global_bits) {
+        const int nch = far_chunks(T, p.window, p.group, hs);
+        const int nparts = hs + nch;
+        const long long avail = workspace_bytes - need;
+        long long per;
+        if (!__builtin_mul_overflow((long long)nparts * B, (long long)H_kv * D * 8, &per)) {
+            // split_bytes(s) >= 16 + s * (per + 4): start from that bound
+            long long slots = avail > 16 ? (avail - 16) / (per + 4) : 0;
+            if (slots > T) slots = T;
+            while (slots > 0 && split_bytes(slots, nparts, B, H_kv, D) > avail) --slots;
+            const long long nfar = (long long)B * H_kv * nch;
+            if (slots > 0 && (long long)B * H_kv * nblk * hs + nfar <= kMaxGridB &&
+                slots * B * H_kv * (D / 4) / 256 + 1 <= kMaxGridB) {
+                p.nslots = (int)slots;
+                p.nchunk = nch;
+                p.nparts = nparts;
+                p.nfar = (int)nfar;
+                char *base = (char *)workspace + need;
+                p.gmeta = (int *)base;
+                p.gpk = (float *)(base + 16 + (slots * 4 + 15) / 16 * 16);
+                p.gpv = p.gpk + slots * nparts * B * H_kv * D;
+            }
+        }
+    }
     hipStream_t s = (hipStream_t)stream;
     const bool win = window >= 0;
     if (dtype == FA_DTYPE_BF16) {

@@ -36,6 +36,21 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// First index in [t, lim) whose 64-bit word of a global-token bitmap is
+// nonzero (lim if none): each lane tests one word, 64 words a step, and a
+// ballot picks the first. Call from wave-uniform control flow, with every
+// word below lim in bounds.
+__device__ __forceinline__ int first_nonzero_word(const unsigned long long *bits, int t,
+                                                  int lim) {
+    const int lane = threadIdx.x & 63;
+    for (; t < lim; t += 64) {
+        const int w = t + lane;
+        const unsigned long long m = __ballot(w < lim && bits[w] != 0ull);
+        if (m != 0ull) return t + __builtin_ctzll(m);
+    }
+    return lim;
+}
+
 // ---------------------------------------------------------------------------
 // LDS tile of 64 rows x D 16-bit elements, rows of 2D bytes, unpadded. The
 // 16-byte chunks of each row are XOR-permuted so that the MFMA operand reads

@@ -215,15 +215,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
         int t = j + 1;
         if (!WINDOW) return t;
         const unsigned long long *gbits = p.gbits;
-        if (t < blo) {
-            if (!gbits) return blo;
-            while (t < blo && gbits[t] == 0ull) ++t;
-            return t;
-        }
+        if (t < blo) return gbits ? first_nonzero_word(gbits, t, blo) : blo;
         if (t <= bhi) return t;
-        if (gbits)
-            while (t < jend && gbits[t] == 0ull) ++t;
-        return min(t, jend);
+        return gbits ? first_nonzero_word(gbits, t, jend) : max(t, jend);
     };
     // Global-token bits of tile t, read between steps (never after a step's
     // prefetch is issued, whose loads a wait for this read would include).

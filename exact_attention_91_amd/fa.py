@@ -64,6 +64,8 @@ def _lib():
         lib.fa_bwd_window.restype = _I
         lib.fa_bwd_workspace_bytes.argtypes = [_I] * 6
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
+        lib.fa_bwd_window_workspace_bytes.argtypes = [_I] * 8
+        lib.fa_bwd_window_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_status_str.argtypes = [_I]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -287,7 +289,15 @@ def bwd_workspace_bytes(B: int, H: int, H_kv: int, T: int, D: int, head_split: i
     return int(_lib().fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split))
 
 
-def _bwd_args(q, k, v, o, lse, dout, scale, head_split, workspace):
+def bwd_window_workspace_bytes(B: int, H: int, H_kv: int, T: int, D: int, window: int,
+                               n_global: int, head_split: int = 0) -> int:
+    """Bytes of device workspace bwd_window uses to split the far queries of
+    up to n_global global tokens (-1 for invalid sizes)."""
+    return int(_lib().fa_bwd_window_workspace_bytes(B, H, H_kv, T, D, int(window),
+                                                    int(n_global), head_split))
+
+
+def _bwd_args(q, k, v, o, lse, dout, scale, head_split, workspace, need=None):
     _check(q, k, v)
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(f"the backward takes bfloat16 or float16 inputs, got {q.dtype}")
@@ -305,7 +315,8 @@ def _bwd_args(q, k, v, o, lse, dout, scale, head_split, workspace):
     H_kv = k.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    need = bwd_workspace_bytes(B, H, H_kv, T, D, head_split)
+    if need is None:
+        need = bwd_workspace_bytes(B, H, H_kv, T, D, head_split)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
@@ -314,13 +325,29 @@ def _bwd_args(q, k, v, o, lse, dout, scale, head_split, workspace):
 
 
 def bwd_window(q, k, v, o, lse, dout, window: int, global_tokens=None, causal: bool = False,
-               scale=None, global_bits=None, workspace=None, head_split: int = 0):
+               scale=None, global_bits=None, workspace=None, head_split: int = 0,
+               n_global=None):
     """Backward of fwd_window (same window, global tokens, causal, scale; o and
-    lse from fwd_window). Returns (dq, dk, dv)."""
-    ptrs, dims, scale, workspace, grads = _bwd_args(q, k, v, o, lse, dout, scale, head_split,
-                                                    workspace)
+    lse from fwd_window). Returns (dq, dk, dv). When `workspace` is None it is
+    sized by bwd_window_workspace_bytes for n_global tokens: len(global_tokens),
+    or the bits set in global_bits when n_global is not given (a device sync)."""
     if global_tokens is not None and global_bits is not None:
         raise ValueError("give global_tokens or global_bits, not both")
+    B, T, H, D = q.shape
+    need = None
+    if workspace is None and (global_tokens is not None or global_bits is not None):
+        if n_global is None:
+            if global_tokens is not None:
+                n_global = len({int(t) for t in global_tokens if 0 <= int(t) < T})
+            else:
+                by = global_bits.view(torch.uint8).to(torch.int32)
+                n_global = int(((by.unsqueeze(-1) >> torch.arange(8, device=by.device)) & 1)
+                               .sum().item())
+        need = bwd_window_workspace_bytes(B, H, k.shape[2], T, D, window, n_global, head_split)
+        if need < 0:
+            raise ValueError("invalid sizes for the backward workspace")
+    ptrs, dims, scale, workspace, grads = _bwd_args(q, k, v, o, lse, dout, scale, head_split,
+                                                    workspace, need)
     if global_tokens is not None:
         global_bits = window_bitmap(global_tokens, dims[3], q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream

@@ -237,8 +237,14 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
  * same window, global_bits, causal and scale. Key tiles that no query sees
  * (outside every band and holding no global token) are skipped on both
  * sides. window >= 0 (FA_ERR_BAD_SHAPE otherwise); global_bits as in
- * fa_fwd_window (NULL = none); everything else as fa_bwd, with the same
- * workspace size.
+ * fa_fwd_window (NULL = none); everything else as fa_bwd.
+ * Workspace: at least fa_bwd_workspace_bytes(...). A tile of 128 keys that
+ * holds a global token is seen by queries far outside its band; bytes past
+ * that size (fa_bwd_window_workspace_bytes sizes them for n_global tokens)
+ * hold per-global-key fp32 partial sums, so that the far queries of such
+ * tiles are shared out over several work-groups and added in a fixed order
+ * by one more kernel (deterministic). Without them the result is the same
+ * up to rounding order, but each such tile is walked by one work-group.
  */
 int fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
                   const float *lse, const void *dout, void *dq, void *dk, void *dv, int B,
@@ -251,6 +257,18 @@ int fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
  * 8 * parts * B * T * H_kv * D when the group's heads are split into parts > 1;
  * -1 for invalid sizes or overflow. */
 long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D, int head_split);
+
+/* Workspace bytes fa_bwd_window needs to split the far queries of up to
+ * n_global global tokens (the count the bitmap was built from): the
+ * fa_bwd_workspace_bytes size plus, for n_global > 0, a 16-byte header, a
+ * slot map (4 bytes a slot, padded to 16) and 8 * slots * parts * B * H_kv * D
+ * bytes of fp32 sums, slots = min(n_global, T); parts depends on T, window,
+ * the group size and head_split. -1 for invalid sizes (window < 0,
+ * n_global < 0) or overflow. After a call, the header's first int32 is the
+ * number of global keys whose far queries were split (those of the first 64
+ * key tiles holding a global token, as long as all their keys have slots). */
+long long fa_bwd_window_workspace_bytes(int B, int H, int H_kv, int T, int D, int window,
+                                        int n_global, int head_split);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *fa_status_str(int status);

@@ -38,7 +38,8 @@ DT = _enum_values("fa_dtype_t")
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_window", "fa_bwd_workspace_bytes", "fa_fwd",
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_window", "fa_bwd_window_workspace_bytes",
+                                     "fa_bwd_workspace_bytes", "fa_fwd",
                                      "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
                                      "fa_fwd_strided", "fa_fwd_window", "fa_lse_combine",
                                      "fa_status_str", "fa_version", "fa_window_bitmap",
@@ -269,6 +270,29 @@ def test_bwd_workspace_bytes(lib):
     assert f(2, 4, 2, 100, 64, -1) == -1
     assert f(-1, 4, 2, 100, 64, 0) == -1
     assert f(1 << 30, 1 << 30, 1, 1 << 30, 64, 1) == -1
+
+
+def test_bwd_window_workspace_bytes(lib):
+    f = lib.fa_bwd_window_workspace_bytes
+    base = lib.fa_bwd_workspace_bytes
+    assert f(1, 2, 2, 2000, 64, 40, 0, 0) == base(1, 2, 2, 2000, 64, 0)
+    # 3 slots: 16-byte header, slot map (12 -> 16 bytes), then fp32 dK and dV
+    # sums of [slots][parts][B][H_kv][D]; parts = 1 head part + 7 far chunks
+    # (32 query tiles of 64 in runs of the band's 5)
+    assert f(1, 2, 2, 2000, 64, 40, 3, 0) == base(1, 2, 2, 2000, 64, 0) + 16 + 16 + \
+        3 * 8 * 1 * 2 * 64 * 8
+    # slots 1..4 share a 16-byte map; each slot adds parts x B x H_kv x D x 8
+    # bytes with parts = 3 head parts + at least one far chunk
+    extra = [f(2, 6, 1, 1800, 64, 50, n, 3) - base(2, 6, 1, 1800, 64, 3) for n in (1, 2, 4)]
+    per = extra[1] - extra[0]
+    assert per > 0 and per % (2 * 1 * 64 * 8) == 0 and (per // (2 * 64 * 8)) >= 3 + 1
+    assert extra[2] - extra[0] == 3 * per and extra[0] == 32 + per
+    assert f(1, 1, 1, 100, 64, 5, 500, 1) == f(1, 1, 1, 100, 64, 5, 100, 1)   # slots <= T
+    assert f(0, 1, 1, 100, 64, 5, 3, 1) == 0
+    assert f(1, 1, 1, 100, 64, -1, 3, 1) == -1
+    assert f(1, 1, 1, 100, 64, 5, -1, 1) == -1
+    assert f(1, 1, 1, 100, 48, 5, 3, 1) == -1
+    assert f(1 << 20, 1 << 10, 1 << 10, 1 << 20, 128, 5, 1 << 20, 1) == -1
 
 
 @pytest.mark.parametrize("kw,code", [

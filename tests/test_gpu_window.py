@@ -253,3 +253,125 @@ def test_window_scale_values(scale):
         check(x, "bf16", causal, scale, 20, (0, 150), o, lse, f"scale={scale}")
         got = run_bwd_window(x, do, causal, scale, 20, (0, 150))
         check_bwd(x, do64, "bf16", causal, scale, 20, (0, 150), got, f"scale={scale}")
+
+
+# ------------------------------------- far queries of global key tiles split
+
+def _bwd_pair(x, do, causal, scale, window, glob, head_split=0, n_global=None, n_split=None):
+    """(split, unsplit) gradients: the split one with a workspace sized for
+    n_global tokens (default: all of them), the unsplit one with fa_bwd's size.
+    The split call leaves in the first header word past fa_bwd's workspace the
+    number of global keys it served (n_split, default: all of them)."""
+    from exact_attention_91_amd import fa
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    B, T, H, D = q.shape
+    bits = fa.window_bitmap(glob, T, q.device)
+    o, lse = fa.fwd_window(q, k, v, window, causal=causal, scale=scale, global_bits=bits)
+    ng = len(set(glob)) if n_global is None else n_global
+    ws = torch.empty((fa.bwd_window_workspace_bytes(B, H, k.shape[2], T, D, window, ng,
+                                                     head_split),), dtype=torch.uint8,
+                     device="cuda")
+    ws0 = torch.empty((fa.bwd_workspace_bytes(B, H, k.shape[2], T, D, head_split),),
+                      dtype=torch.uint8, device="cuda")
+    a = fa.bwd_window(q, k, v, o, lse, do.cuda(), window, causal=causal, scale=scale,
+                      global_bits=bits, head_split=head_split, workspace=ws)
+    a2 = fa.bwd_window(q, k, v, o, lse, do.cuda(), window, causal=causal, scale=scale,
+                       global_bits=bits, head_split=head_split, workspace=ws)
+    u = fa.bwd_window(q, k, v, o, lse, do.cuda(), window, causal=causal, scale=scale,
+                      global_bits=bits, head_split=head_split, workspace=ws0)
+    torch.cuda.synchronize()
+    for s, s2 in zip(a, a2):
+        assert torch.equal(s, s2), "split backward not repeatable"
+    base = fa.bwd_workspace_bytes(B, H, k.shape[2], T, D, head_split)
+    served = int(ws[base:base + 4].cpu().view(torch.int32)[0])
+    assert served == (len({g for g in glob if 0 <= g < T}) if n_split is None else n_split)
+    return a, u
+
+
+def _check_split(a, u, T, glob):
+    """dQ and the rows of keys that are not global are bitwise those of the
+    unsplit walk (the far queries add exact zeros there); the global keys'
+    rows differ only in summation order."""
+    assert torch.equal(a[0], u[0])
+    gl = sorted({g for g in glob if 0 <= g < T})
+    other = torch.ones(T, dtype=torch.bool)
+    other[gl] = False
+    for s, w in zip(a[1:], u[1:]):
+        assert torch.equal(s[:, other.cuda()], w[:, other.cuda()])
+
+
+SPLIT_CASES = [
+    # T, window, globals, (B, H, H_kv), D
+    (2000, 40, (0, 1, 7), (1, 2, 2), 64),
+    (3000, 100, (5, 130, 131, 2999), (2, 2, 1), 64),
+    (1500, 0, (700,), (1, 3, 3), 16),
+    (1100, 64, (0, 500, 1099), (1, 4, 2), 128),
+    (2600, 33, tuple(range(0, 2600, 301)), (1, 2, 1), 32),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T,window,glob,heads,D", SPLIT_CASES)
+def test_bwd_window_split(causal, T, window, glob, heads, D):
+    from exact_attention_91_amd.inputs import generate_dout
+    B, H, H_kv = heads
+    seed = 12100 + T + D
+    say(f"case bwd window split causal={causal} T={T} window={window} globals={len(glob)} "
+        f"B={B} H={H} H_kv={H_kv} D={D} seed={seed}")
+    x = generate(B, H, H_kv, T, D, "bf16", seed)
+    do, do64 = generate_dout(B, H, T, D, "bf16", seed)
+    scale = default_scale(D)
+    a, u = _bwd_pair(x, do, causal, scale, window, glob)
+    _check_split(a, u, T, glob)
+    for g, label in ((a, "split"), (u, "unsplit")):
+        got = tuple(t.double().cpu().numpy() for t in g)
+        check_bwd(x, do64, "bf16", causal, scale, window, glob, got, label)
+
+
+@pytest.mark.parametrize("head_split", [1, 3, 0])
+def test_bwd_window_split_with_head_split(head_split):
+    """Grouped heads: the band part of each head part and the far chunks (all
+    heads) add into the same global-key slots."""
+    from exact_attention_91_amd.inputs import generate_dout
+    B, H, H_kv, T, D = 2, 6, 1, 1800, 64
+    glob = (0, 3, 900)
+    x = generate(B, H, H_kv, T, D, "bf16", 12200 + head_split)
+    do, do64 = generate_dout(B, H, T, D, "bf16", 12200 + head_split)
+    for causal in (False, True):
+        say(f"case bwd window split head_split={head_split} causal={causal}")
+        a, u = _bwd_pair(x, do, causal, 0.125, 50, glob, head_split=head_split)
+        _check_split(a, u, T, glob)
+        got = tuple(t.double().cpu().numpy() for t in a)
+        check_bwd(x, do64, "bf16", causal, 0.125, 50, glob, got, f"split hs={head_split}")
+
+
+@pytest.mark.parametrize("n_global,n_split", [(1, 1), (2, 1), (3, 3), (4, 4), (5, 5)])
+def test_bwd_window_split_too_few_slots(n_global, n_split):
+    """A workspace with slots for fewer global keys than there are: the global
+    tiles whose keys all have slots are split, the later ones keep the full
+    walk; the result is the same either way."""
+    from exact_attention_91_amd.inputs import generate_dout
+    B, H, H_kv, T, D = 1, 2, 2, 2100, 64
+    glob = (2, 300, 301, 1000, 2099)      # key tiles 0, 2, 2, 7, 16
+    x = generate(B, H, H_kv, T, D, "bf16", 12300)
+    do, do64 = generate_dout(B, H, T, D, "bf16", 12300)
+    say(f"case bwd window split n_global={n_global}")
+    a, u = _bwd_pair(x, do, True, 0.125, 30, glob, n_global=n_global, n_split=n_split)
+    _check_split(a, u, T, glob)
+    got = tuple(t.double().cpu().numpy() for t in a)
+    check_bwd(x, do64, "bf16", True, 0.125, 30, glob, got, f"slots={n_global}")
+
+
+def test_bwd_window_split_many_global_tiles():
+    """More key tiles holding a global token than the split serves (64): the
+    first 64 are split, the others keep the full walk."""
+    from exact_attention_91_amd.inputs import generate_dout
+    B, H, H_kv, T, D = 1, 1, 1, 128 * 70, 32
+    glob = tuple(range(5, T, 128))       # one token in each of 70 key tiles
+    x = generate(B, H, H_kv, T, D, "bf16", 12400)
+    do, do64 = generate_dout(B, H, T, D, "bf16", 12400)
+    say("case bwd window split 70 global tiles")
+    a, u = _bwd_pair(x, do, True, default_scale(D), 16, glob, n_split=64)
+    _check_split(a, u, T, glob)
+    got = tuple(t.double().cpu().numpy() for t in a)
+    check_bwd(x, do64, "bf16", True, default_scale(D), 16, glob, got, "70 tiles")
