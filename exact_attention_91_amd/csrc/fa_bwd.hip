@@ -1,5 +1,6 @@
 // fa_bwd.hip -- attention backward for MI355X (gfx950), and its C ABI
-// (fa_bwd, fa_bwd_workspace_bytes in include/fa.h).
+// (fa_bwd, fa_bwd_window, fa_bwd_workspace_bytes, fa_bwd_window_workspace_bytes
+// in include/fa.h).
 //
 // Method: "Flash Attention Memory Optimization Explained" (lzwjava.github.io),
 // "Key Mechanisms", backward checkpointing -- the backward pass recomputes the
@@ -26,6 +27,12 @@
 //    kernel), streams K and V tiles, computes S^T = K Q^T and dP^T = V dO^T,
 //    and accumulates dQ^T += K^T dS^T with K^T from transposing reads of the
 //    K tile.
+//  * fa_bwd_reduce_kernel (head split only): adds the fp32 parts in order.
+//  * Window mode (fa_bwd_window): both main kernels visit only the tiles that
+//    meet a tile's band or hold a global token. A key tile holding a global
+//    token is seen by far queries too; with workspace slots for the global
+//    keys, those far query tiles are shared out to extra dK/dV work-groups
+//    whose fp32 sums fa_bwd_gsum_kernel adds in a fixed order.
 //  Tiles read both as rows and transposed use the dual swizzle (dswz) of
 //  fa_device.h. Causal: key tiles wholly after a query tile are never loaded;
 //  query tiles wholly before a key tile are never loaded; waves skip the math
