@@ -73,6 +73,43 @@ def source_hash():
     return h.hexdigest()
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def one_thread_rate(orc, x, w, causal, seconds):
+    """The oracle on one host thread over evenly spaced query rows of the
+    workload (counted FLOP 4*D per visible key of each row), for about
+    `seconds`; the thread count is restored afterwards."""
+    import numpy as np
+    n_all = w.B * w.H * w.T
+    keep = orc.num_threads()
+    orc.set_num_threads(1)
+    try:
+        n = 64
+        while True:
+            rows = np.linspace(0, n_all - 1, n).astype(np.int64)
+            t0 = time.perf_counter()
+            orc.attention_rows(x.q64, x.k64, x.v64, causal, w.scale, rows)
+            el = time.perf_counter() - t0
+            if el >= seconds or n >= n_all:
+                break
+            n = min(n_all, n * max(2, int(seconds / max(el, 1e-3))))
+        keys = (rows % w.T + 1) if causal else np.full(rows.shape, w.T)
+        flop = float(4 * w.D * np.sum(keys))
+    finally:
+        orc.set_num_threads(keep)
+    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": 1,
+            "sample": f"{len(rows)} evenly spaced query rows of {n_all}, {el:.2f} s"}
+
+
 def traffic_for(workload_name):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source; else None."""
@@ -293,7 +330,10 @@ def main():
                "sample": f"the full {w.name} workload (all {w.B * w.H * w.T} query rows), "
                          f"{reps} repeat(s), {sec:.3f} s each",
                "gpu_vs_oracle_max_abs_err": {"O": float(np.max(np.abs(o_gpu - o_ref))),
-                                             "L": float(np.max(np.abs(l_gpu - l_ref)))}}
+                                             "L": float(np.max(np.abs(l_gpu - l_ref)))},
+               "host_cpu": host_cpu_model()}
+        if w.window < 0:
+            cpu["one_thread"] = one_thread_rate(orc, x, w, causal, a.cpu_seconds / 4)
 
     if a.which == "fwd" and w.name == "gpt2" and a.nsplit == 1:
         metric = METRIC

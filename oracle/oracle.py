@@ -90,6 +90,8 @@ def _lib():
         lib.oracle_attn_bwd_masked_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         _LIB = lib
     return _LIB
 
@@ -116,6 +118,11 @@ def _shape(q, k, v):
 
 def num_threads() -> int:
     return int(_lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle uses from now on (OpenMP)."""
+    _lib().oracle_set_num_threads(int(n))
 
 
 def attention(q, k, v, causal: bool, scale: float):

@@ -517,3 +517,12 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads the oracle's loops use from now on (n >= 1). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

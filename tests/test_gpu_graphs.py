@@ -56,6 +56,8 @@ def test_fwd_graph_replays(causal):
 
 
 def test_bwd_and_splitk_and_window_graph_replays():
+    """Forward, backward, key split, window forward and the window backward
+    with its far split, captured in one graph."""
     from exact_attention_91_amd import fa
     B, H, H_kv, T, D = 1, 8, 2, 400, 64
     x = generate(B, H, H_kv, T, D, "bf16", 12002)
@@ -66,13 +68,18 @@ def test_bwd_and_splitk_and_window_graph_replays():
                        device="cuda")
     ws_s = torch.empty((fa.splitk_workspace_bytes(B, H, T, D, 3),), dtype=torch.uint8,
                        device="cuda")
+    # room for the 3 global keys' partial sums: the window backward's far split
+    ws_w = torch.empty((fa.bwd_window_workspace_bytes(B, H, H_kv, T, D, 33, 3, 0),),
+                       dtype=torch.uint8, device="cuda")
 
     def step():
         o, lse = fa.fwd(q, k, v, causal=True, scale=0.125)
         g = fa.bwd(q, k, v, o, lse, do, causal=True, scale=0.125, workspace=ws_b)
         os_, ls_ = fa.fwd_splitk(q, k, v, causal=True, scale=0.125, nsplit=3, workspace=ws_s)
         ow, lw = fa.fwd_window(q, k, v, 33, causal=True, scale=0.125, global_bits=bits)
-        return (o, lse) + tuple(g) + (os_, ls_, ow, lw)
+        gw = fa.bwd_window(q, k, v, ow, lw, do, 33, causal=True, scale=0.125, global_bits=bits,
+                           workspace=ws_w)
+        return (o, lse) + tuple(g) + (os_, ls_, ow, lw) + tuple(gw)
 
     graph, outs = _capture(step)
     for rep in range(3):

@@ -327,3 +327,24 @@ def test_p15_combine_hand_worked(oracle):
     o_big, l_big = oracle.lse_combine(o_parts, l_parts + 800.0)
     np.testing.assert_allclose(o_big, o, rtol=0, atol=1e-11)
     assert abs(l_big[0] - (800.0 + math.log(8.0))) < 1e-11
+
+
+def test_oracle_threads_do_not_change_results(oracle):
+    """The oracle's OpenMP loops run over independent rows: one thread and all
+    threads give bitwise the same outputs (forward, rows, backward)."""
+    x = generate(2, 4, 2, 70, 16, dtype="f32", seed=4242)
+    do = np.random.default_rng(4243).standard_normal(x.q64.shape)
+    keep = oracle.num_threads()
+    runs = []
+    for n in (keep, 1):
+        oracle.set_num_threads(n)
+        try:
+            o, l = oracle.attention(x.q64, x.k64, x.v64, True, 0.3)
+            ro, rl = oracle.attention_rows(x.q64, x.k64, x.v64, True, 0.3, [0, 5, 300, 559])
+            g = oracle.attention_bwd(x.q64, x.k64, x.v64, do, True, 0.3)
+        finally:
+            oracle.set_num_threads(keep)
+        runs.append((o, l, ro, rl) + tuple(g))
+    for a, b in zip(*runs):
+        np.testing.assert_array_equal(a, b)
+    assert oracle.num_threads() == keep
