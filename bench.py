@@ -340,6 +340,20 @@ def main():
     else:
         metric = (f"attention {a.which} TFLOP/s and % of MFMA peak ({w.name} workload"
                   f"{f', nsplit={a.nsplit}' if a.nsplit > 1 else ''})")
+    roofs = None
+    if a.which == "fwd" and w.window < 0 and a.nsplit == 1:
+        # Times the step could not beat on each unit: the dense MFMA peak, HBM
+        # at 8 TB/s over the compulsory bytes (q, k, v, o once, L in fp32), and
+        # one v_exp_f32 per visible score at the measured issue rate of about
+        # 10.5 cycles per wave64 instruction (256 CUs x 4 SIMDs x 64 lanes at
+        # 2.4 GHz / 10.5 = 15.0e12 exp/s).
+        esz = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
+        nbytes = esz * w.B * w.T * w.D * (2 * w.H + 2 * w.H_kv) + 4 * w.B * w.H * w.T
+        exps = w.B * w.H * (w.T * (w.T + 1) / 2 if causal else w.T * w.T)
+        t = {"mfma_us": flops / (peak * 1e12) * 1e6, "hbm_us": nbytes / 8e12 * 1e6,
+             "exp_us": exps / 15.0e12 * 1e6}
+        roofs = dict(t, largest=max(t, key=t.get)[:-3], measured_us=ms * 1e3,
+                     algorithmic_bytes=nbytes, exps=exps)
     out = {
         "metric": metric, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
@@ -355,6 +369,7 @@ def main():
                       if w.window >= 0 else {})},
         "flop_per_step": flops,
         "roofline": roof,
+        "roofs": roofs,
         "cpu_baseline": cpu,
         "cold": cold,
         "device": torch.cuda.get_device_name(0),

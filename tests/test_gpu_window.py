@@ -310,22 +310,23 @@ SPLIT_CASES = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("T,window,glob,heads,D", SPLIT_CASES)
-def test_bwd_window_split(causal, T, window, glob, heads, D):
+def test_bwd_window_split(dtype, causal, T, window, glob, heads, D):
     from exact_attention_91_amd.inputs import generate_dout
     B, H, H_kv = heads
     seed = 12100 + T + D
-    say(f"case bwd window split causal={causal} T={T} window={window} globals={len(glob)} "
-        f"B={B} H={H} H_kv={H_kv} D={D} seed={seed}")
-    x = generate(B, H, H_kv, T, D, "bf16", seed)
-    do, do64 = generate_dout(B, H, T, D, "bf16", seed)
+    say(f"case bwd window split dtype={dtype} causal={causal} T={T} window={window} "
+        f"globals={len(glob)} B={B} H={H} H_kv={H_kv} D={D} seed={seed}")
+    x = generate(B, H, H_kv, T, D, dtype, seed)
+    do, do64 = generate_dout(B, H, T, D, dtype, seed)
     scale = default_scale(D)
     a, u = _bwd_pair(x, do, causal, scale, window, glob)
     _check_split(a, u, T, glob)
     for g, label in ((a, "split"), (u, "unsplit")):
         got = tuple(t.double().cpu().numpy() for t in g)
-        check_bwd(x, do64, "bf16", causal, scale, window, glob, got, label)
+        check_bwd(x, do64, dtype, causal, scale, window, glob, got, label)
 
 
 @pytest.mark.parametrize("head_split", [1, 3, 0])
