@@ -12,6 +12,7 @@ Functions
 attention(q, k, v, causal, scale)        two-pass softmax over the whole row
                                          (C, OpenMP), the plain definition.
 attention_rows(..., rows)                the same for selected flat rows
+attention_bwd_dq_rows(..., rows)         dQ of selected flat rows (backward)
                                          (b*H + h)*T + i.
 attention_online(..., chunk)             the online-softmax recurrence over key
                                          chunks (C), used to show it reaches the
@@ -88,6 +89,10 @@ def _lib():
         lib.oracle_attn_bwd_masked_f64.argtypes = (common + [_DP, _DP, _DP, _DP] + shape +
                                                    [ctypes.c_int, ctypes.c_void_p])
         lib.oracle_attn_bwd_masked_f64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_dq_rows_f64.argtypes = (
+            [_DP, _DP, _DP, _DP, ctypes.POINTER(ctypes.c_int64), ctypes.c_longlong, _DP] +
+            [ctypes.c_int] * 5 + [ctypes.c_int, ctypes.c_double])
+        lib.oracle_attn_bwd_dq_rows_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -152,6 +157,25 @@ def attention_rows(q, k, v, causal: bool, scale: float, rows):
     if rc:
         raise RuntimeError(f"oracle_attn_rows_f64 failed ({rc})")
     return o, lse
+
+
+def attention_bwd_dq_rows(q, k, v, dout, causal: bool, scale: float, rows):
+    """dQ of selected rows (flat ids (b*H + h)*T + i), plain or causal mask.
+    Returns dq [n, D]."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, H_kv, T, D = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.shape[0]
+    dq = np.empty((n, D), np.float64)
+    rc = _lib().oracle_attn_bwd_dq_rows_f64(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n, _ptr(dq),
+        B, H, H_kv, T, D, int(bool(causal)), float(scale))
+    if rc:
+        raise RuntimeError(f"oracle_attn_bwd_dq_rows_f64 failed ({rc})")
+    return dq
 
 
 def attention_online(q, k, v, causal: bool, scale: float, chunk: int):

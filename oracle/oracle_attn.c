@@ -510,6 +510,76 @@ int oracle_attn_bwd_masked_f64(const double *q, const double *k, const double *v
                     is_global);
 }
 
+/* dQ of selected rows, flat ids (b*H + h)*T + i, for the plain (maskless or
+ * causal) attention: the row's forward recomputed (scores, max, normaliser,
+ * weights P), dP_j = dO_i . v_j, Delta_i = sum_j P_j dP_j, and
+ * dQ_i = scale * sum_j P_j (dP_j - Delta_i) k_j, keys in ascending order --
+ * the dQ part of the full backward above, one row at a time. */
+int oracle_attn_bwd_dq_rows_f64(const double *q, const double *k, const double *v,
+                                const double *dout, const int64_t *rows, long long nrows,
+                                double *dq_rows, int B, int H, int H_kv, int T, int D,
+                                int causal, double scale) {
+    if (bad_args(B, H, H_kv, T, D)) return -1;
+    const long long total = (long long)B * H * T;
+    for (long long r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= total) return -3;
+    const int group = H / H_kv;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)T);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)T);
+        if (!p || !dp) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (long long r = 0; r < nrows; ++r) {
+                const long long id = rows[r];
+                const int i = (int)(id % T);
+                const int h = (int)((id / T) % H);
+                const int b = (int)(id / ((long long)T * H));
+                const int g = h / group;
+                const int n = causal ? i + 1 : T;   /* visible keys 0 .. n-1 */
+                const double *qi = q + qidx(b, i, h, H, T, D);
+                const double *doi = dout + qidx(b, i, h, H, T, D);
+                double *dqi = dq_rows + (size_t)r * D;
+                for (int d = 0; d < D; ++d) dqi[d] = 0.0;
+                double m = -INFINITY;
+                for (int j = 0; j < n; ++j) {
+                    const double *kj = k + qidx(b, j, g, H_kv, T, D);
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+                    p[j] = scale * dot;
+                    if (p[j] > m) m = p[j];
+                }
+                double z = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    p[j] = exp(p[j] - m);
+                    z += p[j];
+                }
+                for (int j = 0; j < n; ++j) p[j] /= z;
+                double rowdot = 0.0;
+                for (int j = 0; j < n; ++j) {
+                    const double *vj = v + qidx(b, j, g, H_kv, T, D);
+                    double dot = 0.0;
+                    for (int d = 0; d < D; ++d) dot += doi[d] * vj[d];
+                    dp[j] = dot;
+                    rowdot += p[j] * dot;
+                }
+                for (int j = 0; j < n; ++j) {
+                    const double ds = p[j] * (dp[j] - rowdot);
+                    const double *kj = k + qidx(b, j, g, H_kv, T, D);
+                    for (int d = 0; d < D; ++d) dqi[d] += scale * ds * kj[d];
+                }
+            }
+        }
+        free(p);
+        free(dp);
+    }
+    return fail ? -2 : 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

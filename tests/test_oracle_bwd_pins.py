@@ -206,3 +206,22 @@ def test_bwd_bad_shapes_rejected(oracle):
         oracle.attention_bwd(q, k, k, q, False, 1.0)
     with pytest.raises(ValueError):
         oracle.attention_bwd(q, q, q, np.zeros((1, 4, 3, 4)), False, 1.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_match_the_full_backward(oracle, causal):
+    """oracle.attention_bwd_dq_rows on selected rows equals the dQ rows of the
+    pinned full backward (same steps, one row at a time), grouped heads and
+    edge rows included."""
+    from exact_attention_91_amd.inputs import generate
+    B, H, H_kv, T, D = 2, 6, 2, 45, 16
+    x = generate(B, H, H_kv, T, D, dtype="f32", seed=5151, qk_sigma=2.0)
+    do = np.random.default_rng(5152).standard_normal(x.q64.shape)
+    dq, _, _ = oracle.attention_bwd(x.q64, x.k64, x.v64, do, causal, 0.35)
+    rows = [0, T - 1, 17, H * T + 3, (B * H - 1) * T + T - 1, (B * H) * T - T]
+    got = oracle.attention_bwd_dq_rows(x.q64, x.k64, x.v64, do, causal, 0.35, rows)
+    for r, g in zip(rows, got):
+        b, h, i = r // (H * T), (r // T) % H, r % T
+        np.testing.assert_allclose(g, dq[b, i, h], rtol=0, atol=1e-13)
+    with pytest.raises(RuntimeError):
+        oracle.attention_bwd_dq_rows(x.q64, x.k64, x.v64, do, causal, 0.35, [B * H * T])
