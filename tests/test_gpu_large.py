@@ -130,3 +130,59 @@ def test_bwd_tensors_past_2e31_elements():
         say(f"  batch {b} alone: o, lse, dq, dk, dv bitwise equal")
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+def test_window_tensors_past_2e31_elements():
+    """Window forward and backward (window 64, causal, global tokens, far split)
+    on [272, 8192, 16, 64] q: the last batch run alone is bitwise the large
+    run's, and that batch is compared in full with the masked oracle (O to
+    2e-2, L to 1e-3; gradients to 2e-2 x max(1, max|ref|))."""
+    from exact_attention_91_amd import fa
+    from oracle import oracle as orc
+    B, T, H, H_kv, D = 272, 8192, 16, 1, 64
+    assert B * T * H * D > 2 ** 31
+    window, glob = 64, (0, 1, 4000, 8191)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4343)
+    q = _randn_bf16((B, T, H, D), g)
+    k = _randn_bf16((B, T, H_kv, D), g)
+    v = _randn_bf16((B, T, H_kv, D), g)
+    do = _randn_bf16((B, T, H, D), g)
+    scale = 0.125
+    say(f"case large window B={B} T={T} H={H} D={D} window={window} globals={glob}")
+    bits = fa.window_bitmap(glob, T, q.device)
+
+    def run(q_, k_, v_, do_):
+        b_ = q_.shape[0]
+        o_, l_ = fa.fwd_window(q_, k_, v_, window, causal=True, scale=scale, global_bits=bits)
+        ws = torch.empty((fa.bwd_window_workspace_bytes(b_, H, H_kv, T, D, window, len(glob),
+                                                        1),), dtype=torch.uint8, device="cuda")
+        g_ = fa.bwd_window(q_, k_, v_, o_, l_, do_, window, causal=True, scale=scale,
+                           global_bits=bits, head_split=1, workspace=ws)
+        return (o_, l_) + tuple(g_)
+
+    big = run(q, k, v, do)
+    torch.cuda.synchronize()
+    b = B - 1
+    small = run(*(t[b:b + 1].contiguous() for t in (q, k, v, do)))
+    torch.cuda.synchronize()
+    for name, x, y in zip(("o", "lse", "dq", "dk", "dv"), big, small):
+        assert torch.equal(x[b:b + 1], y), name
+    say("  last batch alone: bitwise equal")
+
+    def f64(t):
+        return t.to(torch.float64).cpu().numpy()
+
+    q1, k1, v1, d1 = (f64(t[b:b + 1]) for t in (q, k, v, do))
+    ro, rl = orc.attention_masked(q1, k1, v1, True, scale, window, glob)
+    eo, el = float(np.max(np.abs(f64(small[0]) - ro))), float(np.max(np.abs(f64(small[1]) - rl)))
+    say(f"  oracle: |dO|={eo:.2e} |dL|={el:.2e}")
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+    ref = orc.attention_bwd_masked(q1, k1, v1, d1, True, scale, window, glob)
+    for name, got, r in zip(("dq", "dk", "dv"), small[2:], ref):
+        err = float(np.max(np.abs(f64(got) - r)))
+        tol = 2e-2 * max(1.0, float(np.max(np.abs(r))))
+        say(f"  oracle {name}: |err|={err:.2e} (tol {tol:.2e})")
+        assert err <= tol, (name, err, tol)
+    del q, k, v, do, big, small
+    torch.cuda.empty_cache()
