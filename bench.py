@@ -135,7 +135,7 @@ def main():
     import torch
 
     from exact_attention_91_amd import fa
-    from exact_attention_91_amd.inputs import WORKLOADS, generate_workload
+    from exact_attention_91_amd.inputs import WORKLOADS, generate_workload, torch_dtype
 
     w = WORKLOADS[a.workload]
     causal = True if True in w.causal else False
@@ -264,10 +264,12 @@ def main():
                 "ms_p90": float(np.percentile(times, 90))}
 
     peak = PEAK[w.dtype]
+    groups = fa.key_groups(w.B, w.H, w.T, w.D, torch_dtype(w.dtype))
     roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
             "frac": tflops / peak, "traffic": traffic_for(w.name),
             "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
-                       f"{str(a.nsplit > 1).lower()}, false, PAIR> (PAIR as the library picks)"
+                       f"{str(a.nsplit > 1).lower()}, false, "
+                       f"{str(a.nsplit == 1 and groups == 2).lower()}>"
                        if w.dtype in _ELEM else
                        f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
     if w.window >= 0 and a.which == "fwd":

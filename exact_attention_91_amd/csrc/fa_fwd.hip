@@ -1,5 +1,6 @@
 // fa_fwd.hip -- exact, IO-aware, tiled attention forward for MI355X (gfx950):
-// the plain forward (fa_fwd, fa_fwd_strided), its key-split form with the
+// the plain forward (fa_fwd, fa_fwd_strided, and fa_fwd_key_groups, which
+// reports the kernel variant they pick), its key-split form with the
 // logsumexp combine (fa_fwd_splitk, fa_lse_combine), the sliding-window /
 // local-global forward and its token bitmap (fa_fwd_window, fa_window_bitmap),
 // and their C ABI (include/fa.h).
@@ -44,8 +45,14 @@
 //  * Causal: key tiles past the query tile are never loaded; a wave skips the
 //    math of tiles wholly in its future; only tiles that touch the diagonal or
 //    the ragged end T are masked element-wise. Query tiles are issued
-//    heaviest-first; for long rows with every work-group resident, heavy and
-//    light tiles are paired in one work-group (the PAIR instantiation).
+//    heaviest-first.
+//  * Small grids (few query tiles per CU, or long rows with every work-group
+//    resident): the G2 instantiation runs 8 waves per work-group in two groups
+//    of 4 that take the first and second half of the query tile's key tiles,
+//    each with its own LDS buffers, and merges the second group's partial rows
+//    into the first's through LDS with the same online-softmax update. Twice
+//    the waves per query tile, so MFMA and softmax work of different waves
+//    overlap where one wave per SIMD would run them back to back.
 //  * Variants of the same 16-bit kernel (template flags): SPLIT runs a range
 //    of each query tile's key tiles and writes an fp32 partial result that
 //    fa_lse_combine_kernel merges by the logsumexps (the online-softmax update
@@ -87,11 +94,9 @@ struct FwdParams {
     // set (gbits NULL: no global tokens); causal still applies.
     int window;
     const unsigned long long *gbits;
-    // Paired causal mode: work-group t runs query tiles nq-1-t, then t, so every
-    // work-group has the same number of key tiles (used when all work-groups
-    // are resident at once and rows are long, where the heaviest tile would
-    // otherwise set the launch's length).
-    int pair;
+    // 2: two 4-wave groups per work-group split each query tile's key tiles
+    // (the G2 kernel); 1: one group.
+    int groups;
 };
 
 template <bool B>
@@ -127,8 +132,8 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 // layout of fa_device.h: K is read as rows (kswz), V transposed for the V^T
 // operand of P.V (vswz).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW, bool PAIR>
-__global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
+template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW, bool G2>
+__global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
     typedef typename H16::v8 e8_t;
@@ -138,40 +143,30 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
     constexpr int ND = (D + 31) / 32;       // 32-row blocks of O^T
     constexpr int NV = D >= 32 ? D / 32 : 1;  // V^T address variants (one per block)
 
+    static_assert(!G2 || (!SPLIT && !WINDOW && D >= 32), "G2: plain forward, D >= 32");
     // Two K/V buffers as four distinct LDS variables: the accesses of each loop
     // step name their buffers statically, so the compiler knows the copies into
     // one buffer never alias the operand reads of the other and does not make
-    // the reads wait for the copies.
-    __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[L::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[L::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[L::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[L::TILEB];
+    // the reads wait for the copies. With G2 each variable holds both groups'
+    // buffers, group g at offset g * TILEB.
+    constexpr int NG = G2 ? 2 : 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds0_[NG * L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds0_[NG * L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds1_[NG * L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds1_[NG * L::TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = G2 ? (wave8 >> 2) : 0;          // key-range group
+    const int wave = G2 ? (wave8 & 3) : wave8;      // wave within the group
+    unsigned char *const k_lds0 = k_lds0_ + grp * L::TILEB;
+    unsigned char *const v_lds0 = v_lds0_ + grp * L::TILEB;
+    unsigned char *const k_lds1 = k_lds1_ + grp * L::TILEB;
+    unsigned char *const v_lds1 = v_lds1_ + grp * L::TILEB;
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
-    constexpr bool paired = PAIR && CAUSAL && !SPLIT && !WINDOW;
-    for (int pass = 0; pass < (paired ? 2 : 1); ++pass) {
-    Unit u;
-    if (paired) {
-        const int id = blockIdx.x;
-        const int t = id / p.nbh;
-        const int bh = id - t * p.nbh;
-        u.b = bh / p.H;
-        u.h = bh - u.b * p.H;
-        u.g = u.h / p.group;
-        u.s = 0;
-        const int qt = pass == 0 ? p.nq - 1 - t : t;
-        if (pass == 1 && qt == p.nq - 1 - t) break;   // odd count: the middle tile is done
-        u.q0 = qt * kBQ;
-        // every wave starts each pass together (before the second pass this is
-        // also what keeps its first tile's staging off buffers still being read)
-        __syncthreads();
-    } else {
-        u = unit_of(p);
-    }
+    const Unit u = unit_of(p);
     const int wq0 = u.q0 + wave * 32;       // first query row of this wave
     const int qrow = wq0 + col;             // this lane's query row
 
@@ -198,9 +193,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
 
     const int kend = CAUSAL ? min(T, u.q0 + kBQ) : T;
     const int nkt = (kend + BK - 1) / BK;
-    // Key tiles of this work-group: all of them, or split u.s's share.
-    const int jbeg = SPLIT ? u.s * nkt / p.nsplit : 0;
-    const int jend = SPLIT ? (u.s + 1) * nkt / p.nsplit : nkt;
+    // Key tiles of this work-group: all of them, or split u.s's share; with G2,
+    // group 0 takes the first ghalf of them and group 1 the rest.
+    const int ghalf = (nkt + 1) / 2;
+    const int jbeg = SPLIT ? u.s * nkt / p.nsplit : (G2 && grp ? ghalf : 0);
+    const int jend = SPLIT ? (u.s + 1) * nkt / p.nsplit : (G2 && !grp ? ghalf : nkt);
     // Window mode: the key tiles visited are those meeting the band
     // [q0 - window, q_last + window] of this query tile (tiles blo..bhi) and
     // those holding a global token; all others are never loaded.
@@ -379,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
         if (jn < jend)
             stage_tile<D>(kbase, vbase, ks1, vs1, T, jn * BK, wave, koff, voff, kn, vn);
         const int key0 = j * BK;
-        bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31) && (!G2 || j < jend);
         bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
         if (WINDOW) {
             // the band of this wave's 32 rows: [wq0 - window, wq0 + 31 + window]
@@ -409,6 +406,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
             j = jnn;
             gj = gnn;
         }
+    } else if (G2) {
+        // Both groups take ghalf steps, one barrier each; group 1's last step is
+        // idle when nkt is odd (no staging, no math).
+        if (jbeg < jend)
+            stage_tile<D>(kbase, vbase, ks1, vs1, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
+        for (int i = 0; i < ghalf; i += 2) {
+            step(jbeg + i, 0ull, jbeg + i + 1, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (i + 1 < ghalf)
+                step(jbeg + i + 1, 0ull, jbeg + i + 2, k_lds1, v_lds1, k_lds0, v_lds0);
+        }
     } else {
         if (jbeg < jend)
             stage_tile<D>(kbase, vbase, ks1, vs1, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
@@ -418,9 +425,47 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
         }
     }
 
-    if (!wave_live) continue;
+    if (G2) {
+        // Merge: wave w + 4 (group 1) leaves its O^T accumulators, running max and
+        // row sum in LDS, lane-major; wave w (group 0, the same 32 rows) folds them
+        // in with the online-softmax update m = max(m0, m1), x = x0 2^(m0 - m) +
+        // x1 2^(m1 - m). A group that saw no key of a row holds the floor max and
+        // zero sums, so its factor is 0. Every wave takes both barriers; after the
+        // first, all K/V reads are done and the buffers are free.
+        static_assert(!G2 || (ND * 16 + 2) * 64 * 4 <= NG * L::TILEB, "merge area");
+        __syncthreads();
+        float *mb = (float *)(wave == 0 ? k_lds0_ : wave == 1 ? v_lds0_
+                              : wave == 2 ? k_lds1_ : v_lds1_);
+        const float lrow = half_swap_sum(lsum);
+        if (grp == 1 && wave_live) {
+#pragma unroll
+            for (int n = 0; n < ND; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mb[(n * 16 + r) * 64 + lane] = oacc[n][r];
+            mb[ND * 16 * 64 + lane] = mref;
+            mb[(ND * 16 + 1) * 64 + lane] = lrow;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        if (wave_live) {
+            const float m1 = mb[ND * 16 * 64 + lane];
+            const float l1 = mb[(ND * 16 + 1) * 64 + lane];
+            const float m = fmaxf(mref, m1);
+            const float a0 = fast_exp2(mref - m), a1 = fast_exp2(m1 - m);
+#pragma unroll
+            for (int n = 0; n < ND; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    oacc[n][r] = oacc[n][r] * a0 + mb[(n * 16 + r) * 64 + lane] * a1;
+            // the merged row sum, held by the half-0 lane (the epilogue adds halves)
+            lsum = half ? 0.f : lrow * a0 + l1 * a1;
+            mref = m;
+        }
+    }
+
+    if (!wave_live) return;
     const float lt = half_swap_sum(lsum);
-    if (qrow >= T) continue;
+    if (qrow >= T) return;
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
     const float lse_row = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     if (SPLIT) {
@@ -440,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
                 }
             }
         if (half == 0) p.lpart[row] = lse_row;
-        continue;
+        return;
     }
     unsigned short *orow = (unsigned short *)p.o + u.b * p.os[0] + (long long)qrow * p.os[1] +
                            u.h * p.os[2];
@@ -458,7 +503,6 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_half_kernel(FwdParams p) {
             }
         }
     if (half == 0) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
-    }   // pass
 }
 // ---------------------------------------------------------------------------
 // fp32 kernel: fp32 operands on fp32 MFMA (32x32x2), 32-key tiles. Weights stay
@@ -741,13 +785,13 @@ bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 template <int D, bool CAUSAL, bool SPLIT, bool WINDOW>
 void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
-    constexpr bool CAN_PAIR = CAUSAL && !SPLIT && !WINDOW;
-    if (CAN_PAIR && p.pair && dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_PAIR>), grid,
-                           dim3(kThreads), 0, stream, p);
-    else if (CAN_PAIR && p.pair && dtype == FA_DTYPE_F16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_PAIR>), grid,
-                           dim3(kThreads), 0, stream, p);
+    constexpr bool CAN_G2 = D >= 64 && !SPLIT && !WINDOW;
+    if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_BF16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid,
+                           dim3(2 * kThreads), 0, stream, p);
+    else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_F16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid,
+                           dim3(2 * kThreads), 0, stream, p);
     else if (dtype == FA_DTYPE_BF16)
         hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>), grid,
                            dim3(kThreads), 0, stream, p);
@@ -834,7 +878,7 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
     p.opart = p.lpart = nullptr;
     p.window = 0;
     p.gbits = nullptr;
-    p.pair = 0;
+    p.groups = 1;
     return FA_OK;
 }
 
@@ -887,7 +931,26 @@ int launch_combine(const float *opart, const float *lpart, int n, int B, int H, 
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// Two key-range groups per query tile (the G2 kernel) when the grid is small:
+// at most a quarter of the 4-wave work-group slots (256 CUs x 4, or x 2 at
+// D = 128 by registers), or rows of 2048 keys or more with every work-group
+// resident at once. Elsewhere the single-group kernel is faster.
+int key_groups(long long units, int T, int D, int dtype) {
+    const long long slots = kNumCU * (D >= 128 ? 2 : 4);
+    return dtype != FA_DTYPE_F32 && D >= 64 &&
+                   (4 * units <= slots || (T >= 2048 && units <= slots))
+               ? 2
+               : 1;
+}
+
 }  // namespace
+
+extern "C" int fa_fwd_key_groups(int B, int H, int T, int D, int dtype) {
+    if (B < 0 || H < 1 || T < 0 || (D != 16 && D != 32 && D != 64 && D != 128) ||
+        (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16))
+        return -1;
+    return key_groups((long long)B * H * ((T + kBQ - 1) / kBQ), T, D, dtype);
+}
 
 extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
                               int B, int H, int H_kv, int T, int D, int causal, float scale,
@@ -899,14 +962,9 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     const int st = prepare(q, k, v, o, lse, B, H, H_kv, T, D, scale, dtype, q_strides, k_strides,
                            v_strides, o_strides, &p, &empty);
     if (st != FA_OK || empty) return st;
-    // Pair causal query tiles when rows are long and every work-group is
-    // resident at once (work-group slots: 256 CUs x 4, or x 2 at D = 128 by
-    // registers), so the heaviest tile would set the launch's length.
     const long long units = (long long)p.nbh * p.nq;
-    const long long slots = kNumCU * (D >= 128 ? 2 : 4);
-    if (causal && dtype != FA_DTYPE_F32 && T >= 4096 && units <= slots && 2 * units >= slots)
-        p.pair = 1;
-    const dim3 grid((unsigned)(p.pair ? (long long)p.nbh * ((p.nq + 1) / 2) : units));
+    p.groups = key_groups(units, T, D, dtype);
+    const dim3 grid((unsigned)units);
     hipStream_t s = (hipStream_t)stream;
     if (causal)
         launch_d<true, false>(p, D, dtype, grid, s);

@@ -43,6 +43,8 @@ def _lib():
         lib.fa_fwd_strided.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
                                        [ctypes.c_float, _I] + [_LLP] * 4 + [_VP])
         lib.fa_fwd_strided.restype = _I
+        lib.fa_fwd_key_groups.argtypes = [_I] * 5
+        lib.fa_fwd_key_groups.restype = _I
         lib.fa_fwd_splitk.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
                                       [ctypes.c_float, _I, _I, _VP, ctypes.c_longlong, _VP])
         lib.fa_fwd_splitk.restype = _I
@@ -76,6 +78,14 @@ def _lib():
 
 def version() -> int:
     return int(_lib().fa_version())
+
+
+def key_groups(B: int, H: int, T: int, D: int, dtype) -> int:
+    """Key-range groups per query tile that fwd() uses for these sizes (1 or 2;
+    see fa_fwd_key_groups in fa.h). dtype: a torch dtype."""
+    code = {torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_F16,
+            torch.float32: FA_DTYPE_F32}[dtype]
+    return int(_lib().fa_fwd_key_groups(B, H, T, D, code))
 
 
 def status_str(code: int) -> str:

@@ -108,6 +108,20 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
                    const long long o_strides[3], void *stream);
 
 /*
+ * Key-range groups per query tile that fa_fwd and fa_fwd_strided use for these
+ * sizes. 2 for bf16/fp16 with D >= 64 when the launch is small: its
+ * B * H * ceil(T/128) query tiles are at most a quarter of the 4-wave
+ * work-groups the GPU holds at once (1024 at D = 64, 512 at D = 128), or at
+ * most all of them with T >= 2048. Otherwise 1. With 2, the work-group of a
+ * query tile runs two groups of four waves over the first and the second half
+ * of its key tiles and folds the second group's rows into the first's by the
+ * online-softmax update of "Softmax 的在線計算" (yelogs.com Flash
+ * Attention2-in-Triton article); the result differs from the one-group order
+ * only in rounding. Host-only (no HIP call); -1 for invalid sizes or dtype.
+ */
+int fa_fwd_key_groups(int B, int H, int T, int D, int dtype);
+
+/*
  * Split-K forward (the same result as fa_fwd up to rounding, for bf16 and
  * fp16): the key tiles of every 128-row query tile are divided into nsplit
  * contiguous ranges, each handled by its own work-group, so shapes with few

@@ -39,7 +39,7 @@ DT = _enum_values("fa_dtype_t")
 
 def test_header_declares_the_entry_points():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_window", "fa_bwd_window_workspace_bytes",
-                                     "fa_bwd_workspace_bytes", "fa_fwd",
+                                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_key_groups",
                                      "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
                                      "fa_fwd_strided", "fa_fwd_window", "fa_lse_combine",
                                      "fa_status_str", "fa_version", "fa_window_bitmap",
@@ -397,3 +397,35 @@ def test_bwd_window_rejects(lib, kw, code):
                            a["scale"], a["dtype"], a["window"], a["bits"], a["hsplit"], a["ws"],
                            a["ws_bytes"], None)
     assert rc == ST[code]
+
+
+@pytest.mark.parametrize("B,H,T,D,dtype,expect", [
+    (16, 12, 1024, 64, "BF16", 1),    # GPT-2 layer: 1536 query tiles
+    (8, 1, 8192, 128, "BF16", 2),     # long rows, 512 tiles = every work-group resident
+    (8, 12, 4096, 64, "BF16", 1),     # MQA workload: 3072 tiles
+    (64, 1, 1024, 64, "BF16", 1),     # 512 tiles of short rows
+    (64, 1, 1024, 128, "F16", 1),     # 512 tiles of short rows at D = 128
+    (2, 12, 1024, 64, "BF16", 2),     # 192 tiles: under a quarter of 1024
+    (32, 1, 1024, 64, "F16", 2),      # 256 tiles: exactly a quarter
+    (33, 1, 1024, 64, "BF16", 1),     # 264 tiles, short rows
+    (2, 12, 4096, 64, "BF16", 2),     # 768 tiles of 4096-key rows
+    (4, 16, 4096, 64, "BF16", 1),     # 2048 tiles: more than the GPU holds
+    (1, 128, 128, 128, "BF16", 2),    # 128 tiles: a quarter of 512
+    (1, 129, 128, 128, "BF16", 1),
+    (1, 1, 2048, 128, "BF16", 2),
+    (8, 4, 4096, 128, "BF16", 1),     # 1024 tiles at D = 128
+    (1, 1, 1, 64, "BF16", 2),
+    (1, 1, 300, 32, "BF16", 1),       # D < 64: one group
+    (1, 1, 300, 16, "F16", 1),
+    (1, 1, 8192, 128, "F32", 1),      # the fp32 kernel has one group
+    (0, 4, 100, 64, "BF16", 2),       # empty launch: nothing runs
+])
+def test_key_groups_rule(lib, B, H, T, D, dtype, expect):
+    """The launch-shape rule fa_fwd_key_groups reports (pure host code)."""
+    assert lib.fa_fwd_key_groups(B, H, T, D, DT["FA_DTYPE_" + dtype]) == expect
+
+
+@pytest.mark.parametrize("args", [(-1, 1, 10, 64, 1), (1, 0, 10, 64, 1), (1, 1, -1, 64, 1),
+                                  (1, 1, 10, 48, 1), (1, 1, 10, 64, 3), (1, 1, 10, 64, -1)])
+def test_key_groups_invalid(lib, args):
+    assert lib.fa_fwd_key_groups(*args) == -1

@@ -129,12 +129,33 @@ def test_workload_mqa_sampled_rows():
 
 
 @pytest.mark.parametrize("B,T,D", [(5, 8000, 128), (4, 8192, 128), (16, 4200, 64)])
-def test_paired_query_tiles(B, T, D):
-    """Long causal rows with every work-group resident at once: the library
-    runs query tiles in heavy/light pairs (nq-1-t, then t). Odd tile counts
-    (T = 8000 and 4200) leave the middle tile unpaired. Compared in full."""
-    say(f"case paired B={B} T={T} D={D}")
+def test_two_group_long_rows(B, T, D):
+    """Long causal rows with every work-group resident at once: each query
+    tile's keys are split between two wave groups and merged in LDS. Odd
+    key-tile counts (T = 8000 and 4200 end mid-tile) give group 1 one step
+    less. Compared in full."""
+    from exact_attention_91_amd import fa
+    assert fa.key_groups(B, 1, T, D, torch.bfloat16) == 2
+    say(f"case two groups B={B} T={T} D={D}")
     x = generate(B, 1, 1, T, D, "bf16", 9700 + T + D)
     scale = default_scale(D)
     o, lse = run_gpu(x, True, scale)
-    check_full(x, "bf16", True, scale, o, lse, "paired")
+    check_full(x, "bf16", True, scale, o, lse, "two groups")
+
+
+# Sizes with more query tiles than a quarter of the resident work-groups and
+# short rows: the one-group kernel at D = 64 and 128, on ragged and tiny T.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [1, 63, 65, 129, 300])
+def test_one_group_ragged(dtype, D, causal, T):
+    from exact_attention_91_amd import fa
+    B, H = 16, 17
+    assert fa.key_groups(B, H, T, D, torch.bfloat16) == 1
+    seed = 9600 + T * 10 + D
+    say(f"case one group dtype={dtype} D={D} causal={causal} B={B} H={H} T={T} seed={seed}")
+    x = generate(B, H, 1, T, D, dtype, seed)
+    scale = default_scale(D)
+    o, lse = run_gpu(x, causal, scale)
+    check_full(x, dtype, causal, scale, o, lse, "one group")

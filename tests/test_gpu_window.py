@@ -81,9 +81,11 @@ def test_window_token_list_forms():
 @pytest.mark.parametrize("causal", [False, True])
 def test_window_covering_everything_is_fwd_bitwise(causal):
     """window >= T - 1 without global tokens visits every tile with the same
-    arithmetic as fa_fwd: bitwise the same output."""
+    arithmetic as fa_fwd's one-group kernel: bitwise the same output (sizes
+    for which fa_fwd picks that kernel)."""
     from exact_attention_91_amd import fa
-    x = generate(2, 4, 2, 500, 64, "bf16", 9901)
+    assert fa.key_groups(5, 16, 500, 64, torch.bfloat16) == 1
+    x = generate(5, 16, 2, 500, 64, "bf16", 9901)
     q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
     o1, l1 = fa.fwd(q, k, v, causal=causal, scale=0.125)
     o2, l2 = fa.fwd_window(q, k, v, 499, None, causal=causal, scale=0.125)
