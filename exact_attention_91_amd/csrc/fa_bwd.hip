@@ -26,7 +26,10 @@
 //    and L2 = L log2(e) for them (stored in the workspace for the dK/dV
 //    kernel), streams K and V tiles, computes S^T = K Q^T and dP^T = V dO^T,
 //    and accumulates dQ^T += K^T dS^T with K^T from transposing reads of the
-//    K tile.
+//    K tile. At D = 128 on small grids (the forward's two-group rule) its
+//    8-wave G2 instantiation splits each query tile's key tiles between two
+//    groups of 4 waves and adds the second group's dQ^T into the first's
+//    through LDS.
 //  * fa_bwd_reduce_kernel (head split only): adds the fp32 parts in order.
 //  * Window mode (fa_bwd_window): both main kernels visit only the tiles that
 //    meet a tile's band or hold a global token. A key tile holding a global
@@ -58,6 +61,9 @@ struct BwdParams {
     int B, H, H_kv, T;
     int group;              // H / H_kv
     int nblk;               // 128-row tiles per sequence
+    // 2: the dQ kernel splits each query tile's key tiles between two groups
+    // of 4 waves (8-wave work-groups, D = 128, plain masks); 1: one group.
+    int dq_groups;
     float c;                // scale * log2(e) (signed)
     float scale;
     // Head split of the dK/dV kernel: work-group (key tile, b, g, part s)
@@ -563,8 +569,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
 // L2 and Delta are per-lane scalars; register r of block kb is key
 // key0 + 32 kb + 8(r/4) + 4half + r%4.
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool WINDOW>
-__global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
+template <typename E, int D, bool CAUSAL, bool WINDOW, bool G2 = false>
+__global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_bwd_dq_kernel(BwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
     typedef typename H16::v8 e8_t;
@@ -574,15 +580,25 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
     constexpr int ND = (D + 31) / 32;
     constexpr int NV = D >= 32 ? D / 32 : 1;
     constexpr int NI = (L::NLOAD + 3) / 4;
+    static_assert(!G2 || (!WINDOW && D >= 32), "G2: plain masks, D >= 32");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char k_lds0[L::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char v_lds0[L::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char k_lds1[L::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char v_lds1[L::TILEB];
+    // With G2 (8 waves, two key-range groups of 4) each variable holds both
+    // groups' buffers, group g at offset g * TILEB.
+    constexpr int NG = G2 ? 2 : 1;
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds0_[NG * L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds0_[NG * L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_lds1_[NG * L::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_lds1_[NG * L::TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = G2 ? (wave8 >> 2) : 0;
+    const int wave = G2 ? (wave8 & 3) : wave8;
+    unsigned char *const k_lds0 = k_lds0_ + grp * L::TILEB;
+    unsigned char *const v_lds0 = v_lds0_ + grp * L::TILEB;
+    unsigned char *const k_lds1 = k_lds1_ + grp * L::TILEB;
+    unsigned char *const v_lds1 = v_lds1_ + grp * L::TILEB;
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
     const int nbh = p.B * p.H;
@@ -634,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
         if (qrow < T) {
             const long long r = ((long long)b * p.H + h) * T + qrow;
             l2 = p.lse[r] * kLog2e;
-            if (half == 0) {
+            if (half == 0 && grp == 0) {
                 p.delta[r] = dl;
                 p.l2[r] = l2;
             }
@@ -643,6 +659,10 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
 
     const int kend = CAUSAL ? min(T, q0 + kBlk) : T;
     const int nkt = (kend + BK - 1) / BK;
+    // G2: group 0 takes key tiles [0, ghalf), group 1 [ghalf, nkt).
+    const int ghalf = (nkt + 1) / 2;
+    const int jbeg = G2 && grp ? ghalf : 0;
+    const int jend = G2 && !grp ? ghalf : nkt;
     // Window mode: key tiles meeting the band of this query tile (blo..bhi)
     // or holding a global token; the others are never loaded.
     int blo = 0, bhi = nkt - 1;
@@ -777,10 +797,10 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
         __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (jn < nkt)
+        if (jn < jend)
             stage_tile<D>(kbase, vbase, krs, krs, T, jn * BK, wave, koff, voff, kn, vn);
         const int key0 = j * BK;
-        bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31);
+        bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31) && (!G2 || j < jend);
         bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
         if (WINDOW) {
             const long long wlo = (long long)wq0 - p.window, whi = (long long)wq0 + 31 + p.window;
@@ -792,7 +812,38 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dq_kernel(BwdParams p) {
         }
         if (active) tile(need_mask, j, kt, vt, gb);
     };
-    {
+    if (G2) {
+        // both groups take ghalf steps, one barrier each; group 1's last step is
+        // idle when nkt is odd
+        if (jbeg < jend)
+            stage_tile<D>(kbase, vbase, krs, krs, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
+        for (int i = 0; i < ghalf; i += 2) {
+            step(jbeg + i, 0ull, jbeg + i + 1, k_lds0, v_lds0, k_lds1, v_lds1);
+            if (i + 1 < ghalf)
+                step(jbeg + i + 1, 0ull, jbeg + i + 2, k_lds1, v_lds1, k_lds0, v_lds0);
+        }
+        // wave w + 4 leaves its dQ^T accumulators in LDS, lane-major; wave w
+        // (the same 32 rows) adds them after its own. Every wave takes both
+        // barriers; after the first, all K/V reads are done.
+        static_assert(!G2 || ND * 16 * 64 * 4 <= NG * L::TILEB, "merge area");
+        __syncthreads();
+        float *mb = (float *)(wave == 0 ? k_lds0_ : wave == 1 ? v_lds0_
+                              : wave == 2 ? k_lds1_ : v_lds1_);
+        if (grp == 1 && wave_live) {
+#pragma unroll
+            for (int n = 0; n < ND; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mb[(n * 16 + r) * 64 + lane] = dqacc[n][r];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        if (wave_live) {
+#pragma unroll
+            for (int n = 0; n < ND; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dqacc[n][r] += mb[(n * 16 + r) * 64 + lane];
+        }
+    } else {
         int j = next_tile(-1);
         unsigned long long gj = tile_bits(j);
         if (j < nkt)
@@ -956,8 +1007,15 @@ long long split_bytes(long long slots, int nparts, int B, int H_kv, int D) {
 // global-key sums go last, over the rows the dK/dV (or reduce) kernel wrote.
 template <typename E, int D, bool CAUSAL, bool WINDOW>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
-                       dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s, p);
+    constexpr bool CAN_G2 = D == 128 && !WINDOW;
+    if (CAN_G2 && p.dq_groups == 2)
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW, CAN_G2>),
+                           dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(2 * kThreads), 0,
+                           s, p);
+    else
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
+                           dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s,
+                           p);
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW>),
                        dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit + p.nfar)),
                        dim3(kThreads), 0, s, p);
@@ -1059,6 +1117,16 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     p.B = B; p.H = H; p.H_kv = H_kv; p.T = T;
     p.group = H / H_kv;
     p.nblk = (int)nblk;
+    // Two dQ key-range groups on small grids at D = 128 (the forward's rule:
+    // at most a quarter of the 512 resident 4-wave work-groups -- 256 CUs x 2
+    // by registers -- or rows of >= 2048 keys with all of them resident).
+    {
+        const long long units = (long long)B * H * nblk;
+        p.dq_groups = D == 128 && window < 0 &&
+                              (4 * units <= 512 || (T >= 2048 && units <= 512))
+                          ? 2
+                          : 1;
+    }
     p.c = scale * kLog2e;
     p.scale = scale;
     p.hsplit = hs;

@@ -237,7 +237,10 @@ long long fa_window_bitmap_bytes(int T);
  * a head split the fp32 dK and dV parts; overwritten (calls sharing a
  * workspace must be ordered on one stream); FA_ERR_WORKSPACE if too small.
  * dq, dk, dv must not overlap any input, the workspace or each other. Two
- * kernels (three with a head split) are enqueued on `stream`.
+ * kernels (three with a head split) are enqueued on `stream`. At D = 128,
+ * for sizes where fa_fwd_key_groups reports 2, the dQ kernel also splits
+ * each query tile's key tiles between two wave groups and adds their fp32
+ * sums (dQ then differs from the one-group order only in rounding).
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
            const void *dout, void *dq, void *dk, void *dv, int B, int H, int H_kv, int T,
