@@ -66,8 +66,10 @@ struct BwdParams {
     int dq_groups;
     float c;                // scale * log2(e) (signed)
     float scale;
-    // Head split of the dK/dV kernel: work-group (key tile, b, g, part s)
-    // takes query heads [s*group/hsplit, (s+1)*group/hsplit) of kv head g.
+    // Split of the dK/dV kernel: work-group (key tile, b, g, part s) takes
+    // items [s*n/hsplit, (s+1)*n/hsplit) of the key tile's list of n =
+    // group * nper (query head, query tile) items, heads outer -- whole query
+    // heads [s*group/hsplit, (s+1)*group/hsplit) when hsplit divides group.
     // With hsplit > 1 each part writes fp32 sums (dK unscaled) to
     // dkpart/dvpart [s][b][t][g][d], added in part order by the reduce kernel.
     int hsplit;
@@ -357,12 +359,16 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             itb = (int)(chunk * n / p.nchunk);
             ite = (int)((chunk + 1) * n / p.nchunk);
         } else {
+            // part hs of hsplit takes a contiguous run of the key tile's (query
+            // head, query tile) list; with hsplit dividing the group size the
+            // runs are whole heads. A part may get no items (it then writes
+            // zero sums).
             a2 = max(lo, i_beg);
             nper = hi - a2 + 1;
-            hbase = g * p.group + hs * p.group / p.hsplit;     // this part's query heads
-            const int nh = g * p.group + (hs + 1) * p.group / p.hsplit - hbase;
-            itb = 0;
-            ite = nh * nper;
+            hbase = g * p.group;
+            const long long n = (long long)p.group * nper;
+            itb = (int)(hs * n / p.hsplit);
+            ite = (int)((hs + 1) * n / p.hsplit);
         }
         auto qtile0 = [&](int it, int &h) __attribute__((always_inline)) -> int {
             const int hq = it / nper;
@@ -949,15 +955,25 @@ constexpr long long kMaxGridB = (1LL << 24) - 1;
 bool aligned16(const void *ptr) { return ((uintptr_t)ptr % 16) == 0; }
 
 constexpr long long kTargetWG = 1024;   // dK/dV work-groups aimed for (4 per CU)
+constexpr long long kNumCUB = 256;      // MI355X compute units
+constexpr long long kMaxQueryParts = 8; // query-tile runs per key tile (library choice)
 
-// Head parts of the dK/dV kernel: the requested count (capped at the group
-// size) or, for 0, enough parts to bring the launch to kTargetWG work-groups.
-int head_parts(int B, int H, int H_kv, int T, int requested) {
+// Parts of the dK/dV kernel: the requested count (capped at the group size)
+// or, for 0, enough parts to bring the launch to kTargetWG work-groups --
+// runs of query heads, or, with one query head per kv head, key tiles for at
+// most half the CUs and T >= 4096, runs of each key tile's query tiles (not
+// for the window masks, whose key tiles see only their band's query tiles).
+int head_parts(int B, int H, int H_kv, int T, int requested, bool window) {
     const int group = H / H_kv;
     if (requested > 0) return requested < group ? requested : group;
     const long long nwg = (long long)B * H_kv * (((long long)T + kBlk - 1) / kBlk);
     if (nwg <= 0) return 1;
     const long long want = (kTargetWG + nwg - 1) / nwg;
+    // one query head per kv head, key tiles for at most half the CUs and long
+    // rows: split each key tile's query tiles instead (at most kMaxQueryParts
+    // runs; shorter rows or more key tiles lose more to the parts' fp32
+    // traffic than they gain)
+    if (!window && group == 1 && 2 * nwg <= kNumCUB && T >= 4096) return (int)(want < kMaxQueryParts ? want : kMaxQueryParts);
     return (int)(want < group ? want : group);
 }
 
@@ -1054,7 +1070,8 @@ extern "C" long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D
     if (B < 0 || H < 1 || H_kv < 1 || T < 0 || H % H_kv != 0 || head_split < 0 ||
         (D != 16 && D != 32 && D != 64 && D != 128))
         return -1;
-    return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split), nullptr);
+    return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split, false),
+                        nullptr);
 }
 
 extern "C" long long fa_bwd_window_workspace_bytes(int B, int H, int H_kv, int T, int D,
@@ -1062,7 +1079,7 @@ extern "C" long long fa_bwd_window_workspace_bytes(int B, int H, int H_kv, int T
     const long long base = fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split);
     if (base < 0 || window < 0 || n_global < 0) return -1;
     if (n_global == 0 || T == 0 || B == 0) return base;
-    const int hs = head_parts(B, H, H_kv, T, head_split);
+    const int hs = head_parts(B, H, H_kv, T, head_split, true);
     const int w = window < T ? window : T;
     const long long slots = n_global < T ? n_global : T;
     const long long extra =
@@ -1093,9 +1110,12 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     for (const void *ptr : ptrs)
         if (!aligned16(ptr)) return FA_ERR_ALIGN;
     if (((uintptr_t)lse % 4) != 0 || ((uintptr_t)global_bits % 8) != 0) return FA_ERR_ALIGN;
-    const int hs = head_parts(B, H, H_kv, T, head_split);
+    const int hs = head_parts(B, H, H_kv, T, head_split, window >= 0);
+    // The workspace starts with fa_bwd's layout for these arguments (the
+    // window's split sums follow it); the window may use fewer parts of it.
     long long stat_bytes = 0;
-    const long long need = bwd_ws_bytes(B, H, H_kv, T, D, hs, &stat_bytes);
+    const long long need =
+        bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split, false), &stat_bytes);
     if (need < 0) return FA_ERR_OVERFLOW;
     if (workspace_bytes < need) return FA_ERR_WORKSPACE;
     // element counts, 32-bit staging ranges (64 rows of a tile) and grids

@@ -226,11 +226,15 @@ long long fa_window_bitmap_bytes(int T);
  * All contiguous, 16-byte aligned (lse 4-byte). Precision: P and dS are
  * rounded to the input type only as MFMA operands, everything else is fp32;
  * the outputs are rounded to nearest even. fp32 inputs return FA_ERR_DTYPE.
- * head_split: the dK/dV kernel works per (128-key tile, kv head); with
- * several query heads per kv head it can also split the group's heads into
- * head_split parts (capped at H / H_kv) whose fp32 sums a reduce kernel adds
- * in a fixed order (still deterministic). 0 lets the library choose (enough
- * parts to occupy the GPU); 1 means no split; < 0 is FA_ERR_BAD_SHAPE.
+ * head_split: the dK/dV kernel works per (128-key tile, kv head), walking
+ * the list of (query head, query tile) pairs that see the tile, heads outer;
+ * it can split that list into head_split contiguous parts (whole query heads
+ * when head_split divides H / H_kv) whose fp32 sums a reduce kernel adds in
+ * a fixed order (still deterministic). A value > 0 is capped at H / H_kv.
+ * 0 lets the library choose: enough parts to occupy the GPU, up to H / H_kv,
+ * or, with H == H_kv, T >= 4096 and at most 128 (batch, kv head, 128-key
+ * tile) work-groups, up to 8 parts of each key tile's query tiles. 1 means
+ * no split; < 0 is FA_ERR_BAD_SHAPE.
  * workspace: caller-owned device memory, 16-byte aligned, at least
  * fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split) bytes: float32 Delta
  * [B][H][T], float32 lse * log2(e) [B][H][T] (padded to 16 bytes), then with
@@ -271,7 +275,7 @@ int fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
 
 /* Workspace bytes fa_bwd needs for these sizes and head_split (0 = the
  * library's choice, as in fa_bwd): 8 * B * H * T rounded up to 16, plus
- * 8 * parts * B * T * H_kv * D when the group's heads are split into parts > 1;
+ * 8 * parts * B * T * H_kv * D when the dK/dV work is split into parts > 1;
  * -1 for invalid sizes or overflow. */
 long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D, int head_split);
 

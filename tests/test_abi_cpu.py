@@ -258,6 +258,16 @@ def test_bwd_workspace_bytes(lib):
     stat = (2 * 4 * 100 * 8 + 15) // 16 * 16
     assert f(2, 4, 2, 100, 64, 1) == stat                    # no head split
     assert f(2, 4, 4, 100, 64, 0) == stat                    # one query head per kv head
+    # one query head per kv head, rows of >= 4096 keys and at most 128 key-tile
+    # work-groups: the library splits each key tile's query tiles into
+    # min(8, ceil(1024 / work-groups)) parts
+    st = lambda B, H, T: (B * H * T * 8 + 15) // 16 * 16
+    assert f(1, 1, 1, 8192, 128, 0) == st(1, 1, 8192) + 8 * 1 * 8192 * 1 * 128 * 8   # 64 WGs
+    assert f(2, 1, 1, 8192, 128, 0) == st(2, 1, 8192) + 8 * 2 * 8192 * 1 * 128 * 8   # 128 WGs
+    assert f(1, 2, 2, 4096, 64, 0) == st(1, 2, 4096) + 8 * 1 * 4096 * 2 * 64 * 8    # 64 WGs
+    assert f(3, 1, 1, 8192, 128, 0) == st(3, 1, 8192)        # 192 WGs: no split
+    assert f(1, 1, 1, 4095, 128, 0) == st(1, 1, 4095)        # shorter rows: no split
+    assert f(1, 1, 1, 8192, 128, 5) == st(1, 1, 8192)        # explicit: capped at the group
     # two parts: plus fp32 dK and dV parts of [2][B][T][H_kv][D]
     assert f(2, 4, 2, 100, 64, 2) == stat + 2 * 2 * 100 * 2 * 64 * 8
     assert f(2, 4, 2, 100, 64, 9) == f(2, 4, 2, 100, 64, 2)  # capped at the group size
@@ -288,6 +298,13 @@ def test_bwd_window_workspace_bytes(lib):
     assert per > 0 and per % (2 * 1 * 64 * 8) == 0 and (per // (2 * 64 * 8)) >= 3 + 1
     assert extra[2] - extra[0] == 3 * per and extra[0] == 32 + per
     assert f(1, 1, 1, 100, 64, 5, 500, 1) == f(1, 1, 1, 100, 64, 5, 100, 1)   # slots <= T
+    # where fa_bwd splits query tiles (H == H_kv, long rows, few key tiles) the
+    # window keeps one part -- the same split sums as with head_split = 1 --
+    # but they still start past fa_bwd's (larger) size
+    extra0 = f(1, 1, 1, 8192, 128, 64, 2, 0) - base(1, 1, 1, 8192, 128, 0)
+    extra1 = f(1, 1, 1, 8192, 128, 64, 2, 1) - base(1, 1, 1, 8192, 128, 1)
+    assert base(1, 1, 1, 8192, 128, 0) > base(1, 1, 1, 8192, 128, 1)
+    assert extra0 == extra1 and extra0 > 32 and (extra0 - 32) % (2 * 1 * 1 * 128 * 8) == 0
     assert f(0, 1, 1, 100, 64, 5, 3, 1) == 0
     assert f(1, 1, 1, 100, 64, -1, 3, 1) == -1
     assert f(1, 1, 1, 100, 64, 5, -1, 1) == -1
