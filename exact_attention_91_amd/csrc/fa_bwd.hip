@@ -30,7 +30,9 @@
 //    8-wave G2 instantiation splits each query tile's key tiles between two
 //    groups of 4 waves and adds the second group's dQ^T into the first's
 //    through LDS.
-//  * fa_bwd_reduce_kernel (head split only): adds the fp32 parts in order.
+//  * fa_bwd_reduce_kernel (dK/dV parts only): adds the fp32 parts in order;
+//    fa_bwd_dq_reduce_kernel does the same for dQ key parts (long rows, few
+//    query tiles: the two-group dQ kernel's key tiles split over work-groups).
 //  * Window mode (fa_bwd_window): both main kernels visit only the tiles that
 //    meet a tile's band or hold a global token. A key tile holding a global
 //    token is seen by far queries too; with workspace slots for the global
@@ -64,6 +66,12 @@ struct BwdParams {
     // 2: the dQ kernel splits each query tile's key tiles between two groups
     // of 4 waves (8-wave work-groups, D = 128, plain masks); 1: one group.
     int dq_groups;
+    // dQ key parts (two-group kernel only): work-group (query tile, part s)
+    // takes key tiles [s*n/dq_parts, (s+1)*n/dq_parts) of the tile's n and,
+    // with dq_parts > 1, writes fp32 sums (unscaled) to dqpart[s][b][t][h][d];
+    // fa_bwd_dq_reduce_kernel adds them in part order.
+    int dq_parts;
+    float *dqpart;
     float c;                // scale * log2(e) (signed)
     float scale;
     // Split of the dK/dV kernel: work-group (key tile, b, g, part s) takes
@@ -608,8 +616,11 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_bwd_dq_kernel
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
     const int nbh = p.B * p.H;
-    const int tq = blockIdx.x / nbh;
-    const int bh = blockIdx.x - tq * nbh;
+    const int npart = G2 ? p.dq_parts : 1;
+    const int kpart = G2 ? (int)(blockIdx.x % npart) : 0;   // this work-group's key part
+    const int id = G2 ? (int)(blockIdx.x / npart) : (int)blockIdx.x;
+    const int tq = id / nbh;
+    const int bh = id - tq * nbh;
     const int b = bh / p.H, h = bh - b * p.H;
     const int g = h / p.group;
     const int q0 = (p.nblk - 1 - tq) * kBlk;
@@ -656,7 +667,7 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_bwd_dq_kernel
         if (qrow < T) {
             const long long r = ((long long)b * p.H + h) * T + qrow;
             l2 = p.lse[r] * kLog2e;
-            if (half == 0 && grp == 0) {
+            if (half == 0 && grp == 0 && kpart == 0) {
                 p.delta[r] = dl;
                 p.l2[r] = l2;
             }
@@ -665,10 +676,13 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_bwd_dq_kernel
 
     const int kend = CAUSAL ? min(T, q0 + kBlk) : T;
     const int nkt = (kend + BK - 1) / BK;
-    // G2: group 0 takes key tiles [0, ghalf), group 1 [ghalf, nkt).
-    const int ghalf = (nkt + 1) / 2;
-    const int jbeg = G2 && grp ? ghalf : 0;
-    const int jend = G2 && !grp ? ghalf : nkt;
+    // G2: this part's key tiles [pbeg, pend); group 0 takes the first ghalf
+    // of them, group 1 the rest.
+    const int pbeg = (int)((long long)kpart * nkt / npart);
+    const int pend = (int)((long long)(kpart + 1) * nkt / npart);
+    const int ghalf = (pend - pbeg + 1) / 2;
+    const int jbeg = G2 ? (grp ? pbeg + ghalf : pbeg) : 0;
+    const int jend = G2 ? (grp ? pend : pbeg + ghalf) : nkt;
     // Window mode: key tiles meeting the band of this query tile (blo..bhi)
     // or holding a global token; the others are never loaded.
     int blo = 0, bhi = nkt - 1;
@@ -868,6 +882,22 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_bwd_dq_kernel
     }
 
     if (!wave_live || qrow >= T) return;
+    if (G2 && npart > 1) {
+        // this part's fp32 sums; fa_bwd_dq_reduce_kernel adds the parts and scales
+        float *prow = p.dqpart + ((long long)kpart * p.B * T + (long long)b * T + qrow) * qrs +
+                      (long long)h * D;
+#pragma unroll
+        for (int n = 0; n < ND; ++n)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d = 32 * n + 8 * rg + 4 * half;
+                f32x4_t q4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q4[e] = dqacc[n][4 * rg + e];
+                *(f32x4_t *)(prow + d) = q4;
+            }
+        return;
+    }
     unsigned short *dqrow = (unsigned short *)p.dq + ((long long)b * T + qrow) * qrs + h * D;
     const float sc = p.scale;
 #pragma unroll
@@ -915,6 +945,21 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(BwdParams p, long lo
 // sum_part gpv[slot][part], parts in order (deterministic), over the rows the
 // other kernels wrote for those keys. Thread: (slot, b, g, 4 dims).
 // ---------------------------------------------------------------------------
+// dQ = scale * sum_s dqpart[s], parts added in order s = 0, 1, ... Each thread
+// handles four consecutive elements of the [B][T][H][D] array.
+template <typename E>
+__global__ __launch_bounds__(256) void fa_bwd_dq_reduce_kernel(BwdParams p, long long n) {
+    typedef E e4v __attribute__((ext_vector_type(4)));
+    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    f32x4_t q = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.dq_parts; ++s) q += *(const f32x4_t *)(p.dqpart + s * n + i);
+    e4v q4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q4[e] = (E)(q[e] * p.scale);
+    *(e4v *)((E *)p.dq + i) = q4;
+}
+
 template <typename E>
 __global__ __launch_bounds__(256) void fa_bwd_gsum_kernel(BwdParams p, int D) {
     typedef E e4v __attribute__((ext_vector_type(4)));
@@ -973,25 +1018,56 @@ int head_parts(int B, int H, int H_kv, int T, int requested, bool window) {
     // rows: split each key tile's query tiles instead (at most kMaxQueryParts
     // runs; shorter rows or more key tiles lose more to the parts' fp32
     // traffic than they gain)
-    if (!window && group == 1 && 2 * nwg <= kNumCUB && T >= 4096) return (int)(want < kMaxQueryParts ? want : kMaxQueryParts);
+    if (!window && group == 1 && 2 * nwg <= kNumCUB && T >= 4096)
+        return (int)(want < kMaxQueryParts ? want : kMaxQueryParts);
     return (int)(want < group ? want : group);
 }
 
 // Workspace: Delta and L2 (B*H*T floats each, padded to 16 bytes), then, with
 // hs > 1 head parts, the fp32 dK and dV parts (hs * B*T*H_kv*D floats each).
 // Sets *stat_bytes to the size of the first region; -1 on overflow.
-long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, long long *stat_bytes) {
-    long long rows, part, total;
+long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, int dqp,
+                       long long *stat_bytes, long long *dq_offset) {
+    long long rows, part, total, dqb;
     if (__builtin_mul_overflow((long long)B * H, (long long)T, &rows) || rows > (1LL << 58))
         return -1;
     const long long stat = (rows * 8 + 15) / 16 * 16;
     if (stat_bytes) *stat_bytes = stat;
-    if (hs <= 1) return stat;
-    if (__builtin_mul_overflow((long long)B * T, (long long)H_kv * D, &part) ||
-        __builtin_mul_overflow(part, (long long)hs * 8, &part) ||
-        __builtin_add_overflow(stat, part, &total))
-        return -1;
+    total = stat;
+    if (hs > 1) {
+        if (__builtin_mul_overflow((long long)B * T, (long long)H_kv * D, &part) ||
+            __builtin_mul_overflow(part, (long long)hs * 8, &part) ||
+            __builtin_add_overflow(total, part, &total))
+            return -1;
+    }
+    if (dq_offset) *dq_offset = total;
+    if (dqp > 1) {
+        if (__builtin_mul_overflow(rows, (long long)D, &dqb) ||
+            __builtin_mul_overflow(dqb, (long long)dqp * 4, &dqb) ||
+            __builtin_add_overflow(total, dqb, &total))
+            return -1;
+    }
     return total;
+}
+
+// Two key-range groups in the dQ kernel at D = 128 on small grids (the
+// forward's rule: at most a quarter of the 512 resident 4-wave work-groups --
+// 256 CUs x 2 by registers -- or rows of >= 2048 keys with all of them
+// resident); plain masks only.
+int dq_groups_for(int B, int H, int T, int D, bool window) {
+    const long long units = (long long)B * H * (((long long)T + kBlk - 1) / kBlk);
+    return D == 128 && !window && (4 * units <= 512 || (T >= 2048 && units <= 512)) ? 2 : 1;
+}
+
+// Key parts of the two-group dQ kernel: with rows of >= 4096 keys and query
+// tiles for at most half the CUs (one 8-wave work-group per CU), enough parts
+// to give each CU one work-group (at most 8).
+int dq_parts_for(int B, int H, int T, int D, bool window) {
+    if (dq_groups_for(B, H, T, D, window) != 2 || T < 4096) return 1;
+    const long long units = (long long)B * H * (((long long)T + kBlk - 1) / kBlk);
+    if (units <= 0 || 2 * units > kNumCUB) return 1;
+    const long long n = kNumCUB / units;
+    return (int)(n < 8 ? n : 8);
 }
 
 // Far parts per split global tile: runs of about the main work-group's
@@ -1026,8 +1102,8 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
     constexpr bool CAN_G2 = D == 128 && !WINDOW;
     if (CAN_G2 && p.dq_groups == 2)
         hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW, CAN_G2>),
-                           dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(2 * kThreads), 0,
-                           s, p);
+                           dim3((unsigned)((long long)p.B * p.H * p.nblk * p.dq_parts)),
+                           dim3(2 * kThreads), 0, s, p);
     else
         hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
                            dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s,
@@ -1038,6 +1114,11 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
     if (p.hsplit > 1) {
         const long long n = (long long)p.B * p.T * p.H_kv * D;
         hipLaunchKernelGGL((fa_bwd_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
+                           dim3(256), 0, s, p, n);
+    }
+    if (p.dq_parts > 1) {
+        const long long n = (long long)p.B * p.T * p.H * D;
+        hipLaunchKernelGGL((fa_bwd_dq_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
                            dim3(256), 0, s, p, n);
     }
     if (WINDOW && p.nslots > 0) {
@@ -1071,7 +1152,7 @@ extern "C" long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D
         (D != 16 && D != 32 && D != 64 && D != 128))
         return -1;
     return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split, false),
-                        nullptr);
+                        dq_parts_for(B, H, T, D, false), nullptr, nullptr);
 }
 
 extern "C" long long fa_bwd_window_workspace_bytes(int B, int H, int H_kv, int T, int D,
@@ -1113,9 +1194,10 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     const int hs = head_parts(B, H, H_kv, T, head_split, window >= 0);
     // The workspace starts with fa_bwd's layout for these arguments (the
     // window's split sums follow it); the window may use fewer parts of it.
-    long long stat_bytes = 0;
+    long long stat_bytes = 0, dq_offset = 0;
     const long long need =
-        bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split, false), &stat_bytes);
+        bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split, false),
+                     dq_parts_for(B, H, T, D, false), &stat_bytes, &dq_offset);
     if (need < 0) return FA_ERR_OVERFLOW;
     if (workspace_bytes < need) return FA_ERR_WORKSPACE;
     // element counts, 32-bit staging ranges (64 rows of a tile) and grids
@@ -1137,16 +1219,9 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     p.B = B; p.H = H; p.H_kv = H_kv; p.T = T;
     p.group = H / H_kv;
     p.nblk = (int)nblk;
-    // Two dQ key-range groups on small grids at D = 128 (the forward's rule:
-    // at most a quarter of the 512 resident 4-wave work-groups -- 256 CUs x 2
-    // by registers -- or rows of >= 2048 keys with all of them resident).
-    {
-        const long long units = (long long)B * H * nblk;
-        p.dq_groups = D == 128 && window < 0 &&
-                              (4 * units <= 512 || (T >= 2048 && units <= 512))
-                          ? 2
-                          : 1;
-    }
+    p.dq_groups = dq_groups_for(B, H, T, D, window >= 0);
+    p.dq_parts = dq_parts_for(B, H, T, D, window >= 0);
+    p.dqpart = p.dq_parts > 1 ? (float *)((char *)workspace + dq_offset) : nullptr;
     p.c = scale * kLog2e;
     p.scale = scale;
     p.hsplit = hs;

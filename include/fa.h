@@ -238,13 +238,17 @@ long long fa_window_bitmap_bytes(int T);
  * workspace: caller-owned device memory, 16-byte aligned, at least
  * fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split) bytes: float32 Delta
  * [B][H][T], float32 lse * log2(e) [B][H][T] (padded to 16 bytes), then with
- * a head split the fp32 dK and dV parts; overwritten (calls sharing a
- * workspace must be ordered on one stream); FA_ERR_WORKSPACE if too small.
- * dq, dk, dv must not overlap any input, the workspace or each other. Two
- * kernels (three with a head split) are enqueued on `stream`. At D = 128,
- * for sizes where fa_fwd_key_groups reports 2, the dQ kernel also splits
- * each query tile's key tiles between two wave groups and adds their fp32
- * sums (dQ then differs from the one-group order only in rounding).
+ * dK/dV parts the fp32 dK and dV parts, then with dQ parts the fp32 dQ parts;
+ * overwritten (calls sharing a workspace must be ordered on one stream);
+ * FA_ERR_WORKSPACE if too small. dq, dk, dv must not overlap any input, the
+ * workspace or each other. Two kernels are enqueued on `stream`, plus one
+ * reduce kernel for the dK/dV parts and one for the dQ parts when there are
+ * any. At D = 128, for sizes where fa_fwd_key_groups reports 2, the dQ kernel
+ * splits each query tile's key tiles between two wave groups and adds their
+ * fp32 sums; with T >= 4096 and at most 128 query tiles of 128 rows it also
+ * splits them into floor(256 / query tiles) parts (at most 8), each a
+ * work-group whose fp32 sums the dQ reduce kernel adds in part order. dQ then
+ * differs from the one-group order only in rounding.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
            const void *dout, void *dq, void *dk, void *dv, int B, int H, int H_kv, int T,
@@ -275,8 +279,9 @@ int fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
 
 /* Workspace bytes fa_bwd needs for these sizes and head_split (0 = the
  * library's choice, as in fa_bwd): 8 * B * H * T rounded up to 16, plus
- * 8 * parts * B * T * H_kv * D when the dK/dV work is split into parts > 1;
- * -1 for invalid sizes or overflow. */
+ * 8 * parts * B * T * H_kv * D when the dK/dV work is split into parts > 1,
+ * plus 4 * dq_parts * B * T * H * D when dQ's keys are split into parts > 1
+ * (as described at fa_bwd); -1 for invalid sizes or overflow. */
 long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D, int head_split);
 
 /* Workspace bytes fa_bwd_window needs to split the far queries of up to
