@@ -26,10 +26,9 @@
 //    and L2 = L log2(e) for them (stored in the workspace for the dK/dV
 //    kernel), streams K and V tiles, computes S^T = K Q^T and dP^T = V dO^T,
 //    and accumulates dQ^T += K^T dS^T with K^T from transposing reads of the
-//    K tile. At D = 128 on small grids (the forward's two-group rule) its
-//    8-wave G2 instantiation splits each query tile's key tiles between two
-//    groups of 4 waves and adds the second group's dQ^T into the first's
-//    through LDS.
+//    K tile. At D = 64 and 128 on small grids its 8-wave G2 instantiation
+//    splits each query tile's key tiles between two groups of 4 waves and adds
+//    the second group's dQ^T into the first's through LDS.
 //  * fa_bwd_reduce_kernel (dK/dV parts only): adds the fp32 parts in order;
 //    fa_bwd_dq_reduce_kernel does the same for dQ key parts (long rows, few
 //    query tiles: the two-group dQ kernel's key tiles split over work-groups).
@@ -64,7 +63,7 @@ struct BwdParams {
     int group;              // H / H_kv
     int nblk;               // 128-row tiles per sequence
     // 2: the dQ kernel splits each query tile's key tiles between two groups
-    // of 4 waves (8-wave work-groups, D = 128, plain masks); 1: one group.
+    // of 4 waves (8-wave work-groups, D >= 64, plain masks); 1: one group.
     int dq_groups;
     // dQ key parts (two-group kernel only): work-group (query tile, part s)
     // takes key tiles [s*n/dq_parts, (s+1)*n/dq_parts) of the tile's n and,
@@ -1050,13 +1049,17 @@ long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, int dqp,
     return total;
 }
 
-// Two key-range groups in the dQ kernel at D = 128 on small grids (the
-// forward's rule: at most a quarter of the 512 resident 4-wave work-groups --
-// 256 CUs x 2 by registers -- or rows of >= 2048 keys with all of them
-// resident); plain masks only.
+// Two key-range groups in the dQ kernel on small grids, plain masks only. At
+// D = 128 the forward's rule: at most a quarter of the 512 resident 4-wave
+// work-groups (256 CUs x 2 by registers), or rows of >= 2048 keys with all of
+// them resident. At D = 64 (768 resident: 3 per CU by registers) at most a
+// quarter, or half with rows of >= 2048 keys (with all resident it was 5 %
+// slower).
 int dq_groups_for(int B, int H, int T, int D, bool window) {
     const long long units = (long long)B * H * (((long long)T + kBlk - 1) / kBlk);
-    return D == 128 && !window && (4 * units <= 512 || (T >= 2048 && units <= 512)) ? 2 : 1;
+    if (window || D < 64) return 1;
+    if (D == 64) return 4 * units <= 768 || (T >= 2048 && 2 * units <= 768) ? 2 : 1;
+    return 4 * units <= 512 || (T >= 2048 && units <= 512) ? 2 : 1;
 }
 
 // Key parts of the two-group dQ kernel: with rows of >= 4096 keys and query
@@ -1099,7 +1102,7 @@ long long split_bytes(long long slots, int nparts, int B, int H_kv, int D) {
 // global-key sums go last, over the rows the dK/dV (or reduce) kernel wrote.
 template <typename E, int D, bool CAUSAL, bool WINDOW>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
-    constexpr bool CAN_G2 = D == 128 && !WINDOW;
+    constexpr bool CAN_G2 = D >= 64 && !WINDOW;
     if (CAN_G2 && p.dq_groups == 2)
         hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW, CAN_G2>),
                            dim3((unsigned)((long long)p.B * p.H * p.nblk * p.dq_parts)),

@@ -243,9 +243,10 @@ long long fa_window_bitmap_bytes(int T);
  * FA_ERR_WORKSPACE if too small. dq, dk, dv must not overlap any input, the
  * workspace or each other. Two kernels are enqueued on `stream`, plus one
  * reduce kernel for the dK/dV parts and one for the dQ parts when there are
- * any. At D = 128, for sizes where fa_fwd_key_groups reports 2, the dQ kernel
- * splits each query tile's key tiles between two wave groups and adds their
- * fp32 sums; with T >= 4096 and at most 128 query tiles of 128 rows it also
+ * any. On small grids -- at D = 128 the sizes where fa_fwd_key_groups reports
+ * 2, at D = 64 at most 192 query tiles of 128 rows, or 384 with T >= 2048 --
+ * the dQ kernel splits each query tile's key tiles between two wave groups and
+ * adds their fp32 sums; with T >= 4096 and at most 128 query tiles it also
  * splits them into floor(256 / query tiles) parts (at most 8), each a
  * work-group whose fp32 sums the dQ reduce kernel adds in part order. dQ then
  * differs from the one-group order only in rounding.

@@ -268,12 +268,16 @@ def test_bwd_workspace_bytes(lib):
         4 * 1 * 8192 * 1 * 128 * 4                              # 64 tiles: 8 + 4 parts
     assert f(2, 1, 1, 8192, 128, 0) == st(2, 1, 8192) + 8 * 2 * 8192 * 1 * 128 * 8 + \
         2 * 2 * 8192 * 1 * 128 * 4                              # 128 tiles: 8 + 2 parts
-    assert f(1, 2, 2, 4096, 64, 0) == st(1, 2, 4096) + 8 * 1 * 4096 * 2 * 64 * 8    # D = 64
+    assert f(1, 2, 2, 4096, 64, 0) == st(1, 2, 4096) + 8 * 1 * 4096 * 2 * 64 * 8 + \
+        4 * 1 * 4096 * 2 * 64 * 4                               # D = 64, 64 tiles: 8 + 4 parts
     assert f(3, 1, 1, 8192, 128, 0) == st(3, 1, 8192)        # 192 tiles: no split
     assert f(1, 1, 1, 4095, 128, 0) == st(1, 1, 4095)        # shorter rows: no split
     # explicit head_split: dK/dV capped at the group; dQ's parts do not depend on it
     assert f(1, 1, 1, 8192, 128, 5) == st(1, 1, 8192) + 4 * 1 * 8192 * 1 * 128 * 4
-    assert f(1, 1, 1, 8192, 64, 1) == st(1, 1, 8192)         # D = 64: no dQ parts
+    assert f(1, 1, 1, 8192, 64, 1) == st(1, 1, 8192) + 4 * 1 * 8192 * 1 * 64 * 4
+    assert f(1, 1, 1, 8192, 32, 1) == st(1, 1, 8192)         # D < 64: one dQ group, no parts
+    assert f(1, 3, 3, 8192, 64, 1) == st(1, 3, 8192)         # 192 tiles: one dQ part
+
     # two parts: plus fp32 dK and dV parts of [2][B][T][H_kv][D]
     assert f(2, 4, 2, 100, 64, 2) == stat + 2 * 2 * 100 * 2 * 64 * 8
     assert f(2, 4, 2, 100, 64, 9) == f(2, 4, 2, 100, 64, 2)  # capped at the group size

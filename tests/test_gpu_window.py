@@ -217,11 +217,13 @@ def test_bwd_window_head_split(head_split):
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_window_covering_everything_is_bwd_bitwise(causal):
     """A window covering every key without global tokens: the same tiles and
-    arithmetic as fa_bwd, bitwise the same gradients."""
+    arithmetic as fa_bwd, bitwise the same gradients. The sizes give fa_bwd's
+    dQ kernel one wave group (240 query tiles of short rows at D = 64; on small
+    grids it splits keys between two groups, which the window kernels do not)."""
     from exact_attention_91_amd import fa
     from exact_attention_91_amd.inputs import generate_dout
-    x = generate(2, 4, 2, 300, 64, "bf16", 9991)
-    do = generate_dout(2, 4, 300, 64, "bf16", 9991)[0].cuda()
+    x = generate(5, 16, 2, 300, 64, "bf16", 9991)
+    do = generate_dout(5, 16, 300, 64, "bf16", 9991)[0].cuda()
     q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
     o, lse = fa.fwd(q, k, v, causal=causal, scale=0.125)
     a = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=0.125, head_split=1)
