@@ -265,11 +265,14 @@ def main():
 
     peak = PEAK[w.dtype]
     groups = fa.key_groups(w.B, w.H, w.T, w.D, torch_dtype(w.dtype))
+    # head pairs: an even number of query heads per kv head with one key group
+    pairs = groups == 1 and (w.H // w.H_kv) % 2 == 0
     roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
             "frac": tflops / peak, "traffic": traffic_for(w.name),
             "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
                        f"{str(a.nsplit > 1).lower()}, false, "
-                       f"{str(a.nsplit == 1 and groups == 2).lower()}>"
+                       f"{str(a.nsplit == 1 and groups == 2).lower()}, "
+                       f"{str(a.nsplit == 1 and pairs).lower()}>"
                        if w.dtype in _ELEM else
                        f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
     if w.window >= 0 and a.which == "fwd":

@@ -130,17 +130,17 @@ struct Half16<_Float16> {
 constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 family)
 
 
-// Issue this wave's share (of 4 waves) of the global->LDS copies of two
+// Issue this wave's share (of NW waves) of the global->LDS copies of two
 // 64-row tiles, e.g. a K tile and a V tile (buffer loads straight into LDS;
-// rows past T read as zeros). koff/voff: per-lane byte offsets of the global
-// chunk each lane fetches for its LDS slot.
-template <int D>
+// rows past T read as zeros): loads wave, wave + NW, ... koff/voff: per-lane
+// byte offsets of the global chunk each lane fetches for its LDS slot.
+template <int D, int NW = 4>
 __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const unsigned short *vbase,
                                            long long ks1, long long vs1, int T, int key0,
                                            int wave, const int *koff, const int *voff,
                                            unsigned char *kdst, unsigned char *vdst) {
     using L = Bf16Layout<D>;
-    constexpr int NI = (L::NLOAD + 3) / 4;
+    constexpr int NI = (L::NLOAD + NW - 1) / NW;
     // Valid bytes from this tile's first row; (63 * stride + D) * 2 < 2^31 is
     // checked on the host.
     const int rows = min(T - key0, L::BK);
@@ -152,8 +152,8 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
         ((rows - 1) * (int)vs1 + D) * 2, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int idx = wave + 4 * i;
-        if (L::NLOAD % 4 == 0 || idx < L::NLOAD) {
+        const int idx = wave + NW * i;
+        if (L::NLOAD % NW == 0 || idx < L::NLOAD) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kdst + idx * 1024), 16,
                                                      koff[i], 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + idx * 1024), 16,

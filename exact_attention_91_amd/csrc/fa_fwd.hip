@@ -53,6 +53,10 @@
 //    into the first's through LDS with the same online-softmax update. Twice
 //    the waves per query tile, so MFMA and softmax work of different waves
 //    overlap where one wave per SIMD would run them back to back.
+//  * Shared kv heads (an even number of query heads per kv head, one key
+//    group): the HP instantiation runs 8 waves per work-group, the same query
+//    tile of two query heads, which read one set of staged K/V tiles (half
+//    the staging and L2 reads per score; per-row arithmetic unchanged).
 //  * Variants of the same 16-bit kernel (template flags): SPLIT runs a range
 //    of each query tile's key tiles and writes an fp32 partial result that
 //    fa_lse_combine_kernel merges by the logsumexps (the online-softmax update
@@ -97,6 +101,10 @@ struct FwdParams {
     // 2: two 4-wave groups per work-group split each query tile's key tiles
     // (the G2 kernel); 1: one group.
     int groups;
+    // 1: one 8-wave work-group per (query tile, pair of query heads sharing a
+    // kv head), the two heads' groups reading one set of staged K/V tiles (the
+    // HP kernel); 0: one head per work-group.
+    int hpair;
 };
 
 template <bool B>
@@ -132,8 +140,8 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 // layout of fa_device.h: K is read as rows (kswz), V transposed for the V^T
 // operand of P.V (vswz).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW, bool G2>
-__global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kernel(FwdParams p) {
+template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW, bool G2, bool HP = false>
+__global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
     typedef typename H16::v8 e8_t;
@@ -144,6 +152,7 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kern
     constexpr int NV = D >= 32 ? D / 32 : 1;  // V^T address variants (one per block)
 
     static_assert(!G2 || (!SPLIT && !WINDOW && D >= 32), "G2: plain forward, D >= 32");
+    static_assert(!HP || (!G2 && !SPLIT && !WINDOW), "HP: plain forward");
     // Two K/V buffers as four distinct LDS variables: the accesses of each loop
     // step name their buffers statically, so the compiler knows the copies into
     // one buffer never alias the operand reads of the other and does not make
@@ -158,15 +167,35 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kern
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = G2 ? (wave8 >> 2) : 0;          // key-range group
-    const int wave = G2 ? (wave8 & 3) : wave8;      // wave within the group
-    unsigned char *const k_lds0 = k_lds0_ + grp * L::TILEB;
-    unsigned char *const v_lds0 = v_lds0_ + grp * L::TILEB;
-    unsigned char *const k_lds1 = k_lds1_ + grp * L::TILEB;
-    unsigned char *const v_lds1 = v_lds1_ + grp * L::TILEB;
+    // G2: key-range group; HP: query head of the pair
+    const int grp = G2 || HP ? (wave8 >> 2) : 0;
+    const int wave = G2 || HP ? (wave8 & 3) : wave8;   // wave within the group
+    // Staging: HP's two groups share one set of K/V buffers and split its loads
+    // eight ways; otherwise each group's 4 waves fill their own.
+    constexpr int NW = HP ? 8 : 4;
+    const int swave = HP ? wave8 : wave;
+    unsigned char *const k_lds0 = k_lds0_ + (G2 ? grp : 0) * L::TILEB;
+    unsigned char *const v_lds0 = v_lds0_ + (G2 ? grp : 0) * L::TILEB;
+    unsigned char *const k_lds1 = k_lds1_ + (G2 ? grp : 0) * L::TILEB;
+    unsigned char *const v_lds1 = v_lds1_ + (G2 ? grp : 0) * L::TILEB;
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
-    const Unit u = unit_of(p);
+    Unit u;
+    if (HP) {
+        // work-group = (query tile, batch, head pair); group g takes head 2 pair + g
+        // (both heads read the same kv head: the group size is even)
+        const int npair = p.H / 2;
+        const int nbp = p.B * npair;
+        const int t = blockIdx.x / nbp;
+        const int bp = blockIdx.x - t * nbp;
+        u.b = bp / npair;
+        u.h = 2 * (bp - u.b * npair) + grp;
+        u.g = u.h / p.group;
+        u.q0 = (p.nq - 1 - t) * kBQ;
+        u.s = 0;
+    } else {
+        u = unit_of(p);
+    }
     const int wq0 = u.q0 + wave * 32;       // first query row of this wave
     const int qrow = wq0 + col;             // this lane's query row
 
@@ -222,12 +251,12 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kern
         return (WINDOW && p.gbits && t < jend) ? p.gbits[t] : 0ull;
     };
 
-    // Staging: this wave issues 1 KB loads wave, wave+4, ... of each tile.
+    // Staging: this wave issues 1 KB loads swave, swave + NW, ... of each tile.
     // Lane slot (row, physical chunk) -> global byte offset within the tile.
-    int koff[(L::NLOAD + 3) / 4], voff[(L::NLOAD + 3) / 4];
+    int koff[(L::NLOAD + NW - 1) / NW], voff[(L::NLOAD + NW - 1) / NW];
 #pragma unroll
-    for (int i = 0; i < (L::NLOAD + 3) / 4; ++i) {
-        const int idx = wave + 4 * i;
+    for (int i = 0; i < (L::NLOAD + NW - 1) / NW; ++i) {
+        const int idx = swave + NW * i;
         const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
         const int pc = lane % L::C;
         koff[i] = row * (int)ks1 * 2 + 16 * (pc ^ L::kswz(row));
@@ -374,7 +403,7 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kern
         __builtin_amdgcn_s_waitcnt(0);   // this lane's loads of tile j have landed
         __syncthreads();
         if (jn < jend)
-            stage_tile<D>(kbase, vbase, ks1, vs1, T, jn * BK, wave, koff, voff, kn, vn);
+            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jn * BK, swave, koff, voff, kn, vn);
         const int key0 = j * BK;
         bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31) && (!G2 || j < jend);
         bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
@@ -394,7 +423,7 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kern
         int j = next_tile(-1);
         unsigned long long gj = tile_bits(j);
         if (j < jend)
-            stage_tile<D>(kbase, vbase, ks1, vs1, T, j * BK, wave, koff, voff, k_lds0, v_lds0);
+            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, j * BK, swave, koff, voff, k_lds0, v_lds0);
         while (j < jend) {
             const int jn = next_tile(j);
             const unsigned long long gn = tile_bits(jn);
@@ -410,7 +439,7 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kern
         // Both groups take ghalf steps, one barrier each; group 1's last step is
         // idle when nkt is odd (no staging, no math).
         if (jbeg < jend)
-            stage_tile<D>(kbase, vbase, ks1, vs1, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
+            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jbeg * BK, swave, koff, voff, k_lds0, v_lds0);
         for (int i = 0; i < ghalf; i += 2) {
             step(jbeg + i, 0ull, jbeg + i + 1, k_lds0, v_lds0, k_lds1, v_lds1);
             if (i + 1 < ghalf)
@@ -418,7 +447,7 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_fwd_half_kern
         }
     } else {
         if (jbeg < jend)
-            stage_tile<D>(kbase, vbase, ks1, vs1, T, jbeg * BK, wave, koff, voff, k_lds0, v_lds0);
+            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jbeg * BK, swave, koff, voff, k_lds0, v_lds0);
         for (int j = jbeg; j < jend; j += 2) {
             step(j, 0ull, j + 1, k_lds0, v_lds0, k_lds1, v_lds1);
             if (j + 1 < jend) step(j + 1, 0ull, j + 2, k_lds1, v_lds1, k_lds0, v_lds0);
@@ -786,7 +815,14 @@ bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 template <int D, bool CAUSAL, bool SPLIT, bool WINDOW>
 void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
     constexpr bool CAN_G2 = D >= 64 && !SPLIT && !WINDOW;
-    if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_BF16)
+    constexpr bool CAN_HP = !SPLIT && !WINDOW;
+    if (CAN_HP && p.hpair && dtype == FA_DTYPE_BF16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>),
+                           grid, dim3(2 * kThreads), 0, stream, p);
+    else if (CAN_HP && p.hpair && dtype == FA_DTYPE_F16)
+        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>),
+                           grid, dim3(2 * kThreads), 0, stream, p);
+    else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_BF16)
         hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid,
                            dim3(2 * kThreads), 0, stream, p);
     else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_F16)
@@ -879,6 +915,7 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
     p.window = 0;
     p.gbits = nullptr;
     p.groups = 1;
+    p.hpair = 0;
     return FA_OK;
 }
 
@@ -964,7 +1001,8 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     if (st != FA_OK || empty) return st;
     const long long units = (long long)p.nbh * p.nq;
     p.groups = key_groups(units, T, D, dtype);
-    const dim3 grid((unsigned)units);
+    p.hpair = p.groups == 1 && dtype != FA_DTYPE_F32 && p.group % 2 == 0 ? 1 : 0;
+    const dim3 grid((unsigned)(p.hpair ? units / 2 : units));
     hipStream_t s = (hipStream_t)stream;
     if (causal)
         launch_d<true, false>(p, D, dtype, grid, s);

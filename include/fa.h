@@ -108,6 +108,11 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
                    const long long o_strides[3], void *stream);
 
 /*
+ * (fa_fwd, fa_fwd_strided: with an even number of query heads per kv head and
+ * one key-range group, each work-group takes the same query tile of two query
+ * heads that share a kv head and stages that head's K/V tiles once for both;
+ * every row's arithmetic, and so the result, is unchanged bit for bit.)
+ *
  * Key-range groups per query tile that fa_fwd and fa_fwd_strided use for these
  * sizes. 2 for bf16/fp16 with D >= 64 when the launch is small: its
  * B * H * ceil(T/128) query tiles are at most a quarter of the 4-wave

@@ -66,6 +66,29 @@ def test_shared_kv_equals_expanded(dtype, H_kv):
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("D,H,H_kv", [(64, 8, 2), (128, 12, 1), (32, 4, 2)])
+def test_head_pairs_equal_expanded(dtype, D, H, H_kv):
+    """An even number of query heads per kv head and a launch with one key
+    group: the library gives each work-group two query heads that read one set
+    of staged K/V tiles. Every row's arithmetic is unchanged, so the result is
+    bitwise that of the same heads each with its own kv head (one head per
+    work-group), and matches the oracle."""
+    B, T = 16, 300
+    assert fa.key_groups(B, H, T, D, torch.bfloat16) == 1
+    x = generate(B, H, H_kv, T, D, dtype, 304 + D + H)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    ke = k.repeat_interleave(H // H_kv, dim=2).contiguous()
+    ve = v.repeat_interleave(H // H_kv, dim=2).contiguous()
+    for causal in (False, True):
+        o1, l1 = _run(q, k, v, causal)
+        o2, l2 = _run(q, ke, ve, causal)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    from tests.gpu_util import check_full
+    check_full(x, dtype, True, 0.125, o1.double().cpu().numpy(), l1.double().cpu().numpy(),
+               "head pairs")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_strided_bhtd_equals_contiguous(dtype):
     """[B, H, T, D] storage through fa_fwd_strided gives the same bits."""
