@@ -87,6 +87,13 @@ def test_head_pairs_equal_expanded(dtype, D, H, H_kv):
     from tests.gpu_util import check_full
     check_full(x, dtype, True, 0.125, o1.double().cpu().numpy(), l1.double().cpu().numpy(),
                "head pairs")
+    # [B, H, T, D] storage through fa_fwd_strided: the same bits
+    qh = q.transpose(1, 2).contiguous().transpose(1, 2)
+    kh = k.transpose(1, 2).contiguous().transpose(1, 2)
+    vh = v.transpose(1, 2).contiguous().transpose(1, 2)
+    o3, l3 = fa.fwd_strided(qh, kh, vh, causal=True, scale=0.125, out_layout="bhtd")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
