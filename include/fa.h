@@ -100,6 +100,12 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  * k, v and o (head-dim stride 1). Lets callers pass [B, H, T, D] storage or
  * other views without a copy. Strides must be >= 0 and multiples of 8 (bf16,
  * fp16) or 4 (fp32) elements.
+ * Both calls pick the work decomposition from the sizes: the key-range groups
+ * of fa_fwd_key_groups below and, with an even number of query heads per kv
+ * head and one key-range group (16-bit inputs), work-groups that take the
+ * same query tile of two query heads sharing a kv head and stage its K/V
+ * tiles once for both; every row's arithmetic, and so the result, is then
+ * unchanged bit for bit.
  */
 int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
                    int B, int H, int H_kv, int T, int D, int causal, float scale,
@@ -108,11 +114,6 @@ int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *
                    const long long o_strides[3], void *stream);
 
 /*
- * (fa_fwd, fa_fwd_strided: with an even number of query heads per kv head and
- * one key-range group, each work-group takes the same query tile of two query
- * heads that share a kv head and stages that head's K/V tiles once for both;
- * every row's arithmetic, and so the result, is unchanged bit for bit.)
- *
  * Key-range groups per query tile that fa_fwd and fa_fwd_strided use for these
  * sizes. 2 for bf16/fp16 with D >= 64 when the launch is small: its
  * B * H * ceil(T/128) query tiles are at most a quarter of the 4-wave
