@@ -1101,50 +1101,54 @@ long long split_bytes(long long slots, int nparts, int B, int H_kv, int D) {
 // dQ first: it also writes Delta and L2, which the dK/dV kernel reads. The
 // global-key sums go last, over the rows the dK/dV (or reduce) kernel wrote.
 template <typename E, int D, bool CAUSAL, bool WINDOW>
-void launch_bwd(const BwdParams &p, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams &p, hipStream_t s) {
     constexpr bool CAN_G2 = D >= 64 && !WINDOW;
+    hipError_t e;
     if (CAN_G2 && p.dq_groups == 2)
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW, CAN_G2>),
-                           dim3((unsigned)((long long)p.B * p.H * p.nblk * p.dq_parts)),
-                           dim3(2 * kThreads), 0, s, p);
+        e = launch_kernel((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW, CAN_G2>),
+                          dim3((unsigned)((long long)p.B * p.H * p.nblk * p.dq_parts)),
+                          dim3(2 * kThreads), s, p);
     else
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
-                           dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), 0, s,
-                           p);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW>),
-                       dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit + p.nfar)),
-                       dim3(kThreads), 0, s, p);
+        e = launch_kernel((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
+                          dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), s, p);
+    if (e != hipSuccess) return e;
+    e = launch_kernel((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW>),
+                      dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit + p.nfar)),
+                      dim3(kThreads), s, p);
+    if (e != hipSuccess) return e;
     if (p.hsplit > 1) {
         const long long n = (long long)p.B * p.T * p.H_kv * D;
-        hipLaunchKernelGGL((fa_bwd_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
-                           dim3(256), 0, s, p, n);
+        e = launch_kernel((fa_bwd_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
+                          dim3(256), s, p, n);
+        if (e != hipSuccess) return e;
     }
     if (p.dq_parts > 1) {
         const long long n = (long long)p.B * p.T * p.H * D;
-        hipLaunchKernelGGL((fa_bwd_dq_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
-                           dim3(256), 0, s, p, n);
+        e = launch_kernel((fa_bwd_dq_reduce_kernel<E>), dim3((unsigned)((n / 4 + 255) / 256)),
+                          dim3(256), s, p, n);
+        if (e != hipSuccess) return e;
     }
     if (WINDOW && p.nslots > 0) {
         const long long n = (long long)p.nslots * p.B * p.H_kv * (D / 4);
-        hipLaunchKernelGGL((fa_bwd_gsum_kernel<E>), dim3((unsigned)((n + 255) / 256)),
-                           dim3(256), 0, s, p, D);
+        e = launch_kernel((fa_bwd_gsum_kernel<E>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                          s, p, D);
     }
+    return e;
 }
 
 template <typename E, bool CAUSAL, bool WINDOW>
-void launch_bwd_d(const BwdParams &p, int D, hipStream_t s) {
+hipError_t launch_bwd_d(const BwdParams &p, int D, hipStream_t s) {
     switch (D) {
-        case 16: launch_bwd<E, 16, CAUSAL, WINDOW>(p, s); break;
-        case 32: launch_bwd<E, 32, CAUSAL, WINDOW>(p, s); break;
-        case 64: launch_bwd<E, 64, CAUSAL, WINDOW>(p, s); break;
-        default: launch_bwd<E, 128, CAUSAL, WINDOW>(p, s); break;
+        case 16: return launch_bwd<E, 16, CAUSAL, WINDOW>(p, s);
+        case 32: return launch_bwd<E, 32, CAUSAL, WINDOW>(p, s);
+        case 64: return launch_bwd<E, 64, CAUSAL, WINDOW>(p, s);
+        default: return launch_bwd<E, 128, CAUSAL, WINDOW>(p, s);
     }
 }
 
 template <typename E, bool WINDOW>
-void launch_bwd_c(const BwdParams &p, int D, int causal, hipStream_t s) {
-    if (causal) launch_bwd_d<E, true, WINDOW>(p, D, s);
-    else launch_bwd_d<E, false, WINDOW>(p, D, s);
+hipError_t launch_bwd_c(const BwdParams &p, int D, int causal, hipStream_t s) {
+    return causal ? launch_bwd_d<E, true, WINDOW>(p, D, s) : launch_bwd_d<E, false, WINDOW>(p, D, s);
 }
 
 }  // namespace
@@ -1268,14 +1272,14 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     }
     hipStream_t s = (hipStream_t)stream;
     const bool win = window >= 0;
-    if (dtype == FA_DTYPE_BF16) {
-        if (win) launch_bwd_c<__bf16, true>(p, D, causal, s);
-        else launch_bwd_c<__bf16, false>(p, D, causal, s);
-    } else {
-        if (win) launch_bwd_c<_Float16, true>(p, D, causal, s);
-        else launch_bwd_c<_Float16, false>(p, D, causal, s);
-    }
-    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    hipError_t le;
+    if (dtype == FA_DTYPE_BF16)
+        le = win ? launch_bwd_c<__bf16, true>(p, D, causal, s)
+                 : launch_bwd_c<__bf16, false>(p, D, causal, s);
+    else
+        le = win ? launch_bwd_c<_Float16, true>(p, D, causal, s)
+                 : launch_bwd_c<_Float16, false>(p, D, causal, s);
+    return le == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // namespace

@@ -162,4 +162,18 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
     }
 }
 
+// Host: launch `kern` on stream `s` and return the status of this launch alone.
+// The thread's last-error state is neither read nor cleared, so an error left
+// by an unrelated earlier HIP call is not reported as this launch's failure.
+template <typename T>
+struct Same {
+    typedef T type;
+};
+template <typename... P>
+hipError_t launch_kernel(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t s,
+                         typename Same<P>::type... args) {
+    void *argv[] = {(void *)&args...};
+    return hipLaunchKernel((const void *)kern, grid, block, argv, 0, s);
+}
+
 }  // namespace

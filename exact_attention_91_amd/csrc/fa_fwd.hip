@@ -813,39 +813,36 @@ long long extent(const long long s[3], int B, int T, int heads, int D) {
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 template <int D, bool CAUSAL, bool SPLIT, bool WINDOW>
-void launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
+hipError_t launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
     constexpr bool CAN_G2 = D >= 64 && !SPLIT && !WINDOW;
     constexpr bool CAN_HP = !SPLIT && !WINDOW;
     if (CAN_HP && p.hpair && dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>),
-                           grid, dim3(2 * kThreads), 0, stream, p);
+        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, dim3(2 * kThreads), stream, p);
     else if (CAN_HP && p.hpair && dtype == FA_DTYPE_F16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>),
-                           grid, dim3(2 * kThreads), 0, stream, p);
+        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, dim3(2 * kThreads), stream, p);
     else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid,
-                           dim3(2 * kThreads), 0, stream, p);
+        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid, dim3(2 * kThreads), stream, p);
     else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_F16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid,
-                           dim3(2 * kThreads), 0, stream, p);
+        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid, dim3(2 * kThreads), stream, p);
     else if (dtype == FA_DTYPE_BF16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>), grid,
-                           dim3(kThreads), 0, stream, p);
+        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>), grid, dim3(kThreads), stream, p);
     else if (dtype == FA_DTYPE_F16)
-        hipLaunchKernelGGL((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>), grid,
-                           dim3(kThreads), 0, stream, p);
+        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>), grid, dim3(kThreads), stream, p);
     else if (!SPLIT && !WINDOW)
-        hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), 0, stream, p);
+        return launch_kernel((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), stream, p);
+    return hipErrorInvalidValue;   // callers validate dtype first; not reached
 }
 
 template <bool CAUSAL, bool SPLIT, bool WINDOW = false>
-void launch_d(const FwdParams &p, int D, int dtype, dim3 grid, hipStream_t stream) {
+int launch_d(const FwdParams &p, int D, int dtype, dim3 grid, hipStream_t stream) {
+    hipError_t e;
     switch (D) {
-        case 16: launch<16, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
-        case 32: launch<32, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
-        case 64: launch<64, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
-        default: launch<128, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
+        case 16: e = launch<16, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
+        case 32: e = launch<32, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
+        case 64: e = launch<64, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
+        default: e = launch<128, CAUSAL, SPLIT, WINDOW>(p, dtype, grid, stream); break;
     }
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 // Validation shared by the entry points (no HIP calls) and the kernel
@@ -947,8 +944,9 @@ int launch_combine(const float *opart, const float *lpart, int n, int B, int H, 
     const long long blocks = (rows + per_block - 1) / per_block;
     if (blocks > kMaxGrid) return FA_ERR_OVERFLOW;
     const dim3 grid((unsigned)blocks);
+    hipError_t e;
 #define FA_COMBINE(E, DD) \
-    hipLaunchKernelGGL((fa_lse_combine_kernel<E, DD>), grid, dim3(256), 0, stream, c)
+    e = launch_kernel((fa_lse_combine_kernel<E, DD>), grid, dim3(256), stream, c)
 #define FA_COMBINE_D(E)                          \
     switch (D) {                                 \
         case 16: FA_COMBINE(E, 16); break;       \
@@ -965,7 +963,7 @@ int launch_combine(const float *opart, const float *lpart, int n, int B, int H, 
     }
 #undef FA_COMBINE_D
 #undef FA_COMBINE
-    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 // Two key-range groups per query tile (the G2 kernel) when the grid is small:
@@ -1004,11 +1002,8 @@ extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void 
     p.hpair = p.groups == 1 && dtype != FA_DTYPE_F32 && p.group % 2 == 0 ? 1 : 0;
     const dim3 grid((unsigned)(p.hpair ? units / 2 : units));
     hipStream_t s = (hipStream_t)stream;
-    if (causal)
-        launch_d<true, false>(p, D, dtype, grid, s);
-    else
-        launch_d<false, false>(p, D, dtype, grid, s);
-    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    return causal ? launch_d<true, false>(p, D, dtype, grid, s)
+                  : launch_d<false, false>(p, D, dtype, grid, s);
 }
 
 extern "C" int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
@@ -1057,11 +1052,9 @@ extern "C" int fa_fwd_splitk(const void *q, const void *k, const void *v, void *
     p.lpart = p.opart + rows * nsplit * D;
     const dim3 grid((unsigned)(units * nsplit));
     hipStream_t s = (hipStream_t)stream;
-    if (causal)
-        launch_d<true, true>(p, D, dtype, grid, s);
-    else
-        launch_d<false, true>(p, D, dtype, grid, s);
-    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    const int ls = causal ? launch_d<true, true>(p, D, dtype, grid, s)
+                          : launch_d<false, true>(p, D, dtype, grid, s);
+    if (ls != FA_OK) return ls;
     return launch_combine(p.opart, p.lpart, nsplit, B, H, T, D, o, qs, lse, dtype, s);
 }
 
@@ -1097,10 +1090,10 @@ extern "C" int fa_window_bitmap(const int *global_tokens, int n_global, int T, v
     const long long need = fa_window_bitmap_bytes(T);
     if (bits_bytes < need) return FA_ERR_WORKSPACE;
     const int nwords = (int)(need / 8);
-    hipLaunchKernelGGL(fa_global_bits_kernel, dim3((nwords + 255) / 256), dim3(256), 0,
-                       (hipStream_t)stream, global_tokens, n_global, T,
-                       (unsigned long long *)bits, nwords);
-    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    const hipError_t e = launch_kernel(fa_global_bits_kernel, dim3((nwords + 255) / 256),
+                                       dim3(256), (hipStream_t)stream, global_tokens, n_global,
+                                       T, (unsigned long long *)bits, nwords);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" int fa_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -1122,11 +1115,8 @@ extern "C" int fa_fwd_window(const void *q, const void *k, const void *v, void *
     p.gbits = (const unsigned long long *)global_bits;
     const dim3 grid((unsigned)((long long)p.nbh * p.nq));
     hipStream_t s = (hipStream_t)stream;
-    if (causal)
-        launch_d<true, false, true>(p, D, dtype, grid, s);
-    else
-        launch_d<false, false, true>(p, D, dtype, grid, s);
-    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    return causal ? launch_d<true, false, true>(p, D, dtype, grid, s)
+                  : launch_d<false, false, true>(p, D, dtype, grid, s);
 }
 
 extern "C" const char *fa_status_str(int status) {

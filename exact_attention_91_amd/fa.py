@@ -102,12 +102,29 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16, float16 or float32")
 
 
-def _check(q, k, v):
+def check_shapes(q, k, v):
+    """Raise ValueError unless q is [B, T, H, D] and k, v are both
+    [B, T, H_kv, D] with the same B, T and D (the sizes the library reads
+    from q alone). Runs before any device check, so it needs no GPU."""
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
         if t.dim() != 4:
             raise ValueError(f"{name} must be 4-D, got {tuple(t.shape)}")
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError(f"k and v must have one shape, got {tuple(k.shape)} and "
+                         f"{tuple(v.shape)}")
+    B, T, _, D = q.shape
+    if (k.shape[0], k.shape[1], k.shape[3]) != (B, T, D):
+        raise ValueError(f"k/v {tuple(k.shape)} must be [B, T, H_kv, D] with q's "
+                         f"B={B}, T={T}, D={D}")
+
+
+def _check(q, k, v):
+    check_shapes(q, k, v)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     if not (q.device == k.device == v.device):

@@ -10,6 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", n) for n in os.listdir(os.path.join(ROOT, "include"))
+                 if n.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -21,10 +23,13 @@ def lib():
     return fa._lib()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:\w+\s+)*\w+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+def _declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?(?:\w+\s+)*\w+\s*\*?\s*(fa_\w+)\s*\(",
+                                text, re.M))
+    return sorted(names)
 
 
 def _enum_values(name):
@@ -38,7 +43,9 @@ DT = _enum_values("fa_dtype_t")
 
 
 def test_header_declares_the_entry_points():
-    assert _declared_functions() == ["fa_bwd", "fa_bwd_window", "fa_bwd_window_workspace_bytes",
+    assert _declared_functions([os.path.join(ROOT, "include", "fa_roofs.h")]) == [
+        "fa_roof_copy", "fa_roof_mfma", "fa_roof_overlap", "fa_roof_valu"]
+    assert _declared_functions([HEADER]) == ["fa_bwd", "fa_bwd_window", "fa_bwd_window_workspace_bytes",
                                      "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_key_groups",
                                      "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
                                      "fa_fwd_strided", "fa_fwd_window", "fa_lse_combine",
@@ -456,3 +463,70 @@ def test_key_groups_rule(lib, B, H, T, D, dtype, expect):
                                   (1, 1, 10, 48, 1), (1, 1, 10, 64, 3), (1, 1, 10, 64, -1)])
 def test_key_groups_invalid(lib, args):
     assert lib.fa_fwd_key_groups(*args) == -1
+
+
+# The binding reads B, T and D from q alone, so k and v of another shape would
+# be read (and, in the backward, dk/dv written) past their allocations. Every
+# entry point must reject them before any device check or library call; CPU
+# tensors are enough to show the order.
+_BAD_KV = [
+    ((2, 64, 4, 32), (2, 64, 2, 32), (2, 64, 1, 32)),   # k and v differ in heads
+    ((2, 64, 4, 32), (1, 64, 2, 32), (1, 64, 2, 32)),   # batch
+    ((2, 64, 4, 32), (2, 63, 2, 32), (2, 63, 2, 32)),   # tokens
+    ((2, 64, 4, 32), (2, 64, 2, 16), (2, 64, 2, 16)),   # head dim
+    ((2, 64, 4, 32), (2, 64, 2, 32), (2, 65, 2, 32)),   # v alone longer
+    ((2, 64, 4, 32), (2, 64, 2, 32, 1), (2, 64, 2, 32)),  # k not 4-D
+]
+
+
+@pytest.mark.parametrize("qs,ks,vs", _BAD_KV)
+def test_binding_rejects_mismatched_kv(qs, ks, vs):
+    import torch
+    from exact_attention_91_amd import fa
+    q = torch.zeros(qs, dtype=torch.bfloat16)
+    k = torch.zeros(ks, dtype=torch.bfloat16)
+    v = torch.zeros(vs, dtype=torch.bfloat16)
+    o = torch.zeros(qs, dtype=torch.bfloat16)
+    lse = torch.zeros((qs[0], qs[2], qs[1]), dtype=torch.float32)
+    calls = [
+        lambda: fa.fwd(q, k, v, causal=True),
+        lambda: fa.fwd_strided(q, k, v, causal=True),
+        lambda: fa.fwd_splitk(q, k, v, causal=True, nsplit=2),
+        lambda: fa.fwd_window(q, k, v, 8, causal=True),
+        lambda: fa.bwd(q, k, v, o, lse, o, causal=True),
+        lambda: fa.bwd_window(q, k, v, o, lse, o, 8, causal=True),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="k/v|k and v|4-D"):
+            call()
+
+
+def test_binding_shape_check_accepts_grouped_heads():
+    import torch
+    from exact_attention_91_amd import fa
+    q = torch.zeros((2, 64, 4, 32))
+    kv = torch.zeros((2, 64, 2, 32))
+    fa.check_shapes(q, kv, kv)   # H_kv = 2 divides H = 4: the library checks the rest
+
+
+def test_roof_entry_points_reject_bad_arguments(lib):
+    """The microbenchmarks validate their arguments before any HIP call."""
+    _host_only()
+    VP, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    lib.fa_roof_mfma.argtypes = [I, I, VP, VP]
+    lib.fa_roof_valu.argtypes = [I, I, I, VP, VP]
+    lib.fa_roof_overlap.argtypes = [I, I, I, I, I, VP, VP]
+    lib.fa_roof_copy.argtypes = [VP, VP, LL, VP]
+    assert lib.fa_roof_mfma(0, 10, P, None) == 2
+    assert lib.fa_roof_mfma(4, 0, P, None) == 2
+    assert lib.fa_roof_mfma(4, 10, None, None) == 1
+    assert lib.fa_roof_valu(4, 10, 2, P, None) == 2
+    assert lib.fa_roof_valu(4, 10, 0, None, None) == 1
+    assert lib.fa_roof_overlap(4, 10, 10, 0, 0, P, None) == 2
+    assert lib.fa_roof_overlap(4, 10, 10, 0, 4, P, None) == 2
+    assert lib.fa_roof_overlap(4, 10, 10, 5, 3, P, None) == 2
+    assert lib.fa_roof_overlap(4, 10, 10, 1, 3, None, None) == 1
+    assert lib.fa_roof_copy(P, P, 0, None) == 2
+    assert lib.fa_roof_copy(None, P, 64, None) == 1
+    assert lib.fa_roof_copy(P, P, 40, None) == 7
+    assert lib.fa_roof_copy(P + 4, P, 64, None) == 7

@@ -67,7 +67,7 @@ def test_shared_kv_equals_expanded(dtype, H_kv):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("D,H,H_kv", [(64, 8, 2), (128, 12, 1), (32, 4, 2)])
+@pytest.mark.parametrize("D,H,H_kv", [(64, 8, 2), (128, 12, 1), (32, 4, 2), (16, 8, 2)])
 def test_head_pairs_equal_expanded(dtype, D, H, H_kv):
     """An even number of query heads per kv head and a launch with one key
     group: the library gives each work-group two query heads that read one set
