@@ -68,8 +68,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_device.h"
+
+// Scratch of fa_fwd_splitk_noalloc: the key-split partials live in this
+// fixed device array instead of a caller workspace. Every device the library
+// runs on holds its own copy for the life of the process; host code reaches it
+// only through the per-device address from hipGetSymbolAddress.
+constexpr long long kScratchBytes = 64LL << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -1022,10 +1031,40 @@ extern "C" long long fa_fwd_splitk_workspace_bytes(int B, int H, int T, int D, i
     return splitk_bytes(B, H, T, D, nsplit);
 }
 
-extern "C" int fa_fwd_splitk(const void *q, const void *k, const void *v, void *o, float *lse,
-                             int B, int H, int H_kv, int T, int D, int causal, float scale,
-                             int dtype, int nsplit, void *workspace, long long workspace_bytes,
-                             void *stream) {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // per device: address of `scratch`, once looked up
+
+// Device address of `scratch` on the device that owns `stream` (the current
+// device for the NULL stream), looked up with that device current the first
+// time and kept.
+int scratch_address(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return FA_ERR_LAUNCH;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return FA_ERR_LAUNCH;
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return FA_ERR_LAUNCH;
+        if (e != hipSuccess || !ptr) return FA_ERR_LAUNCH;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return FA_OK;
+}
+
+// fa_fwd_splitk with its partials in `workspace`, or, when use_scratch is set,
+// in the library's fixed scratch (workspace arguments ignored).
+int splitk_impl(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H,
+                int H_kv, int T, int D, int causal, float scale, int dtype, int nsplit,
+                void *workspace, long long workspace_bytes, void *stream, bool use_scratch) {
     long long qs[3], ks[3];
     contiguous_strides(T, H, D, qs);
     contiguous_strides(T, H_kv, D, ks);
@@ -1041,22 +1080,48 @@ extern "C" int fa_fwd_splitk(const void *q, const void *k, const void *v, void *
                               ks, qs, stream);
     const long long need = splitk_bytes(B, H, T, D, nsplit);
     if (need < 0) return FA_ERR_OVERFLOW;
-    if (!workspace) return FA_ERR_NULL_PTR;
-    if (workspace_bytes < need) return FA_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
     const long long units = (long long)p.nbh * p.nq;
     if (units * nsplit > kMaxGrid) return FA_ERR_OVERFLOW;
+    hipStream_t s = (hipStream_t)stream;
+    if (use_scratch) {
+        if (need > kScratchBytes) return FA_ERR_SCRATCH;
+        st = scratch_address(s, &workspace);
+        if (st != FA_OK) return st;
+    } else {
+        if (!workspace) return FA_ERR_NULL_PTR;
+        if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
+    }
     const long long rows = (long long)B * H * T;
     p.nsplit = nsplit;
     p.opart = (float *)workspace;
     p.lpart = p.opart + rows * nsplit * D;
     const dim3 grid((unsigned)(units * nsplit));
-    hipStream_t s = (hipStream_t)stream;
     const int ls = causal ? launch_d<true, true>(p, D, dtype, grid, s)
                           : launch_d<false, true>(p, D, dtype, grid, s);
     if (ls != FA_OK) return ls;
     return launch_combine(p.opart, p.lpart, nsplit, B, H, T, D, o, qs, lse, dtype, s);
 }
+
+}  // namespace
+
+extern "C" int fa_fwd_splitk(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int B, int H, int H_kv, int T, int D, int causal, float scale,
+                             int dtype, int nsplit, void *workspace, long long workspace_bytes,
+                             void *stream) {
+    return splitk_impl(q, k, v, o, lse, B, H, H_kv, T, D, causal, scale, dtype, nsplit,
+                       workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int fa_fwd_splitk_noalloc(const void *q, const void *k, const void *v, void *o,
+                                     float *lse, int B, int H, int H_kv, int T, int D,
+                                     int causal, float scale, int dtype, int nsplit,
+                                     void *stream) {
+    return splitk_impl(q, k, v, o, lse, B, H, H_kv, T, D, causal, scale, dtype, nsplit, nullptr,
+                       0, stream, true);
+}
+
+extern "C" long long fa_fwd_splitk_scratch_bytes(void) { return kScratchBytes; }
 
 extern "C" int fa_lse_combine(const float *o_parts, const float *lse_parts, int n, int B, int H,
                               int T, int D, void *o, float *lse, int dtype, void *stream) {
@@ -1136,6 +1201,9 @@ extern "C" const char *fa_status_str(int status) {
         case FA_ERR_STRIDE: return "negative stride";
         case FA_ERR_WORKSPACE:
             return "workspace smaller than fa_fwd_splitk_workspace_bytes() for these sizes";
+        case FA_ERR_SCRATCH:
+            return "sizes need more than the library's fixed scratch "
+                   "(fa_fwd_splitk_scratch_bytes()); call fa_fwd_splitk with a workspace";
         default: return "unknown status";
     }
 }

@@ -48,6 +48,11 @@ def _lib():
         lib.fa_fwd_splitk.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
                                       [ctypes.c_float, _I, _I, _VP, ctypes.c_longlong, _VP])
         lib.fa_fwd_splitk.restype = _I
+        lib.fa_fwd_splitk_noalloc.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
+                                              [ctypes.c_float, _I, _I, _VP])
+        lib.fa_fwd_splitk_noalloc.restype = _I
+        lib.fa_fwd_splitk_scratch_bytes.argtypes = []
+        lib.fa_fwd_splitk_scratch_bytes.restype = ctypes.c_longlong
         lib.fa_fwd_splitk_workspace_bytes.argtypes = [_I] * 5
         lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
@@ -229,6 +234,35 @@ def fwd_splitk(q, k, v, causal: bool = False, scale=None, nsplit: int = 2, works
                               float(scale), _dtype_code(q), int(nsplit),
                               workspace.data_ptr(), nbytes, stream)
     _raise(rc, "fa_fwd_splitk")
+    return o, lse
+
+
+def splitk_scratch_bytes() -> int:
+    """Bytes of the library's fixed scratch used by fwd_splitk_noalloc."""
+    return int(_lib().fa_fwd_splitk_scratch_bytes())
+
+
+def fwd_splitk_noalloc(q, k, v, causal: bool = False, scale=None, nsplit: int = 2):
+    """fwd_splitk without a workspace: the partials live in the library's fixed
+    device scratch (splitk_scratch_bytes()), so the library allocates nothing
+    (o and lse are still allocated here). Calls that overlap on one device
+    share that scratch and must be ordered on one stream. Returns (o, lse)."""
+    _check(q, k, v)
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"fwd_splitk_noalloc takes bfloat16 or float16 inputs, got {q.dtype}")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fwd_splitk_noalloc needs contiguous [B,T,H,D] tensors")
+    B, T, H, D = q.shape
+    H_kv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib().fa_fwd_splitk_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), B, H, H_kv, T, D, int(bool(causal)),
+                                      float(scale), _dtype_code(q), int(nsplit), stream)
+    _raise(rc, "fa_fwd_splitk_noalloc")
     return o, lse
 
 

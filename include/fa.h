@@ -43,7 +43,8 @@
  *
  * Execution. Work is enqueued on `stream` (a hipStream_t; NULL = the default
  * stream) and the call returns without synchronising. Inputs must stay valid
- * until that work completes. Calls are thread-safe (no mutable global state).
+ * until that work completes. Calls are thread-safe: the only global state is
+ * fa_fwd_splitk_noalloc's scratch (see there).
  *
  * Errors. Arguments are validated completely before any HIP call; on an
  * invalid argument nothing is launched and a nonzero fa_status_t is returned.
@@ -73,9 +74,13 @@ typedef enum {
                               aligned, or a stride not a multiple of 16 bytes  */
     FA_ERR_OVERFLOW = 8,   /* an element offset would exceed 2^62, or the grid
                               would exceed 2^24 - 1 work-groups                */
-    FA_ERR_LAUNCH = 9,     /* the HIP runtime rejected the kernel launch       */
+    FA_ERR_LAUNCH = 9,     /* the HIP runtime rejected the kernel launch (or,
+                              for fa_fwd_splitk_noalloc, the lookup of its
+                              scratch address failed)                          */
     FA_ERR_STRIDE = 10,    /* a negative stride                                */
-    FA_ERR_WORKSPACE = 11  /* split-K workspace smaller than required          */
+    FA_ERR_WORKSPACE = 11, /* split-K workspace smaller than required          */
+    FA_ERR_SCRATCH = 12    /* fa_fwd_splitk_noalloc: the partials would need
+                              more than fa_fwd_splitk_scratch_bytes()          */
 } fa_status_t;
 
 /*
@@ -154,6 +159,28 @@ int fa_fwd_splitk(const void *q, const void *k, const void *v, void *o, float *l
                   int B, int H, int H_kv, int T, int D, int causal, float scale,
                   int dtype, int nsplit, void *workspace, long long workspace_bytes,
                   void *stream);
+
+/*
+ * fa_fwd_splitk for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and the same result bit for bit, with the partials kept in a
+ * fixed scratch array inside the library instead of a caller workspace. The
+ * caller still passes inputs and outputs; nothing is allocated or freed.
+ * Limit: the partials, fa_fwd_splitk_workspace_bytes(B, H, T, D, nsplit)
+ * bytes, must fit in fa_fwd_splitk_scratch_bytes() (64 MiB), else
+ * FA_ERR_SCRATCH and nothing is launched. Every device keeps its own scratch
+ * for the life of the process (its address is looked up once per device, on
+ * the device of `stream`). All calls on one device share that scratch, which
+ * keeps the last call's partials: calls that overlap on one device (e.g. on
+ * two streams without ordering) race and give wrong results; order them on
+ * one stream. nsplit == 1 uses no scratch (it is fa_fwd).
+ */
+int fa_fwd_splitk_noalloc(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int H, int H_kv, int T, int D, int causal, float scale,
+                          int dtype, int nsplit, void *stream);
+
+/* Bytes of the fixed scratch of fa_fwd_splitk_noalloc (64 MiB). */
+long long fa_fwd_splitk_scratch_bytes(void);
 
 /*
  * Workspace bytes fa_fwd_splitk needs: nsplit * B * H * T * (D + 1) * 4

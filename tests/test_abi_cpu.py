@@ -47,7 +47,8 @@ def test_header_declares_the_entry_points():
         "fa_roof_copy", "fa_roof_mfma", "fa_roof_overlap", "fa_roof_valu"]
     assert _declared_functions([HEADER]) == ["fa_bwd", "fa_bwd_window", "fa_bwd_window_workspace_bytes",
                                      "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_key_groups",
-                                     "fa_fwd_splitk", "fa_fwd_splitk_workspace_bytes",
+                                     "fa_fwd_splitk", "fa_fwd_splitk_noalloc",
+                                     "fa_fwd_splitk_scratch_bytes", "fa_fwd_splitk_workspace_bytes",
                                      "fa_fwd_strided", "fa_fwd_window", "fa_lse_combine",
                                      "fa_status_str", "fa_version", "fa_window_bitmap",
                                      "fa_window_bitmap_bytes"]
@@ -530,3 +531,27 @@ def test_roof_entry_points_reject_bad_arguments(lib):
     assert lib.fa_roof_copy(None, P, 64, None) == 1
     assert lib.fa_roof_copy(P, P, 40, None) == 7
     assert lib.fa_roof_copy(P + 4, P, 64, None) == 7
+
+
+def test_splitk_noalloc_rejects_before_any_hip_call(lib):
+    """The allocation-free key split validates everything, including that its
+    partials fit the fixed scratch, before its first HIP call (the scratch
+    address lookup)."""
+    _host_only()
+    VP, I = ctypes.c_void_p, ctypes.c_int
+    lib.fa_fwd_splitk_noalloc.argtypes = [VP] * 5 + [I] * 6 + [ctypes.c_float, I, I, VP]
+    lib.fa_fwd_splitk_scratch_bytes.restype = ctypes.c_longlong
+    lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
+    assert lib.fa_fwd_splitk_scratch_bytes() == 64 << 20
+
+    def run(B=2, H=4, H_kv=2, T=1000, D=64, nsplit=4, dtype=DT["FA_DTYPE_BF16"], q=P):
+        return lib.fa_fwd_splitk_noalloc(q, P, P, P, P, B, H, H_kv, T, D, 1, 0.125, dtype,
+                                         nsplit, None)
+    assert run(nsplit=0) == ST["FA_ERR_BAD_SHAPE"]
+    assert run(dtype=DT["FA_DTYPE_F32"]) == ST["FA_ERR_DTYPE"]
+    assert run(q=None) == ST["FA_ERR_NULL_PTR"]
+    assert run(D=48) == ST["FA_ERR_HEAD_DIM"]
+    assert run(B=0) == ST["FA_OK"]          # empty call: nothing launched
+    big = dict(B=4, H=8, T=8192, D=128, nsplit=8)
+    assert lib.fa_fwd_splitk_workspace_bytes(4, 8, 8192, 128, 8) > 64 << 20
+    assert run(H_kv=8, **big) == ST["FA_ERR_SCRATCH"]
