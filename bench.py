@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOP/s and % of MFMA peak (GPT-2 causal bf16 shape)"
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X published dense MFMA, TFLOP/s
+HBM_PEAK_GBS = 8000.0                                     # MI355X published HBM3E bandwidth
 # the forward kernel's sources (its traffic figures are tied to their hash)
 KERNEL_SRCS = [os.path.join(ROOT, "exact_attention_91_amd", "csrc", n)
                for n in ("fa_fwd.hip", "fa_device.h")]
@@ -267,14 +268,30 @@ def main():
     groups = fa.key_groups(w.B, w.H, w.T, w.D, torch_dtype(w.dtype))
     # head pairs: an even number of query heads per kv head with one key group
     pairs = groups == 1 and (w.H // w.H_kv) % 2 == 0
-    roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
-            "frac": tflops / peak, "traffic": traffic_for(w.name),
-            "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
-                       f"{str(a.nsplit > 1).lower()}, false, "
-                       f"{str(a.nsplit == 1 and groups == 2).lower()}, "
-                       f"{str(a.nsplit == 1 and pairs).lower()}>"
-                       if w.dtype in _ELEM else
-                       f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")}
+    # Compulsory bytes: q, k, v, o once each in the element type, L in fp32.
+    esz = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
+    nbytes = esz * w.B * w.T * w.D * (2 * w.H + 2 * w.H_kv) + 4 * w.B * w.H * w.T
+    # The binding roof of the plain forward: the larger of the MFMA time
+    # (counted FLOP at the published dense peak) and the HBM time (compulsory
+    # bytes at 8 TB/s). The GPT-2 layer's intensity, 254 FLOP/B, lies below the
+    # ridge (2.5 PFLOP/s / 8 TB/s = 312), so there the binding roof is HBM.
+    hbm_bound = (a.which == "fwd" and w.window < 0 and a.nsplit == 1 and
+                 nbytes / HBM_PEAK_GBS / 1e9 > flops / (peak * 1e12))
+    if hbm_bound:
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s",
+                "frac": tflops / peak}
+    roof.update({"traffic": traffic_for(w.name),
+                 "mfma_tflops": tflops, "mfma_frac": tflops / peak,
+                 "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
+                            f"{str(a.nsplit > 1).lower()}, false, "
+                            f"{str(a.nsplit == 1 and groups == 2).lower()}, "
+                            f"{str(a.nsplit == 1 and pairs).lower()}>"
+                            if w.dtype in _ELEM else
+                            f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")})
     if w.window >= 0 and a.which == "fwd":
         roof["kernel"] = (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
                           f"false, true, false> (window)")
@@ -347,18 +364,28 @@ def main():
                   f"{f', nsplit={a.nsplit}' if a.nsplit > 1 else ''})")
     roofs = None
     if a.which == "fwd" and w.window < 0 and a.nsplit == 1:
-        # Times the step could not beat on each unit: the dense MFMA peak, HBM
-        # at 8 TB/s over the compulsory bytes (q, k, v, o once, L in fp32), and
-        # one v_exp_f32 per visible score at the measured issue rate of about
-        # 10.5 cycles per wave64 instruction (256 CUs x 4 SIMDs x 64 lanes at
-        # 2.4 GHz / 10.5 = 15.0e12 exp/s).
-        esz = {"f32": 4, "bf16": 2, "f16": 2}[w.dtype]
-        nbytes = esz * w.B * w.T * w.D * (2 * w.H + 2 * w.H_kv) + 4 * w.B * w.H * w.T
+        # Times the step could not beat on each unit, against the published
+        # peaks (dense MFMA, 8 TB/s HBM over the compulsory bytes) and against
+        # the rates the microbenchmarks of include/fa_roofs.h measured on this
+        # GPU model (profiles/roofs_mi355x.json): sustained bf16 MFMA, a
+        # device-memory copy, and v_exp_f32 with one exponential per visible
+        # score.
+        from exact_attention_91_amd import roofs as roofs_mod
+        meas = roofs_mod.load() or {}
         exps = w.B * w.H * (w.T * (w.T + 1) / 2 if causal else w.T * w.T)
-        t = {"mfma_us": flops / (peak * 1e12) * 1e6, "hbm_us": nbytes / 8e12 * 1e6,
-             "exp_us": exps / 15.0e12 * 1e6}
+        t = {"mfma_us": flops / (peak * 1e12) * 1e6, "hbm_us": nbytes / (HBM_PEAK_GBS * 1e9) * 1e6}
+        if meas.get("exp_per_s"):
+            t["exp_us"] = exps / meas["exp_per_s"] * 1e6
         roofs = dict(t, largest=max(t, key=t.get)[:-3], measured_us=ms * 1e3,
                      algorithmic_bytes=nbytes, exps=exps)
+        if w.dtype in ("bf16", "f16") and meas.get("mfma_bf16_tflops"):
+            roofs["measured_mfma_tflops"] = meas["mfma_bf16_tflops"]
+            roofs["frac_of_measured_mfma"] = tflops / meas["mfma_bf16_tflops"]
+        if meas.get("copy_gbps"):
+            roofs["measured_copy_gbps"] = meas["copy_gbps"]
+            roofs["frac_of_measured_copy"] = nbytes / (ms * 1e-3) / 1e9 / meas["copy_gbps"]
+        if meas:
+            roofs["measured_roofs_file"] = os.path.relpath(roofs_mod.ROOFS_FILE, ROOT)
     out = {
         "metric": metric, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,

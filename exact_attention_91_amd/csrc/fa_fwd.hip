@@ -83,7 +83,11 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 namespace {
 
 constexpr int kBQ = 128;        // query rows per work-group (32 per wave)
-constexpr float kMaxFloor = -1e30f;
+// Starting value of the running max: below every finite fp32 score, so only
+// rows with no visible key (all scores -inf) keep it. exp2(kMaxFloor - m) is 0
+// for any finite m above it, and exp2(-inf - kMaxFloor) is 0 for masked keys,
+// with no -inf - (-inf) anywhere.
+constexpr float kMaxFloor = -3.40282347e38f;
 
 struct FwdParams {
     const void *q, *k, *v;

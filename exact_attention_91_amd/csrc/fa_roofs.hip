@@ -79,11 +79,24 @@ __global__ __launch_bounds__(512) void roof_overlap_kernel(int n_mfma, int n_val
     }
 }
 
+// Four 16-byte vectors in flight per thread: all loads of a step are issued
+// before its stores. n16: 16-byte vectors in the buffer.
 __global__ __launch_bounds__(256) void roof_copy_kernel(const u32x4_t *src, u32x4_t *dst,
-                                                        long long n) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        dst[i] = src[i];
+                                                        long long n16) {
+    const long long nthreads = (long long)gridDim.x * blockDim.x;
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    long long i = t;
+    for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
+        const u32x4_t a = __builtin_nontemporal_load(src + i);
+        const u32x4_t b = __builtin_nontemporal_load(src + i + nthreads);
+        const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * nthreads);
+        const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * nthreads);
+        __builtin_nontemporal_store(a, dst + i);
+        __builtin_nontemporal_store(b, dst + i + nthreads);
+        __builtin_nontemporal_store(c, dst + i + 2 * nthreads);
+        __builtin_nontemporal_store(d, dst + i + 3 * nthreads);
+    }
+    for (; i < n16; i += nthreads) dst[i] = src[i];
 }
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : 9; }

@@ -31,6 +31,17 @@
  * nearest even. fp16 path: the same with IEEE half in place of bfloat16.
  * fp32 path: everything in fp32 (fp32 MFMA), no down-conversion.
  *
+ * Range. Inputs must be finite (NaN or Inf in q, k or v propagates). Every
+ * visible score must satisfy |scale * q.k| < 1.4e9 (|score * log2 e| < 2^31):
+ * the weights are exp2(fma(s, c, -m)) with c = |scale| log2 e and m the
+ * rounded running max of s*c, so all weights of a row share the factor
+ * 2^(m_exact - m), which cancels in O and L but overflows exp2 once the
+ * rounding error of m (half an ulp of s*c) exceeds 64. The raw products q.k
+ * are also accumulated in fp32, so max|q| * max|k| * D must stay below 3.4e38.
+ * Within the range any finite score is handled; the running max starts below
+ * every finite fp32 value. L is returned in fp32, so for |L| far above 1 its
+ * error is relative (a few ulp of L), not absolute.
+ *
  * Layout. Elements are addressed with element strides (batch, token, head);
  * the head-dim stride is 1.
  *   fa_fwd:         q, o contiguous [B, T, H, D]; k, v contiguous [B, T, H_kv, D]

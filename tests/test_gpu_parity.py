@@ -62,6 +62,50 @@ def test_scale_values(dtype, scale):
         check_full(x, dtype, causal, scale, o, lse, f"scale={scale} causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mag", [-1.0e9, 1.0e9])
+@pytest.mark.parametrize("two_level", [False, True])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (4, 1)])
+def test_scores_at_range_edge(dtype, mag, two_level, H, H_kv):
+    """Scaled scores of magnitude up to 1e9, the edge of the documented range
+    (|scale * q.k| < 1.4e9). At that size fp32 resolves scores only to ~64, so
+    the inputs avoid near ties: key rows are one vector (every score of a row
+    equal: uniform weights, O the (prefix) mean of V, L = s + ln n) or, with
+    two_level, alternate between that vector and 1 + 2^-7 times it (scores
+    differ by ~8e6: the larger level takes all the weight). The raw dot products
+    are accumulated in fp32 (relative error up to D * 2^-24 = 3.8e-6 for
+    D = 64) and L is stored in fp32, so L is judged against 1e-3 + 8e-6 |L|."""
+    from exact_attention_91_amd.inputs import Inputs, _round
+    B, T, D = 2, 300, 64
+    say(f"case range edge dtype={dtype} mag={mag} two_level={two_level} H={H} H_kv={H_kv}")
+    rng = np.random.default_rng(4243)
+    kappa = 64.0
+    a = rng.uniform(0.5, 1.0, size=(B, T, H, 1))
+    # score = 0.125 * D * q * kappa * level  ->  q = mag * a / (0.125 * D * kappa)
+    q = np.broadcast_to(a * mag / (0.125 * D * kappa), (B, T, H, D)).copy()
+    k = np.full((B, T, H_kv, D), kappa)
+    if two_level:
+        k[:, 1::2] *= 1.0 + 2.0 ** -7
+    v = rng.standard_normal((B, T, H_kv, D))
+    qt, q64 = _round(q, dtype)
+    kt, k64 = _round(k, dtype)
+    vt, v64 = _round(v, dtype)
+    scores = 0.125 * np.einsum("bthd,bshd->bhts", q64[:, :, :1], k64[:, :, :1])
+    assert np.max(np.abs(scores)) < 1.4e9
+    x = Inputs(q64, k64, v64, qt, kt, vt)
+    from oracle import oracle as orc
+    for causal in (False, True):
+        o, lse = run_gpu(x, causal, 0.125)
+        o_ref, l_ref = orc.attention(x.q64, x.k64, x.v64, causal, 0.125)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        eo = float(np.max(np.abs(o - o_ref)))
+        rel_l = float(np.max(np.abs(lse - l_ref) / (1e-3 + 8e-6 * np.abs(l_ref))))
+        say(f"  causal={causal} max|dO|={eo:.3e} max|dL|/(1e-3+8e-6|L|)={rel_l:.3e} "
+            f"L range [{l_ref.min():.3e}, {l_ref.max():.3e}]")
+        assert eo <= TOL[dtype][0]
+        assert rel_l <= 1.0
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_large_scores_rescaling(causal):
     """q, k ~ N(0, 4^2): scores of magnitude ~100 force many rescales."""
