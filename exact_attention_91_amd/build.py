@@ -46,5 +46,46 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """The library with its host code (argument validation, dispatch, the C
+    ABI) built with AddressSanitizer and UndefinedBehaviorSanitizer, for the CPU
+    sanitizer tests; device code is compiled as usual, without sanitizers (the
+    -fsanitize flags apply to the host pass only). Load it with the clang ASan
+    runtime preloaded (host_sanitizer_runtime())."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libfa_host_asan.so")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-g",
+           "-fno-omit-frame-pointer", "-shared-libsan"]
+    objs = [os.path.join(out_dir, os.path.basename(src) + ".o") for src in SRCS]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    procs = []
+    for src, obj in zip(SRCS, objs):
+        cmd = [HIPCC, *compile_flags, *san, "-I", os.path.join(ROOT, "include"), "-c", "-o", obj,
+               src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+    failed = [p.args for p in procs if p.wait() != 0]
+    if failed:
+        raise subprocess.CalledProcessError(1, failed[0])
+    subprocess.run([HIPCC, *FLAGS, *san, "-o", out, *objs], check=True)
+    return out
+
+
+def host_sanitizer_runtime() -> str:
+    """Path of the clang ASan runtime that build_host_sanitized() links against."""
+    res = subprocess.run([os.path.join(os.path.dirname(HIPCC), "..", "lib", "llvm", "bin", "clang"),
+                          "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True).stdout.strip()
+    if not os.path.isabs(res) or not os.path.exists(res):
+        import glob
+        found = glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        if not found:
+            raise FileNotFoundError("clang ASan runtime not found")
+        res = found[0]
+    return res
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -1010,14 +1010,14 @@ constexpr long long kMaxQueryParts = 8; // query-tile runs per key tile (library
 int head_parts(int B, int H, int H_kv, int T, int requested, bool window) {
     const int group = H / H_kv;
     if (requested > 0) return requested < group ? requested : group;
-    const long long nwg = (long long)B * H_kv * (((long long)T + kBlk - 1) / kBlk);
+    const long long nwg = mul_sat(mul_sat(B, H_kv), ((long long)T + kBlk - 1) / kBlk);
     if (nwg <= 0) return 1;
-    const long long want = (kTargetWG + nwg - 1) / nwg;
+    const long long want = nwg >= kTargetWG ? 1 : (kTargetWG + nwg - 1) / nwg;
     // one query head per kv head, key tiles for at most half the CUs and long
     // rows: split each key tile's query tiles instead (at most kMaxQueryParts
     // runs; shorter rows or more key tiles lose more to the parts' fp32
     // traffic than they gain)
-    if (!window && group == 1 && 2 * nwg <= kNumCUB && T >= 4096)
+    if (!window && group == 1 && nwg <= kNumCUB / 2 && T >= 4096)
         return (int)(want < kMaxQueryParts ? want : kMaxQueryParts);
     return (int)(want < group ? want : group);
 }
@@ -1056,10 +1056,10 @@ long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, int dqp,
 // quarter, or half with rows of >= 2048 keys (with all resident it was 5 %
 // slower).
 int dq_groups_for(int B, int H, int T, int D, bool window) {
-    const long long units = (long long)B * H * (((long long)T + kBlk - 1) / kBlk);
+    const long long units = mul_sat(mul_sat(B, H), ((long long)T + kBlk - 1) / kBlk);
     if (window || D < 64) return 1;
-    if (D == 64) return 4 * units <= 768 || (T >= 2048 && 2 * units <= 768) ? 2 : 1;
-    return 4 * units <= 512 || (T >= 2048 && units <= 512) ? 2 : 1;
+    if (D == 64) return units <= 768 / 4 || (T >= 2048 && units <= 768 / 2) ? 2 : 1;
+    return units <= 512 / 4 || (T >= 2048 && units <= 512) ? 2 : 1;
 }
 
 // Key parts of the two-group dQ kernel: with rows of >= 4096 keys and query
@@ -1067,8 +1067,8 @@ int dq_groups_for(int B, int H, int T, int D, bool window) {
 // to give each CU one work-group (at most 8).
 int dq_parts_for(int B, int H, int T, int D, bool window) {
     if (dq_groups_for(B, H, T, D, window) != 2 || T < 4096) return 1;
-    const long long units = (long long)B * H * (((long long)T + kBlk - 1) / kBlk);
-    if (units <= 0 || 2 * units > kNumCUB) return 1;
+    const long long units = mul_sat(mul_sat(B, H), ((long long)T + kBlk - 1) / kBlk);
+    if (units <= 0 || units > kNumCUB / 2) return 1;
     const long long n = kNumCUB / units;
     return (int)(n < 8 ? n : 8);
 }
@@ -1192,6 +1192,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
     if (!isfinite(scale) || !isfinite(scale * kLog2e)) return FA_ERR_SCALE;
     if (B == 0 || T == 0) return FA_OK;
+    if (T > (1 << 30)) return FA_ERR_OVERFLOW;   // 32-bit row arithmetic in the kernels
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
         return FA_ERR_NULL_PTR;
     const void *ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};

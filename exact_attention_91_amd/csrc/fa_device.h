@@ -162,6 +162,13 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
     }
 }
 
+// Host: a * b for non-negative sizes, saturating at LLONG_MAX instead of
+// overflowing (size heuristics compare the result with small thresholds).
+inline long long mul_sat(long long a, long long b) {
+    long long r;
+    return __builtin_mul_overflow(a, b, &r) ? __LONG_LONG_MAX__ : r;
+}
+
 // Host: launch `kern` on stream `s` and return the status of this launch alone.
 // The thread's last-error state is neither read nor cleared, so an error left
 // by an unrelated earlier HIP call is not reported as this launch's failure.

@@ -809,6 +809,7 @@ __global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int
 // Host side: validation (no HIP calls), dispatch, launch.
 // ---------------------------------------------------------------------------
 constexpr long long kMaxOffset = 1LL << 62;
+constexpr int kMaxT = (1 << 30);    // longest sequence accepted (32-bit row arithmetic)
 constexpr long long kNumCU = 256;   // MI355X compute units
 constexpr long long kMaxGrid = (1LL << 24) - 1;
 
@@ -902,7 +903,9 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
         (64 * 2 * (k_strides[1] > v_strides[1] ? k_strides[1] : v_strides[1]) + 2 * D >
          (1LL << 31) - 1))
         return FA_ERR_OVERFLOW;
-    const long long nq = (T + kBQ - 1) / kBQ;
+    // Kernels index rows and round T up to whole tiles in 32-bit ints.
+    if (T > kMaxT) return FA_ERR_OVERFLOW;
+    const long long nq = ((long long)T + kBQ - 1) / kBQ;
     const long long nbh = (long long)B * H;
     if (nbh > kMaxGrid || nbh * nq > kMaxGrid || nbh * T > kMaxOffset) return FA_ERR_OVERFLOW;
 
@@ -986,7 +989,7 @@ int launch_combine(const float *opart, const float *lpart, int n, int B, int H, 
 int key_groups(long long units, int T, int D, int dtype) {
     const long long slots = kNumCU * (D >= 128 ? 2 : 4);
     return dtype != FA_DTYPE_F32 && D >= 64 &&
-                   (4 * units <= slots || (T >= 2048 && units <= slots))
+                   (units <= slots / 4 || (T >= 2048 && units <= slots))
                ? 2
                : 1;
 }
@@ -997,7 +1000,7 @@ extern "C" int fa_fwd_key_groups(int B, int H, int T, int D, int dtype) {
     if (B < 0 || H < 1 || T < 0 || (D != 16 && D != 32 && D != 64 && D != 128) ||
         (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16))
         return -1;
-    return key_groups((long long)B * H * ((T + kBQ - 1) / kBQ), T, D, dtype);
+    return key_groups(mul_sat(mul_sat(B, H), ((long long)T + kBQ - 1) / kBQ), T, D, dtype);
 }
 
 extern "C" int fa_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -1200,7 +1203,8 @@ extern "C" const char *fa_status_str(int status) {
         case FA_ERR_ALIGN:
             return "misaligned: q/k/v/o need 16-byte alignment and 16-byte-multiple strides, "
                    "lse 4-byte alignment";
-        case FA_ERR_OVERFLOW: return "size overflow: offsets beyond 2^62 or grid beyond 2^24-1";
+        case FA_ERR_OVERFLOW:
+            return "size overflow: offsets beyond 2^62, grid beyond 2^24-1 or T beyond 2^30";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_STRIDE: return "negative stride";
         case FA_ERR_WORKSPACE:

@@ -83,8 +83,8 @@ typedef enum {
     FA_ERR_SCALE = 6,      /* scale is NaN or infinite                         */
     FA_ERR_ALIGN = 7,      /* q/k/v/o not 16-byte aligned, lse not 4-byte
                               aligned, or a stride not a multiple of 16 bytes  */
-    FA_ERR_OVERFLOW = 8,   /* an element offset would exceed 2^62, or the grid
-                              would exceed 2^24 - 1 work-groups                */
+    FA_ERR_OVERFLOW = 8,   /* an element offset would exceed 2^62, the grid
+                              would exceed 2^24 - 1 work-groups, or T > 2^30   */
     FA_ERR_LAUNCH = 9,     /* the HIP runtime rejected the kernel launch (or,
                               for fa_fwd_splitk_noalloc, the lookup of its
                               scratch address failed)                          */

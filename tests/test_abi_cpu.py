@@ -555,3 +555,21 @@ def test_splitk_noalloc_rejects_before_any_hip_call(lib):
     big = dict(B=4, H=8, T=8192, D=128, nsplit=8)
     assert lib.fa_fwd_splitk_workspace_bytes(4, 8, 8192, 128, 8) > 64 << 20
     assert run(H_kv=8, **big) == ST["FA_ERR_SCRATCH"]
+
+
+def test_size_heuristics_saturate(lib):
+    """The kernel-variant choice for absurd sizes: the unit count saturates
+    instead of overflowing (found by the UndefinedBehaviorSanitizer leg)."""
+    lib.fa_fwd_key_groups.argtypes = [ctypes.c_int] * 5
+    assert lib.fa_fwd_key_groups(1 << 30, 1 << 30, 1 << 30, 64, DT["FA_DTYPE_BF16"]) == 1
+    assert lib.fa_fwd_key_groups((1 << 31) - 1, (1 << 31) - 1, (1 << 31) - 1, 128,
+                                 DT["FA_DTYPE_F16"]) == 1
+    lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 6
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
+    assert lib.fa_bwd_workspace_bytes((1 << 31) - 1, (1 << 31) - 1, 1, (1 << 31) - 1, 128, 0) == -1
+
+
+def test_sequence_length_limit(lib):
+    """T above 2^30 is rejected (the kernels use 32-bit row arithmetic)."""
+    _host_only()
+    assert call(lib, B=1, H=1, H_kv=1, T=(1 << 30) + 1) == ST["FA_ERR_OVERFLOW"]
