@@ -93,6 +93,9 @@ def _lib():
             [_DP, _DP, _DP, _DP, ctypes.POINTER(ctypes.c_int64), ctypes.c_longlong, _DP] +
             [ctypes.c_int] * 5 + [ctypes.c_int, ctypes.c_double])
         lib.oracle_attn_bwd_dq_rows_f64.restype = ctypes.c_int
+        lib.oracle_attn_decode_f64.argtypes = (common + [_DP, _DP] + [ctypes.c_int] * 6 +
+                                               [ctypes.c_int, ctypes.c_double])
+        lib.oracle_attn_decode_f64.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -140,6 +143,25 @@ def attention(q, k, v, causal: bool, scale: float):
                                 B, H, H_kv, T, D, int(bool(causal)), float(scale))
     if rc:
         raise RuntimeError(f"oracle_attn_f64 failed ({rc})")
+    return o, lse
+
+
+def attention_decode(q, k, v, causal: bool, scale: float):
+    """T_q query rows (the last T_q positions) against T_k keys: q [B, T_q, H, D],
+    k, v [B, T_k, H_kv, D]. Returns (o [B, T_q, H, D], lse [B, H, T_q])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4 or k.shape != v.shape:
+        raise ValueError("q [B, T_q, H, D] and k, v [B, T_k, H_kv, D] expected")
+    B, Tq, H, D = q.shape
+    Tk, H_kv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or H % H_kv:
+        raise ValueError(f"k/v shape {k.shape} does not match q {q.shape}")
+    o = np.empty((B, Tq, H, D), np.float64)
+    lse = np.empty((B, H, Tq), np.float64)
+    rc = _lib().oracle_attn_decode_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       B, H, H_kv, Tq, Tk, D, int(bool(causal)), float(scale))
+    if rc:
+        raise RuntimeError(f"oracle_attn_decode_f64 failed ({rc})")
     return o, lse
 
 

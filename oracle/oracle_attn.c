@@ -58,6 +58,16 @@
  * window contains the row itself, i.e. never for window >= 0) gets O = 0,
  * L = -inf.
  *
+ * oracle_attn_decode_f64 is the definition for T_q query rows against T_k
+ * keys and values (a key/value cache), the decoding case that "Flash
+ * Attention Memory Optimization Explained", "Why It Matters", names
+ * (FlashDecoding for inference). The query rows are the last T_q positions of
+ * the T_k-long sequence: query i sits at position T_k - T_q + i, and under the
+ * causal mask sees keys j <= T_k - T_q + i ("因果掩碼的高效實現": key position
+ * <= query position). A row with no visible key (possible when T_q > T_k)
+ * gets O = 0, L = -inf. Layout: q, o [B, T_q, H, D]; k, v [B, T_k, H_kv, D];
+ * lse [B, H, T_q]. With T_q = T_k it is oracle_attn_f64.
+ *
  * oracle_attn_bwd_f64 is the gradient of that definition, for a loss whose
  * gradient with respect to O is dO (L is treated as an auxiliary output that
  * the loss does not use). "Flash Attention Memory Optimization Explained",
@@ -576,6 +586,67 @@ int oracle_attn_bwd_dq_rows_f64(const double *q, const double *k, const double *
         }
         free(p);
         free(dp);
+    }
+    return fail ? -2 : 0;
+}
+
+/* Decode-shaped attention: T_q query rows at positions T_k - T_q + i against
+ * T_k keys. Returns 0, -1 on bad shape, -2 on no memory. */
+int oracle_attn_decode_f64(const double *q, const double *k, const double *v, double *o,
+                           double *lse, int B, int H, int H_kv, int Tq, int Tk, int D,
+                           int causal, double scale) {
+    if (B < 1 || H < 1 || H_kv < 1 || Tq < 1 || Tk < 1 || D < 1 || (H % H_kv) != 0) return -1;
+    const int group = H / H_kv;
+    const long long nrows = (long long)B * H * Tq;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)Tk);
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(dynamic, 16)
+        for (long long r = 0; r < nrows; ++r) {
+            if (!s) continue;
+            const int i = (int)(r % Tq);
+            const int h = (int)((r / Tq) % H);
+            const int b = (int)(r / ((long long)Tq * H));
+            const int g = h / group;
+            /* keys 0 .. last are visible */
+            long long last = causal ? (long long)Tk - Tq + i : (long long)Tk - 1;
+            if (last > Tk - 1) last = Tk - 1;
+            double *orow = o + qidx(b, i, h, H, Tq, D);
+            double *lrow = lse + ((size_t)b * H + h) * Tq + i;
+            if (last < 0) {
+                for (int d = 0; d < D; ++d) orow[d] = 0.0;
+                *lrow = -INFINITY;
+                continue;
+            }
+            const int nvis = (int)last + 1;
+            const double *qi = q + qidx(b, i, h, H, Tq, D);
+            double m = -INFINITY;
+            for (int j = 0; j < nvis; ++j) {
+                const double *kj = k + qidx(b, j, g, H_kv, Tk, D);
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) dot += qi[d] * kj[d];
+                s[j] = scale * dot;
+                if (s[j] > m) m = s[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j < nvis; ++j) {
+                s[j] = exp(s[j] - m);
+                z += s[j];
+            }
+            for (int d = 0; d < D; ++d) orow[d] = 0.0;
+            for (int j = 0; j < nvis; ++j) {
+                const double w = s[j] / z;
+                const double *vj = v + qidx(b, j, g, H_kv, Tk, D);
+                for (int d = 0; d < D; ++d) orow[d] += w * vj[d];
+            }
+            *lrow = m + log(z);
+        }
+        free(s);
     }
     return fail ? -2 : 0;
 }

@@ -40,7 +40,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
     if not os.path.exists(asan):
         pytest.skip("gcc's libasan is not installed")
     out = _run_child(asan, "-", lib, ["test_oracle_pins.py", "test_oracle_mask_pins.py",
-                                      "test_oracle_bwd_pins.py"])
+                                      "test_oracle_bwd_pins.py", "test_oracle_decode_pins.py"])
     assert " passed" in out
 
 
