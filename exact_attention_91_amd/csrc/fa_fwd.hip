@@ -118,6 +118,12 @@ struct FwdParams {
     // kv head), the two heads' groups reading one set of staged K/V tiles (the
     // HP kernel); 0: one head per work-group.
     int hpair;
+    // Decode mode (the DECODE kernel): Tq query rows, the last Tq positions of
+    // the T-long key sequence (query i sits at position T - Tq + i). The rows
+    // of the group query heads sharing kv head g are packed, r = hh * Tq + i
+    // (head h = g * group + hh), R = group * Tq of them per (batch, kv head);
+    // nq counts 128-row tiles of those packed rows.
+    int Tq, R;
 };
 
 template <bool B>
@@ -153,7 +159,8 @@ __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
 // layout of fa_device.h: K is read as rows (kswz), V transposed for the V^T
 // operand of P.V (vswz).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW, bool G2, bool HP = false>
+template <typename E, int D, bool CAUSAL, bool SPLIT, bool WINDOW, bool G2, bool HP = false,
+          bool DECODE = false>
 __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_half_kernel(FwdParams p) {
     using L = Bf16Layout<D>;
     using H16 = Half16<E>;
@@ -166,6 +173,7 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
 
     static_assert(!G2 || (!SPLIT && !WINDOW && D >= 32), "G2: plain forward, D >= 32");
     static_assert(!HP || (!G2 && !SPLIT && !WINDOW), "HP: plain forward");
+    static_assert(!DECODE || (SPLIT && !G2 && !HP && !WINDOW), "DECODE: key-split partials");
     // Two K/V buffers as four distinct LDS variables: the accesses of each loop
     // step name their buffers statically, so the compiler knows the copies into
     // one buffer never alias the operand reads of the other and does not make
@@ -206,11 +214,33 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         u.g = u.h / p.group;
         u.q0 = (p.nq - 1 - t) * kBQ;
         u.s = 0;
+    } else if (DECODE) {
+        // work-group = (packed row tile, batch, kv head, split)
+        int id = blockIdx.x;
+        u.s = id % p.nsplit;
+        id /= p.nsplit;
+        const int nbg = p.B * p.H_kv;
+        const int t = id / nbg;
+        const int bg = id - t * nbg;
+        u.b = bg / p.H_kv;
+        u.g = bg - u.b * p.H_kv;
+        u.h = u.g * p.group;
+        u.q0 = t * kBQ;
     } else {
         u = unit_of(p);
     }
     const int wq0 = u.q0 + wave * 32;       // first query row of this wave
-    const int qrow = wq0 + col;             // this lane's query row
+    const int qrow = wq0 + col;             // this lane's query row (decode: packed row)
+    // Decode: this lane's query head and position among the Tq rows, and the
+    // last key position its row sees under the causal mask.
+    int dh = u.h, di = qrow, dlast = qrow;
+    if (DECODE) {
+        const int hh = qrow / p.Tq;
+        di = qrow - hh * p.Tq;
+        dh = u.g * p.group + hh;
+        dlast = T - p.Tq + di;
+    }
+    const bool row_live = DECODE ? qrow < p.R : qrow < T;
 
     const unsigned short *kbase =
         (const unsigned short *)p.k + u.b * p.ks[0] + u.g * p.ks[2];
@@ -223,17 +253,17 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     e8_t qf[KS];
     {
         const unsigned short *qr = (const unsigned short *)p.q + u.b * p.qs[0] +
-                                   u.h * p.qs[2] + (long long)qrow * p.qs[1] + 8 * half;
+                                   dh * p.qs[2] + (long long)di * p.qs[1] + 8 * half;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4_t x = {0u, 0u, 0u, 0u};
-            if (qrow < T) x = *(const u32x4_t *)(qr + 16 * ks);
+            if (row_live) x = *(const u32x4_t *)(qr + 16 * ks);
             x ^= p.qsign;
             qf[ks] = __builtin_bit_cast(e8_t, x);
         }
     }
 
-    const int kend = CAUSAL ? min(T, u.q0 + kBQ) : T;
+    const int kend = CAUSAL && !DECODE ? min(T, u.q0 + kBQ) : T;
     const int nkt = (kend + BK - 1) / BK;
     // Key tiles of this work-group: all of them, or split u.s's share; with G2,
     // group 0 takes the first ghalf of them and group 1 the rest.
@@ -304,7 +334,7 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     // slowly than one with three VGPR operands.
     float c;
     asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
-    const bool wave_live = wq0 < T;
+    const bool wave_live = DECODE ? wq0 < p.R : wq0 < T;
 
     auto tile = [&](bool need_mask, int j, const unsigned char *kt, const unsigned char *vt,
                     unsigned long long gb) {
@@ -323,7 +353,7 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
 
         // Element r of block kb is key key0 + 32kb + 8(r/4) + 4half + r%4.
         if (need_mask) {
-            const int lim = (CAUSAL ? min(qrow, T - 1) : T - 1) - key0 - 4 * half;
+            const int lim = (CAUSAL ? min(dlast, T - 1) : T - 1) - key0 - 4 * half;
             if (WINDOW) {
                 // in the band: lo <= off <= hi; global: bit (off + 4half) of gb
                 const int lo = qrow - p.window - key0 - 4 * half;
@@ -418,8 +448,9 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         if (jn < jend)
             stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jn * BK, swave, koff, voff, kn, vn);
         const int key0 = j * BK;
-        bool active = wave_live && (!CAUSAL || key0 <= wq0 + 31) && (!G2 || j < jend);
-        bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > wq0);
+        // (decode: every row sees keys up to at least T - Tq, and some row up to T - 1)
+        bool active = wave_live && (!CAUSAL || DECODE || key0 <= wq0 + 31) && (!G2 || j < jend);
+        bool need_mask = (key0 + BK > T) || (CAUSAL && key0 + BK - 1 > (DECODE ? T - p.Tq : wq0));
         if (WINDOW) {
             // the band of this wave's 32 rows: [wq0 - window, wq0 + 31 + window]
             const long long wlo = (long long)wq0 - p.window, whi = (long long)wq0 + 31 + p.window;
@@ -507,12 +538,13 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
 
     if (!wave_live) return;
     const float lt = half_swap_sum(lsum);
-    if (qrow >= T) return;
+    if (!row_live) return;
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
     const float lse_row = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     if (SPLIT) {
         // Partial result over this split's keys, normalised by its own l.
-        const long long row = (((long long)u.s * p.B + u.b) * p.H + u.h) * T + qrow;
+        const long long row = DECODE ? (((long long)u.s * p.B + u.b) * p.H + dh) * p.Tq + di
+                                     : (((long long)u.s * p.B + u.b) * p.H + u.h) * T + qrow;
         float *orow = p.opart + row * D;
 #pragma unroll
         for (int n = 0; n < ND; ++n)
@@ -830,21 +862,43 @@ template <int D, bool CAUSAL, bool SPLIT, bool WINDOW>
 hipError_t launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
     constexpr bool CAN_G2 = D >= 64 && !SPLIT && !WINDOW;
     constexpr bool CAN_HP = !SPLIT && !WINDOW;
+    const dim3 b4(kThreads), b8(2 * kThreads);
     if (CAN_HP && p.hpair && dtype == FA_DTYPE_BF16)
-        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, dim3(2 * kThreads), stream, p);
+        return launch_kernel(
+            (fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, b8,
+            stream, p);
     else if (CAN_HP && p.hpair && dtype == FA_DTYPE_F16)
-        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, dim3(2 * kThreads), stream, p);
+        return launch_kernel(
+            (fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, b8,
+            stream, p);
     else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_BF16)
-        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid, dim3(2 * kThreads), stream, p);
+        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid,
+                             b8, stream, p);
     else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_F16)
-        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid, dim3(2 * kThreads), stream, p);
+        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>),
+                             grid, b8, stream, p);
     else if (dtype == FA_DTYPE_BF16)
-        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>), grid, dim3(kThreads), stream, p);
+        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>), grid,
+                             b4, stream, p);
     else if (dtype == FA_DTYPE_F16)
-        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>), grid, dim3(kThreads), stream, p);
+        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>),
+                             grid, b4, stream, p);
     else if (!SPLIT && !WINDOW)
-        return launch_kernel((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(kThreads), stream, p);
+        return launch_kernel((fa_fwd_f32_kernel<D, CAUSAL>), grid, b4, stream, p);
     return hipErrorInvalidValue;   // callers validate dtype first; not reached
+}
+
+// The decode kernel: packed query rows of the heads sharing a kv head, key
+// split into parts whose partials fa_lse_combine_kernel merges.
+template <int D, bool CAUSAL>
+hipError_t launch_decode(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
+    if (dtype == FA_DTYPE_BF16)
+        return launch_kernel(
+            (fa_fwd_half_kernel<__bf16, D, CAUSAL, true, false, false, false, true>), grid,
+            dim3(kThreads), stream, p);
+    return launch_kernel(
+        (fa_fwd_half_kernel<_Float16, D, CAUSAL, true, false, false, false, true>), grid,
+        dim3(kThreads), stream, p);
 }
 
 template <bool CAUSAL, bool SPLIT, bool WINDOW = false>
@@ -929,6 +983,8 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
     p.gbits = nullptr;
     p.groups = 1;
     p.hpair = 0;
+    p.Tq = T;
+    p.R = 0;
     return FA_OK;
 }
 
@@ -1129,6 +1185,81 @@ extern "C" int fa_fwd_splitk_noalloc(const void *q, const void *k, const void *v
 }
 
 extern "C" long long fa_fwd_splitk_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" long long fa_fwd_decode_workspace_bytes(int B, int H, int Tq, int D, int nsplit) {
+    if (B < 0 || H < 1 || Tq < 0 || nsplit < 1 || (D != 16 && D != 32 && D != 64 && D != 128))
+        return -1;
+    return splitk_bytes(B, H, Tq, D, nsplit);
+}
+
+extern "C" int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                             int B, int H, int H_kv, int Tq, int Tk, int D, int causal,
+                             float scale, int dtype, int nsplit, void *workspace,
+                             long long workspace_bytes, void *stream) {
+    if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_DTYPE;
+    if (B < 0 || Tq < 0 || Tk < 1 || H < 1 || H_kv < 1 || nsplit < 1) return FA_ERR_BAD_SHAPE;
+    if (H % H_kv != 0) return FA_ERR_HEADS;
+    if (D != 16 && D != 32 && D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
+    const float c = fabsf(scale) * kLog2e;
+    if (!isfinite(c)) return FA_ERR_SCALE;
+    if (B == 0 || Tq == 0) return FA_OK;
+    if (Tq > kMaxT || Tk > kMaxT) return FA_ERR_OVERFLOW;
+    if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL_PTR;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(workspace, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    long long qs[3], ks[3];
+    contiguous_strides(Tq, H, D, qs);
+    contiguous_strides(Tk, H_kv, D, ks);
+    const long long eq = extent(qs, B, Tq, H, D), ek = extent(ks, B, Tk, H_kv, D);
+    if (eq < 0 || ek < 0 || eq > kMaxOffset || ek > kMaxOffset) return FA_ERR_OVERFLOW;
+    const long long rows = (long long)(H / H_kv) * Tq;     // packed rows per (batch, kv head)
+    if (rows > kMaxT) return FA_ERR_OVERFLOW;
+    const long long nq = (rows + kBQ - 1) / kBQ;
+    const long long units = mul_sat(mul_sat(B, H_kv), nq);
+    if (units > kMaxGrid || units * nsplit > kMaxGrid) return FA_ERR_OVERFLOW;
+    const long long need = splitk_bytes(B, H, Tq, D, nsplit);
+    if (need < 0) return FA_ERR_OVERFLOW;
+    if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+    FwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    for (int j = 0; j < 3; ++j) {
+        p.qs[j] = qs[j]; p.os[j] = qs[j];
+        p.ks[j] = ks[j]; p.vs[j] = ks[j];
+    }
+    p.B = B; p.H = H; p.H_kv = H_kv; p.T = Tk;
+    p.group = H / H_kv;
+    p.nq = (int)nq;
+    p.nbh = (int)mul_sat(B, H);
+    p.c = c > 0.f ? c : 1.17549435e-38f;
+    p.qsign = scale < 0.f ? 0x80008000u : 0u;
+    p.nsplit = nsplit;
+    p.opart = (float *)workspace;
+    p.lpart = p.opart + (long long)B * H * Tq * nsplit * D;
+    p.window = 0;
+    p.gbits = nullptr;
+    p.groups = 1;
+    p.hpair = 0;
+    p.Tq = Tq;
+    p.R = (int)rows;
+    const dim3 grid((unsigned)(units * nsplit));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    switch (D) {
+        case 16: e = causal ? launch_decode<16, true>(p, dtype, grid, s)
+                            : launch_decode<16, false>(p, dtype, grid, s); break;
+        case 32: e = causal ? launch_decode<32, true>(p, dtype, grid, s)
+                            : launch_decode<32, false>(p, dtype, grid, s); break;
+        case 64: e = causal ? launch_decode<64, true>(p, dtype, grid, s)
+                            : launch_decode<64, false>(p, dtype, grid, s); break;
+        default: e = causal ? launch_decode<128, true>(p, dtype, grid, s)
+                            : launch_decode<128, false>(p, dtype, grid, s); break;
+    }
+    if (e != hipSuccess) return FA_ERR_LAUNCH;
+    return launch_combine(p.opart, p.lpart, nsplit, B, H, Tq, D, o, qs, lse, dtype, s);
+}
 
 extern "C" int fa_lse_combine(const float *o_parts, const float *lse_parts, int n, int B, int H,
                               int T, int D, void *o, float *lse, int dtype, void *stream) {

@@ -53,6 +53,11 @@ def _lib():
         lib.fa_fwd_splitk_noalloc.restype = _I
         lib.fa_fwd_splitk_scratch_bytes.argtypes = []
         lib.fa_fwd_splitk_scratch_bytes.restype = ctypes.c_longlong
+        lib.fa_fwd_decode.argtypes = ([_VP] * 5 + [_I] * 7 + [ctypes.c_float, _I, _I, _VP,
+                                                              ctypes.c_longlong, _VP])
+        lib.fa_fwd_decode.restype = _I
+        lib.fa_fwd_decode_workspace_bytes.argtypes = [_I] * 5
+        lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_fwd_splitk_workspace_bytes.argtypes = [_I] * 5
         lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
         lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
@@ -263,6 +268,61 @@ def fwd_splitk_noalloc(q, k, v, causal: bool = False, scale=None, nsplit: int = 
                                       lse.data_ptr(), B, H, H_kv, T, D, int(bool(causal)),
                                       float(scale), _dtype_code(q), int(nsplit), stream)
     _raise(rc, "fa_fwd_splitk_noalloc")
+    return o, lse
+
+
+def decode_workspace_bytes(B: int, H: int, T_q: int, D: int, nsplit: int) -> int:
+    """Bytes of device workspace fwd_decode needs (-1 for invalid sizes)."""
+    return int(_lib().fa_fwd_decode_workspace_bytes(B, H, T_q, D, nsplit))
+
+
+def decode_splits(B: int, H_kv: int, H: int, T_q: int, T_k: int) -> int:
+    """A key split for fwd_decode: enough parts that the launch has about two
+    work-groups per compute unit, each part at least 256 keys, at most 64."""
+    units = B * H_kv * -(-(H // H_kv) * T_q // 128)
+    want = max(1, -(-512 // max(units, 1)))
+    return int(max(1, min(want, T_k // 256, 64)))
+
+
+def fwd_decode(q, k, v, causal: bool = True, scale=None, nsplit=None, workspace=None):
+    """Decode-shaped attention forward (bfloat16 or float16, contiguous):
+    q [B, T_q, H, D] holds the last T_q positions of a sequence whose keys and
+    values are k, v [B, T_k, H_kv, D] (a key/value cache); under the causal
+    mask query i sees keys j <= T_k - T_q + i. The keys are split into `nsplit`
+    ranges (decode_splits(...) when None) merged by their logsumexps.
+    Returns (o [B, T_q, H, D], lse [B, H, T_q] float32)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D torch tensor")
+    if tuple(k.shape) != tuple(v.shape):
+        raise ValueError(f"k and v must have one shape, got {tuple(k.shape)} and "
+                         f"{tuple(v.shape)}")
+    B, T_q, H, D = q.shape
+    T_k, H_kv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k/v {tuple(k.shape)} must be [B, T_k, H_kv, D] with q's B={B}, D={D}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("fwd_decode takes bfloat16 or float16 q, k, v of one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("fwd_decode needs contiguous tensors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if nsplit is None:
+        nsplit = decode_splits(B, H_kv, H, T_q, T_k)
+    need = decode_workspace_bytes(B, H, T_q, D, nsplit)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T_q), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = _lib().fa_fwd_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, H_kv, T_q, T_k, D, int(bool(causal)),
+                              float(scale), _dtype_code(q), int(nsplit), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), stream)
+    _raise(rc, "fa_fwd_decode")
     return o, lse
 
 

@@ -194,6 +194,37 @@ int fa_fwd_splitk_noalloc(const void *q, const void *k, const void *v, void *o, 
 long long fa_fwd_splitk_scratch_bytes(void);
 
 /*
+ * Decode-shaped forward: T_q query rows against a T_k-long key/value cache
+ * (bf16 or fp16, contiguous). The query rows are the last T_q positions of the
+ * sequence, so query i sits at position T_k - T_q + i and, when causal, sees
+ * keys j <= T_k - T_q + i ("因果掩碼的高效實現", yelogs.com Flash
+ * Attention2-in-Triton article: key position <= query position); a row that
+ * sees no key (T_q > T_k) gets O = 0, L = -inf. This is the inference case
+ * "Flash Attention Memory Optimization Explained", "Why It Matters", names
+ * (FlashDecoding): few query rows, a long cache. The rows of the H / H_kv
+ * query heads sharing a kv head are processed together, so each key/value
+ * tile is read once per (batch, kv head, key part), not once per query head;
+ * the keys are split into nsplit contiguous ranges of 64-key tiles whose
+ * partial results are merged by their logsumexps as in fa_fwd_splitk.
+ *   q, o  [B, T_q, H, D]     k, v [B, T_k, H_kv, D]     lse [B, H, T_q] fp32
+ *   T_q >= 0 (0: nothing to do), T_k >= 1, nsplit >= 1; workspace: caller's
+ *   device memory, 16-byte aligned, at least
+ *   fa_fwd_decode_workspace_bytes(B, H, T_q, D, nsplit) bytes (scratch; calls
+ *   sharing it must be ordered on one stream). Same range and precision as
+ *   fa_fwd_splitk. Two kernels on `stream`. Returns an fa_status_t
+ *   (FA_ERR_DTYPE for fp32, FA_ERR_BAD_SHAPE for T_k < 1 or nsplit < 1,
+ *   FA_ERR_WORKSPACE for a workspace too small).
+ */
+int fa_fwd_decode(const void *q, const void *k, const void *v, void *o, float *lse,
+                  int B, int H, int H_kv, int T_q, int T_k, int D, int causal, float scale,
+                  int dtype, int nsplit, void *workspace, long long workspace_bytes,
+                  void *stream);
+
+/* Workspace bytes fa_fwd_decode needs: nsplit * B * H * T_q * (D + 1) * 4;
+ * -1 for invalid sizes or overflow. */
+long long fa_fwd_decode_workspace_bytes(int B, int H, int T_q, int D, int nsplit);
+
+/*
  * Workspace bytes fa_fwd_splitk needs: nsplit * B * H * T * (D + 1) * 4
  * (fp32 partial outputs, then fp32 partial logsumexps); -1 for invalid sizes
  * or overflow.

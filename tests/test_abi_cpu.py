@@ -46,7 +46,7 @@ def test_header_declares_the_entry_points():
     assert _declared_functions([os.path.join(ROOT, "include", "fa_roofs.h")]) == [
         "fa_roof_copy", "fa_roof_mfma", "fa_roof_overlap", "fa_roof_valu"]
     assert _declared_functions([HEADER]) == ["fa_bwd", "fa_bwd_window", "fa_bwd_window_workspace_bytes",
-                                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_key_groups",
+                                     "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes", "fa_fwd_key_groups",
                                      "fa_fwd_splitk", "fa_fwd_splitk_noalloc",
                                      "fa_fwd_splitk_scratch_bytes", "fa_fwd_splitk_workspace_bytes",
                                      "fa_fwd_strided", "fa_fwd_window", "fa_lse_combine",
@@ -573,3 +573,32 @@ def test_sequence_length_limit(lib):
     """T above 2^30 is rejected (the kernels use 32-bit row arithmetic)."""
     _host_only()
     assert call(lib, B=1, H=1, H_kv=1, T=(1 << 30) + 1) == ST["FA_ERR_OVERFLOW"]
+
+
+def test_decode_rejects_and_workspace(lib):
+    """fa_fwd_decode validates before any HIP call; its workspace size."""
+    _host_only()
+    VP, I = ctypes.c_void_p, ctypes.c_int
+    lib.fa_fwd_decode.argtypes = [VP] * 5 + [I] * 7 + [ctypes.c_float, I, I, VP,
+                                                        ctypes.c_longlong, VP]
+    lib.fa_fwd_decode_workspace_bytes.argtypes = [I] * 5
+    lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_longlong
+    ws = lib.fa_fwd_decode_workspace_bytes
+    assert ws(2, 8, 3, 64, 4) == 4 * 2 * 8 * 3 * 65 * 4
+    assert ws(2, 8, 3, 48, 4) == -1 and ws(2, 8, 3, 64, 0) == -1 and ws(-1, 8, 3, 64, 1) == -1
+
+    def run(B=2, H=8, H_kv=2, Tq=3, Tk=500, D=64, dtype=DT["FA_DTYPE_BF16"], nsplit=4,
+            wsb=1 << 20, q=P, scale=0.125):
+        return lib.fa_fwd_decode(q, P, P, P, P, B, H, H_kv, Tq, Tk, D, 1, scale, dtype, nsplit,
+                                 P, wsb, None)
+    assert run(dtype=DT["FA_DTYPE_F32"]) == ST["FA_ERR_DTYPE"]
+    assert run(Tk=0) == ST["FA_ERR_BAD_SHAPE"]
+    assert run(nsplit=0) == ST["FA_ERR_BAD_SHAPE"]
+    assert run(H_kv=3) == ST["FA_ERR_HEADS"]
+    assert run(D=48) == ST["FA_ERR_HEAD_DIM"]
+    assert run(scale=float("inf")) == ST["FA_ERR_SCALE"]
+    assert run(q=None) == ST["FA_ERR_NULL_PTR"]
+    assert run(q=P + 8) == ST["FA_ERR_ALIGN"]
+    assert run(wsb=100) == ST["FA_ERR_WORKSPACE"]
+    assert run(Tq=(1 << 30) + 1) == ST["FA_ERR_OVERFLOW"]
+    assert run(B=0) == ST["FA_OK"] and run(Tq=0) == ST["FA_OK"]
