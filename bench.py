@@ -45,9 +45,13 @@ def parse():
     # to settle; shorter warm-ups time the ramp, not the kernel.
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="gpt2")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd",
                     help="bwd: time fa_bwd (gradients for a seeded dO, from the "
-                         "forward's o and lse computed once before timing)")
+                         "forward's o and lse computed once before timing); decode: time "
+                         "fa_fwd_decode on --decode-shape (the workload is not used)")
+    ap.add_argument("--decode-shape", default="16,32,8,1,8192,128",
+                    help="B,H,H_kv,T_q,T_k,D of the decode step (default: a 32-head "
+                         "layer with 8 kv heads, one new token, an 8192-token cache)")
     ap.add_argument("--head-split", type=int, default=0,
                     help="bwd: query-head parts of the dK/dV kernel (0: library choice)")
     ap.add_argument("--nsplit", type=int, default=1,
@@ -124,6 +128,66 @@ def traffic_for(workload_name):
     return t.get("bytes_per_launch")
 
 
+def bench_decode(a):
+    """One decode step per call: fa_fwd_decode (split kernel + combine) on
+    seeded bf16 inputs, library split choice. The kernel is bound by reading
+    the key/value cache once, so the roofline is HBM: compulsory bytes (q, k,
+    v, o once, lse fp32) over the time per step."""
+    import numpy as np
+    import torch
+    from exact_attention_91_amd import fa
+    B, H, H_kv, Tq, Tk, D = (int(x) for x in a.decode_shape.split(","))
+    torch.cuda.set_device(0)
+    rng = np.random.default_rng(2024)
+    mk = lambda *sh: torch.from_numpy(rng.standard_normal(sh).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    q, k, v = mk(B, Tq, H, D), mk(B, Tk, H_kv, D), mk(B, Tk, H_kv, D)
+    nsplit = fa.decode_splits(B, H_kv, H, Tq, Tk)
+    nbytes = fa.decode_workspace_bytes(B, H, Tq, D, nsplit)
+    ws = torch.empty((nbytes,), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device="cuda")
+    lib = fa._lib()
+    stream = torch.cuda.current_stream()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv,
+            Tq, Tk, D, 1, D ** -0.5, fa.FA_DTYPE_BF16, nsplit, ws.data_ptr(), nbytes,
+            stream.cuda_stream)
+
+    def step():
+        rc = lib.fa_fwd_decode(*args)
+        if rc:
+            raise RuntimeError(fa.status_str(rc))
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    comp = 2 * (B * Tq * H * D * 2) + 2 * (B * Tk * H_kv * D * 2) + 4 * B * H * Tq
+    gbs = comp / (ms * 1e-3) / 1e9
+    vis = sum(min(Tk, Tk - Tq + i + 1) for i in range(Tq))
+    flops = 4.0 * B * H * D * vis
+    out = {"metric": f"attention decode GB/s and % of HBM peak (B={B} H={H} H_kv={H_kv} "
+                     f"T_q={Tq} T_k={Tk} D={D})",
+           "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"decode: B={B} H={H} H_kv={H_kv} T_q={Tq} T_k={Tk} D={D} "
+                                  f"bf16 causal, nsplit={nsplit}",
+                      "pass": "decode", "nsplit": nsplit, "parallelism": "single GPU"},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                        "kernel": "fa_fwd_half_kernel<__bf16, ..., DECODE> + "
+                                  "fa_lse_combine_kernel (rate over the step)"},
+           "tflops": flops / (ms * 1e-3) / 1e12, "algorithmic_bytes": comp,
+           "cpu_baseline": None, "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,6 +195,9 @@ def main():
               "by batch/head with no exchange, and multi-GPU runs are not part of "
               "this build. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if a.which == "decode":
+        return bench_decode(a)
 
     import numpy as np
     import torch

@@ -99,6 +99,26 @@ __global__ __launch_bounds__(256) void roof_copy_kernel(const u32x4_t *src, u32x
     for (; i < n16; i += nthreads) dst[i] = src[i];
 }
 
+// Reads n16 16-byte vectors, eight in flight per thread, and folds them into
+// one word per thread (stored only if it matches an impossible pattern).
+__global__ __launch_bounds__(256) void roof_read_kernel(const u32x4_t *src, long long n16,
+                                                        float *sink) {
+    const long long nthreads = (long long)gridDim.x * blockDim.x;
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    long long i = t;
+    for (; i + 7 * nthreads < n16; i += 8 * nthreads) {
+        u32x4_t x[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(src + i + r * nthreads);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) acc ^= x[r];
+    }
+    for (; i < n16; i += nthreads) acc ^= src[i];
+    const unsigned w = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (w == 0x9e3779b9u && t == 0) sink[blockIdx.x] = 1.f;
+}
+
 int status(hipError_t e) { return e == hipSuccess ? 0 : 9; }
 
 }  // namespace
@@ -133,6 +153,14 @@ extern "C" int fa_roof_overlap(int grid_blocks, int n_mfma, int n_valu, int op, 
                                       dim3(512), s, n_mfma, n_valu, mask, sink)
                       : launch_kernel(roof_overlap_kernel<FA_ROOF_FMA>, dim3(grid_blocks),
                                       dim3(512), s, n_mfma, n_valu, mask, sink));
+}
+
+extern "C" int fa_roof_read(const void *src, long long bytes, float *sink, void *stream) {
+    if (bytes < 16) return 2;
+    if (!src || !sink) return 1;
+    if (bytes % 16 != 0 || (uintptr_t)src % 16 != 0) return 7;
+    return status(launch_kernel(roof_read_kernel, dim3(256 * 8), dim3(256), (hipStream_t)stream,
+                                (const u32x4_t *)src, bytes / 16, sink));
 }
 
 extern "C" int fa_roof_copy(const void *src, void *dst, long long bytes, void *stream) {

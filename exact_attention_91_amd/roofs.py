@@ -34,7 +34,9 @@ def _lib():
         lib.fa_roof_valu.argtypes = [_I, _I, _I, _VP, _VP]
         lib.fa_roof_overlap.argtypes = [_I, _I, _I, _I, _I, _VP, _VP]
         lib.fa_roof_copy.argtypes = [_VP, _VP, _LL, _VP]
-        for f in (lib.fa_roof_mfma, lib.fa_roof_valu, lib.fa_roof_overlap, lib.fa_roof_copy):
+        lib.fa_roof_read.argtypes = [_VP, _LL, _VP, _VP]
+        for f in (lib.fa_roof_mfma, lib.fa_roof_valu, lib.fa_roof_overlap, lib.fa_roof_copy,
+                  lib.fa_roof_read):
             f.restype = _I
         lib._roofs_typed = True
     return lib
@@ -111,7 +113,13 @@ def measure(copy_mib: int = 1024):
     out["copy_bytes"] = nbytes
     out["copy_gbps"] = 2 * nbytes / (ms * 1e-3) / 1e9   # read + write
     out["copy_ms"] = ms
-    del src, dst
+    del dst
+    big = torch.zeros(2048, dtype=torch.float32, device="cuda")
+    ms = _time(lambda: _check(lib.fa_roof_read(src.data_ptr(), nbytes, big.data_ptr(), sp),
+                              "fa_roof_read"))
+    out["read_gbps"] = nbytes / (ms * 1e-3) / 1e9
+    out["read_ms"] = ms
+    del src
     out["device"] = torch.cuda.get_device_name(0)
     return out
 

@@ -24,11 +24,13 @@
  *                  kind `op` when mask bit 1 is set. Comparing the time with
  *                  both bits against each alone shows the overlap.
  *   fa_roof_copy:  reads and writes `bytes` bytes (16-byte vectors).
+ *   fa_roof_read:  reads `bytes` bytes (16-byte vectors, eight in flight per
+ *                  thread); sink needs 2048 elements (one per work-group).
  * sink: device float array of at least grid_blocks elements (written, holds
  * nothing useful; it keeps the arithmetic from being optimised away).
  * Returns 0 on success, 9 (FA_ERR_LAUNCH) if the runtime rejects a launch,
  * 2 for a non-positive size or count, 1 for a NULL pointer, 7 for a pointer
- * or size not a multiple of 16 bytes (copy).
+ * or size not a multiple of 16 bytes (copy, read).
  */
 #ifndef FA_ROOFS_H_
 #define FA_ROOFS_H_
@@ -44,6 +46,7 @@ int fa_roof_valu(int grid_blocks, int n_iter, int op, float *sink, void *stream)
 int fa_roof_overlap(int grid_blocks, int n_mfma, int n_valu, int op, int mask, float *sink,
                     void *stream);
 int fa_roof_copy(const void *src, void *dst, long long bytes, void *stream);
+int fa_roof_read(const void *src, long long bytes, float *sink, void *stream);
 
 #ifdef __cplusplus
 }

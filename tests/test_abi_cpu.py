@@ -44,7 +44,7 @@ DT = _enum_values("fa_dtype_t")
 
 def test_header_declares_the_entry_points():
     assert _declared_functions([os.path.join(ROOT, "include", "fa_roofs.h")]) == [
-        "fa_roof_copy", "fa_roof_mfma", "fa_roof_overlap", "fa_roof_valu"]
+        "fa_roof_copy", "fa_roof_mfma", "fa_roof_overlap", "fa_roof_read", "fa_roof_valu"]
     assert _declared_functions([HEADER]) == ["fa_bwd", "fa_bwd_window", "fa_bwd_window_workspace_bytes",
                                      "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_decode", "fa_fwd_decode_workspace_bytes", "fa_fwd_key_groups",
                                      "fa_fwd_splitk", "fa_fwd_splitk_noalloc",
@@ -531,6 +531,11 @@ def test_roof_entry_points_reject_bad_arguments(lib):
     assert lib.fa_roof_copy(None, P, 64, None) == 1
     assert lib.fa_roof_copy(P, P, 40, None) == 7
     assert lib.fa_roof_copy(P + 4, P, 64, None) == 7
+    lib.fa_roof_read.argtypes = [VP, LL, VP, VP]
+    assert lib.fa_roof_read(P, 0, P, None) == 2
+    assert lib.fa_roof_read(None, 64, P, None) == 1
+    assert lib.fa_roof_read(P, 64, None, None) == 1
+    assert lib.fa_roof_read(P, 40, P, None) == 7
 
 
 def test_splitk_noalloc_rejects_before_any_hip_call(lib):
