@@ -96,6 +96,8 @@ struct Bf16Layout {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));   // the builtin's type
@@ -158,6 +160,29 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
                                                      koff[i], 0, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + idx * 1024), 16,
                                                      voff[i], 0, 0, 0);
+        }
+    }
+}
+
+// Issue this wave's share (of NW waves) of the global->LDS copy of `rows`
+// (1..64) rows of D 16-bit elements, `stride` elements apart, into one tile in
+// the K layout (chunk c of row r at c ^ kswz(r)); rows past `rows` read as zeros.
+template <int D, int NW = 4>
+__device__ __forceinline__ void stage_rows(const unsigned short *base, long long stride, int rows,
+                                           int wave, unsigned char *dst) {
+    using L = Bf16Layout<D>;
+    const int lane = threadIdx.x & 63;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned short *>(base), (short)0, ((rows - 1) * (int)stride + D) * 2,
+        kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < (L::NLOAD + NW - 1) / NW; ++i) {
+        const int idx = wave + NW * i;
+        if (L::NLOAD % NW == 0 || idx < L::NLOAD) {
+            const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
+            const int off = row * (int)stride * 2 + 16 * ((lane % L::C) ^ L::kswz(row));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + idx * 1024), 16, off,
+                                                     0, 0, 0);
         }
     }
 }

@@ -39,6 +39,12 @@
 //    memory into LDS (buffer loads to LDS) with XOR-permuted 16-byte chunks;
 //    the fp32 kernel stages through registers into padded rows. Either way
 //    the MFMA operand reads are bank-conflict free.
+//  * The plain forward (one key group, one head per work-group, unsplit)
+//    moves q and O through LDS: the work-group's 128 q rows arrive with the
+//    first K/V tile as whole-row buffer loads into the idle second buffer and
+//    are read out as MFMA operands; each wave writes its O rows into the
+//    buffer the last tile did not use and stores them as whole rows, 16 bytes
+//    per lane, instead of 8-byte pieces of 32 rows per instruction.
 //  * The scale is applied to fp32 scores (folded with log2 e into one FMA
 //    before exp2); q is never rescaled in its input precision. A negative scale
 //    flips q's sign bits in registers (exact) so the kernel always sees c > 0.
@@ -68,6 +74,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "fa.h"
@@ -250,8 +257,14 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
 
     // Q fragment = B operand of S^T = K Q^T: lane (col, half) holds
     // q[qrow, 16*ks + 8*half + 0..7].
+    // The plain forward (one head, one key group, unsplit) moves q and O
+    // through LDS: q rows arrive with the first K/V tile as whole-row buffer
+    // loads into the second K/V buffer and are read from there as MFMA operands;
+    // O rows leave from the buffer the last tile did not use as whole-row
+    // 16-byte stores. The other variants load q and store O from registers.
+    constexpr bool QO = !G2 && !HP && !SPLIT && !WINDOW && !DECODE;
     e8_t qf[KS];
-    {
+    if (!QO) {
         const unsigned short *qr = (const unsigned short *)p.q + u.b * p.qs[0] +
                                    dh * p.qs[2] + (long long)di * p.qs[1] + 8 * half;
 #pragma unroll
@@ -490,8 +503,36 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
                 step(jbeg + i + 1, 0ull, jbeg + i + 2, k_lds1, v_lds1, k_lds0, v_lds0);
         }
     } else {
+        if (QO) {
+            // q rows q0..q0+63 into k_lds1, q0+64..q0+127 into v_lds1, in the K
+            // tile layout (rows past T arrive as zeros)
+            const unsigned short *qb =
+                (const unsigned short *)p.q + u.b * p.qs[0] + u.h * p.qs[2];
+            const long long qs1 = p.qs[1];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int r0 = u.q0 + 64 * hb;
+                if (r0 < T)
+                    stage_rows<D, NW>(qb + (long long)r0 * qs1, qs1, min(T - r0, 64), swave,
+                                      hb ? v_lds1 : k_lds1);
+            }
+        }
         if (jbeg < jend)
             stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jbeg * BK, swave, koff, voff, k_lds0, v_lds0);
+        if (QO) {
+            // Every wave's q rows have landed after this barrier. The first step's
+            // wait and barrier then order these reads before tile jbeg + 1 is
+            // copied over them.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const unsigned char *qt = (wave < 2 ? k_lds1 : v_lds1) + (wave & 1) * 32 * L::ROWB;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4_t x = __builtin_bit_cast(u32x4_t, *(const lds_bf16x8_t *)(qt + kaddr[ks]));
+                x ^= p.qsign;
+                qf[ks] = __builtin_bit_cast(e8_t, x);
+            }
+        }
         for (int j = jbeg; j < jend; j += 2) {
             step(j, 0ull, j + 1, k_lds0, v_lds0, k_lds1, v_lds1);
             if (j + 1 < jend) step(j + 1, 0ull, j + 2, k_lds1, v_lds1, k_lds0, v_lds0);
@@ -538,7 +579,7 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
 
     if (!wave_live) return;
     const float lt = half_swap_sum(lsum);
-    if (!row_live) return;
+    if (!QO && !row_live) return;   // QO: every lane takes part in the LDS transpose
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
     const float lse_row = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     if (SPLIT) {
@@ -559,6 +600,42 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
                 }
             }
         if (half == 0) p.lpart[row] = lse_row;
+        return;
+    }
+    if (QO) {
+        // The buffer pair that did not hold the last tile is free: its last reads
+        // (tile jend - 2) and copies ended before the last step's barrier. Wave w
+        // writes its 32 rows (row = col) there, 16-byte chunk c of a row at
+        // c ^ oswz(row), then reads them back a row-contiguous 16 bytes per lane.
+        constexpr int C = L::C;
+        auto oswz = [](int r) { return (r >> 1) & (C - 1); };
+        const bool last_in0 = ((jend - 1 - jbeg) & 1) == 0;
+        unsigned char *ob = (last_in0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
+                            (wave & 1) * 32 * L::ROWB;
+#pragma unroll
+        for (int n = 0; n < ND; ++n)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d = 32 * n + 8 * rg + 4 * half;
+                if (D >= 32 || d < D) {
+                    e4_t o4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[n][4 * rg + e] * inv);
+                    *(lds_u32x2_t *)(ob + col * L::ROWB + 16 * ((d >> 3) ^ oswz(col)) + 8 * half) =
+                        __builtin_bit_cast(u32x2_t, o4);
+                }
+            }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        unsigned short *obase = (unsigned short *)p.o + u.b * p.os[0] + u.h * p.os[2];
+#pragma unroll
+        for (int i = 0; i < C / 2; ++i) {
+            const int r = i * (64 / C) + lane / C;
+            const int c = lane % C;
+            const u32x4_t x = *(const lds_u32x4_t *)(ob + r * L::ROWB + 16 * (c ^ oswz(r)));
+            if (wq0 + r < T) *(u32x4_t *)(obase + (long long)(wq0 + r) * p.os[1] + 8 * c) = x;
+        }
+        if (half == 0 && row_live) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
         return;
     }
     unsigned short *orow = (unsigned short *)p.o + u.b * p.os[0] + (long long)qrow * p.os[1] +
@@ -952,11 +1029,11 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
     if (eq < 0 || eo < 0 || ek < 0 || ev < 0 || eq > kMaxOffset || eo > kMaxOffset ||
         ek > kMaxOffset || ev > kMaxOffset)
         return FA_ERR_OVERFLOW;
-    // The 16-bit kernel addresses one 64-key tile with 32-bit byte offsets.
-    if (half16 &&
-        (64 * 2 * (k_strides[1] > v_strides[1] ? k_strides[1] : v_strides[1]) + 2 * D >
-         (1LL << 31) - 1))
-        return FA_ERR_OVERFLOW;
+    // The 16-bit kernel addresses 64 rows of q, k or v with 32-bit byte offsets.
+    if (half16) {
+        const long long s1 = std::max(q_strides[1], std::max(k_strides[1], v_strides[1]));
+        if (64 * 2 * s1 + 2 * D > (1LL << 31) - 1) return FA_ERR_OVERFLOW;
+    }
     // Kernels index rows and round T up to whole tiles in 32-bit ints.
     if (T > kMaxT) return FA_ERR_OVERFLOW;
     const long long nq = ((long long)T + kBQ - 1) / kBQ;

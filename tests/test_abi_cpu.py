@@ -162,6 +162,11 @@ def test_strided_rejects(lib):
     assert call_strided(lib, **huge) == ST["FA_ERR_OVERFLOW"]
     wrap = dict(base, os_=((1 << 62) + 8, 4 * 64, 64))
     assert call_strided(lib, **wrap) == ST["FA_ERR_OVERFLOW"]
+    # 64 rows of q (or k, v) at this row stride span more than 2 GiB: the
+    # kernel's 32-bit tile offsets would wrap
+    for key in ("qs", "ks"):
+        far = dict(base, **{key: (100 << 24, 1 << 24, 64)})
+        assert call_strided(lib, **far) == ST["FA_ERR_OVERFLOW"]
     from exact_attention_91_amd.fa import _LL3
     _host_only()
     rc = lib.fa_fwd_strided(P, P, P, P, P, 2, 4, 2, 100, 64, 0, 0.125, 1,
