@@ -130,6 +130,7 @@ struct Half16<_Float16> {
     }
 };
 constexpr unsigned kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit dwords (gfx9 family)
+constexpr int kCachePolicyNT = 2;              // buffer instruction cache policy: nt (gfx950)
 
 
 // Issue this wave's share (of NW waves) of the global->LDS copies of two
@@ -167,6 +168,8 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
 // Issue this wave's share (of NW waves) of the global->LDS copy of `rows`
 // (1..64) rows of D 16-bit elements, `stride` elements apart, into one tile in
 // the K layout (chunk c of row r at c ^ kswz(r)); rows past `rows` read as zeros.
+// The rows are read once, so the loads are non-temporal (cache policy nt):
+// they do not displace the K/V tiles other work-groups re-read from L2.
 template <int D, int NW = 4>
 __device__ __forceinline__ void stage_rows(const unsigned short *base, long long stride, int rows,
                                            int wave, unsigned char *dst) {
@@ -182,7 +185,7 @@ __device__ __forceinline__ void stage_rows(const unsigned short *base, long long
             const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
             const int off = row * (int)stride * 2 + 16 * ((lane % L::C) ^ L::kswz(row));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + idx * 1024), 16, off,
-                                                     0, 0, 0);
+                                                     0, 0, kCachePolicyNT);
         }
     }
 }

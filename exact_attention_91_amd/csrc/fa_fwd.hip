@@ -44,7 +44,9 @@
 //    first K/V tile as whole-row buffer loads into the idle second buffer and
 //    are read out as MFMA operands; each wave writes its O rows into the
 //    buffer the last tile did not use and stores them as whole rows, 16 bytes
-//    per lane, instead of 8-byte pieces of 32 rows per instruction.
+//    per lane, instead of 8-byte pieces of 32 rows per instruction. Both the q
+//    loads and the O stores carry the non-temporal cache policy (read or
+//    written once), which leaves L2 to the K/V tiles that are re-read.
 //  * The scale is applied to fp32 scores (folded with log2 e into one FMA
 //    before exp2); q is never rescaled in its input precision. A negative scale
 //    flips q's sign bits in registers (exact) so the kernel always sees c > 0.
@@ -633,7 +635,8 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
             const int r = i * (64 / C) + lane / C;
             const int c = lane % C;
             const u32x4_t x = *(const lds_u32x4_t *)(ob + r * L::ROWB + 16 * (c ^ oswz(r)));
-            if (wq0 + r < T) *(u32x4_t *)(obase + (long long)(wq0 + r) * p.os[1] + 8 * c) = x;
+            if (wq0 + r < T)   // written once: non-temporal, like the q loads
+                __builtin_nontemporal_store(x, (u32x4_t *)(obase + (long long)(wq0 + r) * p.os[1] + 8 * c));
         }
         if (half == 0 && row_live) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
         return;
