@@ -13,7 +13,8 @@ count; the masked upper triangle is not counted).
 Prints ONE JSON line. Extra keys: `roofline` (achieved vs MI355X dense bf16
 MFMA peak), `cpu_baseline` (the float64 oracle timed on this host, with the
 GPU output compared against it as a by-product), `cold` (per-call times with
-the 256 MB last-level cache flushed before each call).
+the L2s and the 256 MB last-level cache emptied of the step's data before each
+call, by reading a 512 MiB buffer; `after_fill` the same after writing it).
 """
 import argparse
 import hashlib
@@ -313,23 +314,36 @@ def main():
 
     cold = None
     if not a.no_cold:
-        # 512 MiB fill between calls evicts the 256 MB MALL and the L2s.
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        times = []
-        for _ in range(20):
-            flush.fill_(1)
-            c0 = torch.cuda.Event(enable_timing=True)
-            c1 = torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            step()
-            c1.record(stream)
-            torch.cuda.synchronize()
-            times.append(c0.elapsed_time(c1))
+        # Caches emptied of the step's data before each of 20 calls by touching
+        # a 512 MiB buffer (twice the 256 MB MALL, far above the L2s):
+        #   "cold": the buffer is read (summed), which leaves clean lines only;
+        #   "after_fill": the buffer is written (filled), which leaves 256 MB of
+        #   dirty lines whose write-back to HBM competes with the step.
+        flush = torch.ones(512 << 18, dtype=torch.int32, device="cuda")
+        sink = torch.zeros((), dtype=torch.int64, device="cuda")
+
+        def timed_after(evict):
+            times = []
+            for _ in range(20):
+                evict()
+                c0 = torch.cuda.Event(enable_timing=True)
+                c1 = torch.cuda.Event(enable_timing=True)
+                c0.record(stream)
+                step()
+                c1.record(stream)
+                torch.cuda.synchronize()
+                times.append(c0.elapsed_time(c1))
+            return times
+
+        times = timed_after(lambda: sink.add_(flush.sum()))
+        ftimes = timed_after(lambda: flush.fill_(1))
         del flush
         cms = float(np.median(times))
+        fms = float(np.median(ftimes))
         cold = {"ms_median": cms, "tflops": flops / (cms * 1e-3) / 1e12,
                 "ms_p10": float(np.percentile(times, 10)),
-                "ms_p90": float(np.percentile(times, 90))}
+                "ms_p90": float(np.percentile(times, 90)),
+                "after_fill": {"ms_median": fms, "tflops": flops / (fms * 1e-3) / 1e12}}
 
     peak = PEAK[w.dtype]
     groups = fa.key_groups(w.B, w.H, w.T, w.D, torch_dtype(w.dtype))
