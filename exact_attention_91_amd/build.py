@@ -22,9 +22,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-mllvm", "-simplifycfg-hoist-common=false"]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    """Compile each source to an object in parallel, then link the library."""
-    objs = [os.path.join(HERE, "csrc", os.path.basename(src) + ".o") for src in SRCS]
+def build(verbose: bool = False, extra=(), out: str = None) -> str:
+    """Compile each source to an object in parallel, then link the library
+    (libfa.so, or `out`)."""
+    out = out or LIB
+    tag = os.path.splitext(os.path.basename(out))[0]
+    objs = [os.path.join(HERE, "csrc", f"{os.path.basename(src)}.{tag}.o") for src in SRCS]
     compile_flags = [f for f in FLAGS if f != "-shared"]
     procs = []
     for src, obj in zip(SRCS, objs):
@@ -36,14 +39,25 @@ def build(verbose: bool = False, extra=()) -> str:
     failed = [p.args for p in procs if p.wait() != 0]
     if failed:
         raise subprocess.CalledProcessError(1, failed[0])
-    cmd = [HIPCC, *FLAGS, *extra, "-o", LIB + ".tmp", *objs]
+    cmd = [HIPCC, *FLAGS, *extra, "-o", out + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     for obj in objs:
         os.remove(obj)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+POISON_LIB = os.path.join(HERE, "libfa_poison.so")
+
+
+def build_poison(verbose: bool = False) -> str:
+    """The debug build of the same library in which every staged LDS buffer
+    reads as NaN between its last reader and its refill (FA_LDS_POISON): the
+    GPU tests run a set of parity cases through it, so a read that races a
+    refill shows up as NaN instead of stale data. Slower; not for use."""
+    return build(verbose, extra=("-DFA_LDS_POISON",), out=POISON_LIB)
 
 
 def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:

@@ -488,9 +488,14 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of tile `it` have landed
             __syncthreads();
+            // (debug builds: the buffers about to be refilled read as NaN until then)
+            lds_poison2(it + 1 < ite, qn, on, L::TILEB, tid, kThreads);
+            lds_poison(it + 1 < ite, sn, 2 * BQ * 4, tid, kThreads);
             if (it + 1 < ite) stage(it + 1, qn, on, sn);
             if (wave_live) compute(it, qt, ot, st);
         };
+        lds_poison2(job > 0 && itb < ite, q_lds0, o_lds0, L::TILEB, tid, kThreads);
+        lds_poison(job > 0 && itb < ite, st_lds0, 2 * BQ * 4, tid, kThreads);
         if (itb < ite) stage(itb, q_lds0, o_lds0, st_lds0);
         for (int it = itb; it < ite; it += 2) {
             step(it, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1);
@@ -816,6 +821,9 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_bwd_dq_kernel
         __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        // (debug builds: the buffers about to be refilled read as NaN until then;
+        // with G2 each group fills its own)
+        lds_poison2(jn < jend, kn, vn, L::TILEB, G2 ? (tid & (kThreads - 1)) : tid, kThreads);
         if (jn < jend)
             stage_tile<D>(kbase, vbase, krs, krs, T, jn * BK, wave, koff, voff, kn, vn);
         const int key0 = j * BK;

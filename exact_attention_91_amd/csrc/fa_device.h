@@ -190,6 +190,44 @@ __device__ __forceinline__ void stage_rows(const unsigned short *base, long long
     }
 }
 
+// Debug builds compiled with FA_LDS_POISON (libfa_poison.so): between the
+// barrier that ends the last reads of an LDS buffer and its refill, the buffer
+// is set to all-ones bits (a NaN in every element type) and a second barrier
+// orders that fill before the refill, so a read that races the refill, or an
+// access the tile's barriers do not cover, returns NaN instead of stale data.
+// Every wave of the work-group calls it the same number of times (it holds a
+// barrier); `fill` says whether the caller's buffer is refilled at this step;
+// threads t, t + nt, ... of the caller's group share the writes. Release
+// builds compile it to nothing.
+__device__ __forceinline__ void lds_poison(bool fill, void *buf, int bytes, int t, int nt) {
+#ifdef FA_LDS_POISON
+    if (fill) {
+        const u32x4_t ones = {~0u, ~0u, ~0u, ~0u};
+        for (int i = t; i < bytes / 16; i += nt)
+            *(lds_u32x4_t *)((__attribute__((address_space(3))) unsigned char *)buf + 16 * i) = ones;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#else
+    (void)fill; (void)buf; (void)bytes; (void)t; (void)nt;
+#endif
+}
+__device__ __forceinline__ void lds_poison2(bool fill, void *a, void *b, int bytes, int t, int nt) {
+#ifdef FA_LDS_POISON
+    if (fill) {
+        const u32x4_t ones = {~0u, ~0u, ~0u, ~0u};
+        for (int i = t; i < bytes / 16; i += nt) {
+            *(lds_u32x4_t *)((__attribute__((address_space(3))) unsigned char *)a + 16 * i) = ones;
+            *(lds_u32x4_t *)((__attribute__((address_space(3))) unsigned char *)b + 16 * i) = ones;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#else
+    (void)fill; (void)a; (void)b; (void)bytes; (void)t; (void)nt;
+#endif
+}
+
 // Host: a * b for non-negative sizes, saturating at LLONG_MAX instead of
 // overflowing (size heuristics compare the result with small thresholds).
 inline long long mul_sat(long long a, long long b) {

@@ -460,6 +460,10 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
                     const unsigned char *vt, unsigned char *kn, unsigned char *vn) {
         __builtin_amdgcn_s_waitcnt(0);   // this lane's loads of tile j have landed
         __syncthreads();
+        // (debug builds: the buffers about to be refilled read as NaN until then;
+        // with G2 each group fills its own)
+        lds_poison2(jn < jend, kn, vn, L::TILEB, G2 ? (tid & (kThreads - 1)) : tid,
+                    HP ? 2 * kThreads : kThreads);
         if (jn < jend)
             stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jn * BK, swave, koff, voff, kn, vn);
         const int key0 = j * BK;
@@ -614,6 +618,10 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         const bool last_in0 = ((jend - 1 - jbeg) & 1) == 0;
         unsigned char *ob = (last_in0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
                             (wave & 1) * 32 * L::ROWB;
+#ifdef FA_LDS_POISON
+        for (int i = lane; i < 2 * L::ROWB; i += 64)   // 32 rows: NaN until written
+            *(lds_u32x4_t *)(ob + 16 * i) = u32x4_t{~0u, ~0u, ~0u, ~0u};
+#endif
 #pragma unroll
         for (int n = 0; n < ND; ++n)
 #pragma unroll
@@ -672,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
     constexpr int CH = BK * D / 4;          // float4 chunks per tile
     constexpr int CPT = (CH + kThreads - 1) / kThreads;
 
-    __shared__ float k_lds[2][BK * KST];
+    __shared__ __attribute__((aligned(16))) float k_lds[2][BK * KST];
     __shared__ __attribute__((aligned(16))) float v_lds[2][BK * VST];
 
     const int tid = threadIdx.x;
@@ -747,6 +755,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(FwdParams p) {
     load_tile(0);
     for (int j = 0; j < nkt; ++j) {
         const int buf = j & 1;
+        // (debug builds: buffer buf, last read at step j - 2, reads as NaN until
+        // its refill)
+        lds_poison(true, k_lds[buf], sizeof(k_lds[0]), tid, kThreads);
+        lds_poison(true, v_lds[buf], sizeof(v_lds[0]), tid, kThreads);
         store_tile(buf);
         __syncthreads();
         if (j + 1 < nkt) load_tile(j + 1);

@@ -6,6 +6,7 @@ backward) on torch's current stream. Every step of the attention runs in the
 library's HIP kernels; there is no fallback. If libfa.so is missing, every
 call raises.
 """
+import contextlib
 import ctypes
 import math
 import os
@@ -37,53 +38,73 @@ def _lib():
             raise RuntimeError(
                 f"libfa.so not found at {_LIB_PATH}: build it first "
                 "(python -c 'import __graft_entry__ as g; g.build()')")
-        lib = ctypes.CDLL(_LIB_PATH)
-        lib.fa_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP] + [_I] * 6 + [ctypes.c_float, _I, _VP]
-        lib.fa_fwd.restype = _I
-        lib.fa_fwd_strided.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
-                                       [ctypes.c_float, _I] + [_LLP] * 4 + [_VP])
-        lib.fa_fwd_strided.restype = _I
-        lib.fa_fwd_key_groups.argtypes = [_I] * 5
-        lib.fa_fwd_key_groups.restype = _I
-        lib.fa_fwd_splitk.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
-                                      [ctypes.c_float, _I, _I, _VP, ctypes.c_longlong, _VP])
-        lib.fa_fwd_splitk.restype = _I
-        lib.fa_fwd_splitk_noalloc.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
-                                              [ctypes.c_float, _I, _I, _VP])
-        lib.fa_fwd_splitk_noalloc.restype = _I
-        lib.fa_fwd_splitk_scratch_bytes.argtypes = []
-        lib.fa_fwd_splitk_scratch_bytes.restype = ctypes.c_longlong
-        lib.fa_fwd_decode.argtypes = ([_VP] * 5 + [_I] * 7 + [ctypes.c_float, _I, _I, _VP,
-                                                              ctypes.c_longlong, _VP])
-        lib.fa_fwd_decode.restype = _I
-        lib.fa_fwd_decode_workspace_bytes.argtypes = [_I] * 5
-        lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_longlong
-        lib.fa_fwd_splitk_workspace_bytes.argtypes = [_I] * 5
-        lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
-        lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
-        lib.fa_lse_combine.restype = _I
-        lib.fa_fwd_window.argtypes = ([_VP] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _VP])
-        lib.fa_fwd_window.restype = _I
-        lib.fa_window_bitmap.argtypes = [_VP, _I, _I, _VP, ctypes.c_longlong, _VP]
-        lib.fa_window_bitmap.restype = _I
-        lib.fa_window_bitmap_bytes.argtypes = [_I]
-        lib.fa_window_bitmap_bytes.restype = ctypes.c_longlong
-        lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP,
-                                                        ctypes.c_longlong, _VP]
-        lib.fa_bwd.restype = _I
-        lib.fa_bwd_window.argtypes = ([_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _I,
-                                                              _VP, ctypes.c_longlong, _VP])
-        lib.fa_bwd_window.restype = _I
-        lib.fa_bwd_workspace_bytes.argtypes = [_I] * 6
-        lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
-        lib.fa_bwd_window_workspace_bytes.argtypes = [_I] * 8
-        lib.fa_bwd_window_workspace_bytes.restype = ctypes.c_longlong
-        lib.fa_status_str.argtypes = [_I]
-        lib.fa_status_str.restype = ctypes.c_char_p
-        lib.fa_version.argtypes = []
-        lib.fa_version.restype = _I
-        _LIB = lib
+        _LIB = _configure(ctypes.CDLL(_LIB_PATH))
     return _LIB
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Inside the with-block every call of this binding goes to the C ABI of
+    the library at `path`, another build of the same sources (the LDS-poisoning
+    debug build libfa_poison.so in the tests)."""
+    global _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it first")
+    prev = _LIB
+    _LIB = _configure(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _LIB = prev
+
+
+def _configure(lib):
+    """Declare the argument and result types of every entry point of `lib`."""
+    lib.fa_fwd.argtypes = [_VP, _VP, _VP, _VP, _VP] + [_I] * 6 + [ctypes.c_float, _I, _VP]
+    lib.fa_fwd.restype = _I
+    lib.fa_fwd_strided.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
+                                   [ctypes.c_float, _I] + [_LLP] * 4 + [_VP])
+    lib.fa_fwd_strided.restype = _I
+    lib.fa_fwd_key_groups.argtypes = [_I] * 5
+    lib.fa_fwd_key_groups.restype = _I
+    lib.fa_fwd_splitk.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
+                                  [ctypes.c_float, _I, _I, _VP, ctypes.c_longlong, _VP])
+    lib.fa_fwd_splitk.restype = _I
+    lib.fa_fwd_splitk_noalloc.argtypes = ([_VP, _VP, _VP, _VP, _VP] + [_I] * 6 +
+                                          [ctypes.c_float, _I, _I, _VP])
+    lib.fa_fwd_splitk_noalloc.restype = _I
+    lib.fa_fwd_splitk_scratch_bytes.argtypes = []
+    lib.fa_fwd_splitk_scratch_bytes.restype = ctypes.c_longlong
+    lib.fa_fwd_decode.argtypes = ([_VP] * 5 + [_I] * 7 + [ctypes.c_float, _I, _I, _VP,
+                                                          ctypes.c_longlong, _VP])
+    lib.fa_fwd_decode.restype = _I
+    lib.fa_fwd_decode_workspace_bytes.argtypes = [_I] * 5
+    lib.fa_fwd_decode_workspace_bytes.restype = ctypes.c_longlong
+    lib.fa_fwd_splitk_workspace_bytes.argtypes = [_I] * 5
+    lib.fa_fwd_splitk_workspace_bytes.restype = ctypes.c_longlong
+    lib.fa_lse_combine.argtypes = [_VP, _VP] + [_I] * 5 + [_VP, _VP, _I, _VP]
+    lib.fa_lse_combine.restype = _I
+    lib.fa_fwd_window.argtypes = ([_VP] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _VP])
+    lib.fa_fwd_window.restype = _I
+    lib.fa_window_bitmap.argtypes = [_VP, _I, _I, _VP, ctypes.c_longlong, _VP]
+    lib.fa_window_bitmap.restype = _I
+    lib.fa_window_bitmap_bytes.argtypes = [_I]
+    lib.fa_window_bitmap_bytes.restype = ctypes.c_longlong
+    lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP,
+                                                    ctypes.c_longlong, _VP]
+    lib.fa_bwd.restype = _I
+    lib.fa_bwd_window.argtypes = ([_VP] * 9 + [_I] * 6 + [ctypes.c_float, _I, _I, _VP, _I,
+                                                          _VP, ctypes.c_longlong, _VP])
+    lib.fa_bwd_window.restype = _I
+    lib.fa_bwd_workspace_bytes.argtypes = [_I] * 6
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_longlong
+    lib.fa_bwd_window_workspace_bytes.argtypes = [_I] * 8
+    lib.fa_bwd_window_workspace_bytes.restype = ctypes.c_longlong
+    lib.fa_status_str.argtypes = [_I]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = _I
+    return lib
 
 
 def version() -> int:
