@@ -81,6 +81,9 @@ struct BwdParams {
     // dkpart/dvpart [s][b][t][g][d], added in part order by the reduce kernel.
     int hsplit;
     float *dkpart, *dvpart;
+    // 1: the D = 128 dK/dV kernel keeps V rows in LDS and walks 32-row query
+    // tiles (two work-groups per CU); 0: V in registers, 64-row tiles.
+    int vlds;
     // Window mode (as the window forward): key j visible to query i iff
     // |i - j| <= window (clamped to T) or bit j%64 of gbits[j/64] is set
     // (gbits NULL: no global tokens); causal still applies.
@@ -195,13 +198,20 @@ __device__ void scan_global_tiles(const BwdParams &p, int tk, SplitLds &sl) {
 // registers 8 s2 .. 8 s2 + 7, whose queries 16 s2 + 8(e/4) + 4half + e%4 are
 // exactly the rows the transposing reads of dO^T / Q^T hand lane (d, half).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool WINDOW>
+template <typename E, int D, bool CAUSAL, bool WINDOW, bool VL = false>
 __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
-    using L = Bf16Layout<D>;
+    // VL (D = 128 only): the V rows of the work-group's 128 keys live in LDS
+    // (read as MFMA operands) instead of 32 registers per lane, and query tiles
+    // are 32 rows, so that the kernel fits 256 registers and two work-groups
+    // share a CU (two waves per SIMD). Otherwise V stays in registers and query
+    // tiles are 64 rows (D = 128: one work-group per CU).
+    static_assert(!VL || (D == 128 && !WINDOW), "VL: plain masks, D = 128");
+    using L = Bf16Layout<D, VL ? 32 : 64>;
     using H16 = Half16<E>;
     typedef typename H16::v8 e8_t;
     typedef typename H16::v4 e4_t;
-    constexpr int BQ = L::BK;               // 64 query rows per staged tile
+    constexpr int BQ = L::BK;               // query rows per staged tile
+    constexpr int NSUB = BQ / 32;           // 32-row blocks per tile
     constexpr int KS = D / 16;              // k-steps over the head dim
     constexpr int ND = (D + 31) / 32;       // 32-row blocks of dK^T / dV^T
     constexpr int NV = D >= 32 ? D / 32 : 1;
@@ -213,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) unsigned char o_lds1[L::TILEB];
     __shared__ __attribute__((aligned(16))) float st_lds0[2 * BQ];   // L2 then Delta
     __shared__ __attribute__((aligned(16))) float st_lds1[2 * BQ];
+    __shared__ __attribute__((aligned(1024))) unsigned char v_rows[VL ? kBlk * L::ROWB : 16];
     __shared__ SplitLds sl;
 
     const int tid = threadIdx.x;
@@ -305,7 +316,9 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
         const bool wave_live = wk0 < T;
 
         // K and V rows of this lane's key as B operands: lane (col, half) holds
-        // dims 16 ks + 8 half + 0..7.
+        // dims 16 ks + 8 half + 0..7. VL: the V rows of keys k0..k0+127 are
+        // copied into v_rows instead (row r at r * ROWB, chunk c at
+        // c ^ dswz(r), rows past T zero) and read with the row-read offsets.
         e8_t kf[KS], vf[KS];
         {
             const long long off = ((long long)b * T + key) * krs + (long long)g * D + 8 * half;
@@ -314,10 +327,37 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
                 u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
                 if (key < T) {
                     x = *(const u32x4_t *)((const unsigned short *)p.k + off + 16 * ks);
-                    y = *(const u32x4_t *)((const unsigned short *)p.v + off + 16 * ks);
+                    if (!VL) y = *(const u32x4_t *)((const unsigned short *)p.v + off + 16 * ks);
                 }
                 kf[ks] = __builtin_bit_cast(e8_t, x);
                 vf[ks] = __builtin_bit_cast(e8_t, y);
+            }
+        }
+        // (debug builds: the previous job's V rows read as NaN until replaced)
+        lds_poison(VL && job > 0, v_rows, sizeof(v_rows), tid, kThreads);
+        if (VL) {
+            // two 64-row halves, each addressed from its own first row
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int r0 = k0 + 64 * hb;
+                if (r0 < T) {
+                    const int rows = min(T - r0, 64);
+                    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<unsigned short *>((const unsigned short *)p.v +
+                                                     ((long long)b * T + r0) * krs +
+                                                     (long long)g * D),
+                        (short)0, ((rows - 1) * (int)krs + D) * 2, kRsrcWord3);
+                    constexpr int NL = 64 * L::ROWB / 1024;   // 1 KB loads per half
+#pragma unroll
+                    for (int i = 0; i < NL / 4; ++i) {
+                        const int idx = wave + 4 * i;
+                        const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
+                        const int voff = row * (int)krs * 2 + 16 * ((lane % L::C) ^ L::dswz(row));
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rv, (lds_void_t *)(v_rows + (64 * hb) * L::ROWB + idx * 1024), 16,
+                            voff, 0, 0, 0);
+                    }
+                }
             }
         }
 
@@ -389,9 +429,10 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             int h;
             const int q0 = qtile0(it, h);
             const long long hoff = (long long)b * T * qrs + (long long)h * D;
-            stage_tile<D>((const unsigned short *)p.q + hoff, (const unsigned short *)p.dout + hoff,
-                          qrs, qrs, T, q0, wave, qoff, qoff, qd, od);
-            if (wave < 2) {
+            stage_tile<D, 4, BQ>((const unsigned short *)p.q + hoff,
+                                 (const unsigned short *)p.dout + hoff, qrs, qrs, T, q0, wave, qoff,
+                                 qoff, qd, od);
+            if (wave < 2 && (BQ == 64 || lane < BQ)) {   // one float per lane
                 const long long r = ((long long)b * p.H + h) * T + q0;
                 const float *src = (wave == 0 ? p.l2 : p.delta) + r;
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -406,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             int h;
             const int q0 = qtile0(it, h);
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
+            for (int sub = 0; sub < NSUB; ++sub) {
                 const int n0 = q0 + 32 * sub;
                 if (n0 >= T || (CAUSAL && n0 + 31 < wk0)) continue;   // wave-uniform
                 bool need_mask = (CAUSAL && n0 < wk0 + 31) || (wk0 + 31 >= T);
@@ -424,8 +465,12 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
                         e8_t, *(const lds_bf16x8_t *)(qt + raddr[ks] + 32 * sub * L::ROWB));
                     const e8_t a2v = __builtin_bit_cast(
                         e8_t, *(const lds_bf16x8_t *)(ot + raddr[ks] + 32 * sub * L::ROWB));
+                    const e8_t bv = VL ? __builtin_bit_cast(
+                                             e8_t, *(const lds_bf16x8_t *)(
+                                                       v_rows + 32 * wave * L::ROWB + raddr[ks]))
+                                       : vf[ks];
                     s = H16::mfma(a, kf[ks], s);
-                    dp = H16::mfma(a2v, vf[ks], dp);
+                    dp = H16::mfma(a2v, bv, dp);
                 }
                 // P and dS; register r is query n0 + 8(r/4) + 4half + r%4.
 #pragma unroll
@@ -1015,6 +1060,18 @@ constexpr long long kMaxQueryParts = 8; // query-tile runs per key tile (library
 // runs of query heads, or, with one query head per kv head, key tiles for at
 // most half the CUs and T >= 4096, runs of each key tile's query tiles (not
 // for the window masks, whose key tiles see only their band's query tiles).
+// The D = 128 dK/dV variant with V rows in LDS and 32-row query tiles (two
+// work-groups per CU) for plain masks, except for long rows with two or more
+// work-groups of whole key tiles per CU already, where 64-row tiles' lower
+// per-step cost wins (measured on MI355X, bf16 causal: B=64 T=1024 88 vs 95
+// us, B=16 H_kv=4 T=2048 975 vs 1099 us, B=1 T=8192 116 vs 118 us; but
+// B=8 T=8192 522 vs 505 us).
+bool dkdv_vlds(int B, int H_kv, int T, int D, bool window) {
+    if (D != 128 || window) return false;
+    const long long units = mul_sat(mul_sat(B, H_kv), ((long long)T + kBlk - 1) / kBlk);
+    return !(T >= 4096 && units >= 2 * kNumCUB);
+}
+
 int head_parts(int B, int H, int H_kv, int T, int requested, bool window) {
     const int group = H / H_kv;
     if (requested > 0) return requested < group ? requested : group;
@@ -1120,9 +1177,13 @@ hipError_t launch_bwd(const BwdParams &p, hipStream_t s) {
         e = launch_kernel((fa_bwd_dq_kernel<E, D, CAUSAL, WINDOW>),
                           dim3((unsigned)((long long)p.B * p.H * p.nblk)), dim3(kThreads), s, p);
     if (e != hipSuccess) return e;
-    e = launch_kernel((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW>),
-                      dim3((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit + p.nfar)),
-                      dim3(kThreads), s, p);
+    constexpr bool CAN_VL = D == 128 && !WINDOW;
+    const dim3 grid((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit + p.nfar));
+    if (CAN_VL && p.vlds)
+        e = launch_kernel((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW, CAN_VL>), grid, dim3(kThreads),
+                          s, p);
+    else
+        e = launch_kernel((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW>), grid, dim3(kThreads), s, p);
     if (e != hipSuccess) return e;
     if (p.hsplit > 1) {
         const long long n = (long long)p.B * p.T * p.H_kv * D;
@@ -1241,6 +1302,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     p.c = scale * kLog2e;
     p.scale = scale;
     p.hsplit = hs;
+    p.vlds = dkdv_vlds(B, H_kv, T, D, window >= 0) ? 1 : 0;
     p.dkpart = p.dvpart = nullptr;
     if (hs > 1) {
         p.dkpart = (float *)((char *)workspace + stat_bytes);

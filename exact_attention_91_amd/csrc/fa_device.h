@@ -52,7 +52,7 @@ __device__ __forceinline__ int first_nonzero_word(const unsigned long long *bits
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile of 64 rows x D 16-bit elements, rows of 2D bytes, unpadded. The
+// LDS tile of 64 (or ROWS) rows x D 16-bit elements, rows of 2D bytes, unpadded. The
 // 16-byte chunks of each row are XOR-permuted so that the MFMA operand reads
 // are bank-conflict free (64 banks of 4 bytes; a 16-byte read serves 16 lanes
 // per cycle, an 8-byte read 32):
@@ -70,9 +70,9 @@ __device__ __forceinline__ int first_nonzero_word(const unsigned long long *bits
 // (e = 0..3) of the 64 halfwords the group reads, so a group reading a
 // 4-row x 16-column block row by row hands lane i the 4 rows of column i.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int ROWS = 64>
 struct Bf16Layout {
-    static constexpr int BK = 64;                 // keys per tile
+    static constexpr int BK = ROWS;               // rows (keys) per tile
     static constexpr int C = D / 8;               // 16-byte chunks per row
     static constexpr int R = 16 / C;              // rows per 256 bytes
     static constexpr int ROWB = 2 * D;            // bytes per row
@@ -134,15 +134,15 @@ constexpr int kCachePolicyNT = 2;              // buffer instruction cache polic
 
 
 // Issue this wave's share (of NW waves) of the global->LDS copies of two
-// 64-row tiles, e.g. a K tile and a V tile (buffer loads straight into LDS;
+// ROWS-row tiles (64 unless stated), e.g. a K tile and a V tile (buffer loads straight into LDS;
 // rows past T read as zeros): loads wave, wave + NW, ... koff/voff: per-lane
 // byte offsets of the global chunk each lane fetches for its LDS slot.
-template <int D, int NW = 4>
+template <int D, int NW = 4, int ROWS = 64>
 __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const unsigned short *vbase,
                                            long long ks1, long long vs1, int T, int key0,
                                            int wave, const int *koff, const int *voff,
                                            unsigned char *kdst, unsigned char *vdst) {
-    using L = Bf16Layout<D>;
+    using L = Bf16Layout<D, ROWS>;
     constexpr int NI = (L::NLOAD + NW - 1) / NW;
     // Valid bytes from this tile's first row; (63 * stride + D) * 2 < 2^31 is
     // checked on the host.

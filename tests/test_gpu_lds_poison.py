@@ -107,6 +107,18 @@ def test_backward(D, causal):
     same(a, b, f"bwd D={D} causal={causal}")
 
 
+def test_backward_long_rows_d128():
+    """D = 128 with long rows and many key tiles: the dK/dV kernel that keeps V
+    in registers and walks 64-row query tiles (the other D = 128 cases above
+    take the V-in-LDS variant)."""
+    B, H, T, D = 16, 1, 4096, 128
+    x, q, k, v = inputs(B, H, H, T, D, "bf16", 20)
+    do = generate_dout(B, H, T, D, "bf16", 21)[0].cuda()
+    o, lse = fa.fwd(q, k, v, causal=True, scale=default_scale(D))
+    a, b = both(lambda: fa.bwd(q, k, v, o, lse, do, causal=True, scale=default_scale(D)))
+    same(a, b, "bwd long rows D=128")
+
+
 def test_backward_head_split_and_window():
     x, q, k, v = inputs(1, 12, 1, 600, 64, "bf16", 18)
     do = generate_dout(1, 12, 600, 64, "bf16", 19)[0].cuda()
