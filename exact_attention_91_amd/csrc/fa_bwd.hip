@@ -262,23 +262,31 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     }
     // Row reads (A operand of S = Q K^T and dP = dO V^T): lane (col, half)
     // reads row col (+32 for the second block), dims 16 ks + 8 half + 0..7.
-    int raddr[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        raddr[ks] = col * L::ROWB + 16 * ((2 * ks + half) ^ L::dswz(col));
+    // Operand offsets. The row read of k-step ks is rbase ^ 32 ks and the
+    // transposing read of block n is tbase ^ 64 n (^ T8 for its +8-row half):
+    // the chunk index of a row is XOR-permuted and the row base shares no bit
+    // with it. The XOR is issued at each use (lane_xor) instead of holding
+    // 2 KS + 2 NV offsets in registers for the whole loop.
+    const int rbase = col * L::ROWB + 16 * (half ^ L::dswz(col));
     // Transposing reads (A operand dO^T / Q^T): rows r0 and r0 + 8 of each
     // 16-row step, dims 32 n + dl .. + 3.
-    int taddr[NV], taddr8[NV];
+    int tbase;
     {
         const int r0 = 4 * half + ((lane & 15) >> 2);
         const int dl = (D >= 32 ? 16 * ((lane >> 4) & 1) : 0) + 4 * (lane & 3);
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            const int d = 32 * n + dl;
-            taddr[n] = r0 * L::ROWB + 16 * ((d >> 3) ^ L::dswz(r0)) + 2 * (d & 7);
-            taddr8[n] = (r0 + 8) * L::ROWB + 16 * ((d >> 3) ^ L::dswz(r0 + 8)) + 2 * (d & 7);
-        }
+        tbase = r0 * L::ROWB + 16 * ((dl >> 3) ^ L::dswz(r0)) + 2 * (dl & 7);
     }
+    // rows r0 + 8: dswz(r0 + 8) = dswz(r0) ^ (D == 16 ? 1 : 2) for every r0 < 8
+    constexpr int T8 = 16 * (D == 16 ? 1 : 2) + 8 * L::ROWB;
+    // (window mode keeps the plain XOR, which the compiler may hold in registers:
+    // its extra per-job state leaves no registers to win)
+    auto roff = [&](int ks) __attribute__((always_inline)) {
+        return WINDOW ? rbase ^ (32 * ks) : lane_xor(rbase, 32 * ks);
+    };
+    auto toff = [&](int n, int r8) __attribute__((always_inline)) {
+        const int k = 64 * n ^ (r8 ? T8 : 0);
+        return WINDOW ? tbase ^ k : lane_xor(tbase, k);
+    };
     const bool tzero = D < 32 && col >= D;   // D=16: rows 16..31 of dO^T / Q^T are zero
     float c;
     asm volatile("v_mov_b32 %0, %1" : "=v"(c) : "s"(p.c));
@@ -461,13 +469,14 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
                 f32x16_t s = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
+                    const int ra = roff(ks);
                     const e8_t a = __builtin_bit_cast(
-                        e8_t, *(const lds_bf16x8_t *)(qt + raddr[ks] + 32 * sub * L::ROWB));
+                        e8_t, *(const lds_bf16x8_t *)(qt + ra + 32 * sub * L::ROWB));
                     const e8_t a2v = __builtin_bit_cast(
-                        e8_t, *(const lds_bf16x8_t *)(ot + raddr[ks] + 32 * sub * L::ROWB));
+                        e8_t, *(const lds_bf16x8_t *)(ot + ra + 32 * sub * L::ROWB));
                     const e8_t bv = VL ? __builtin_bit_cast(
                                              e8_t, *(const lds_bf16x8_t *)(
-                                                       v_rows + 32 * wave * L::ROWB + raddr[ks]))
+                                                       v_rows + 32 * wave * L::ROWB + ra))
                                        : vf[ks];
                     s = H16::mfma(a, kf[ks], s);
                     dp = H16::mfma(a2v, bv, dp);
@@ -505,17 +514,22 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
                     sb[0][e] = (E)dp[e];
                     sb[1][e] = (E)dp[8 + e];
                 }
+                int t0[ND], t1[ND];   // transposing-read offsets of this block
+#pragma unroll
+                for (int n = 0; n < ND; ++n) {
+                    t0[n] = toff(D >= 32 ? n : 0, 0);
+                    t1[n] = toff(D >= 32 ? n : 0, 1);
+                }
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const int ro = (32 * sub + 16 * s2) * L::ROWB;
 #pragma unroll
                     for (int n = 0; n < ND; ++n) {
-                        const int tn = D >= 32 ? n : 0;
-                        e8_t ao = __builtin_shufflevector(H16::read_tr(ot + taddr[tn] + ro),
-                                                          H16::read_tr(ot + taddr8[tn] + ro), 0,
+                        e8_t ao = __builtin_shufflevector(H16::read_tr(ot + t0[n] + ro),
+                                                          H16::read_tr(ot + t1[n] + ro), 0,
                                                           1, 2, 3, 4, 5, 6, 7);
-                        e8_t aq = __builtin_shufflevector(H16::read_tr(qt + taddr[tn] + ro),
-                                                          H16::read_tr(qt + taddr8[tn] + ro), 0,
+                        e8_t aq = __builtin_shufflevector(H16::read_tr(qt + t0[n] + ro),
+                                                          H16::read_tr(qt + t1[n] + ro), 0,
                                                           1, 2, 3, 4, 5, 6, 7);
                         if (tzero) {
                             ao = e8_t{};

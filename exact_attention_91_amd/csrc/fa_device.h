@@ -190,6 +190,17 @@ __device__ __forceinline__ void stage_rows(const unsigned short *base, long long
     }
 }
 
+// base ^ k for a per-lane base and a constant k, issued where it is used: an
+// asm statement the compiler neither hoists out of a loop nor keeps live, so a
+// kernel can derive many LDS offsets from one register at the cost of one VALU
+// instruction per use.
+__device__ __forceinline__ int lane_xor(int base, int k) {
+    if (k == 0) return base;
+    int r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(k), "v"(base));
+    return r;
+}
+
 // Debug builds compiled with FA_LDS_POISON (libfa_poison.so): between the
 // barrier that ends the last reads of an LDS buffer and its refill, the buffer
 // is set to all-ones bits (a NaN in every element type) and a second barrier
