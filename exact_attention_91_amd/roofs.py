@@ -3,7 +3,7 @@
 Runs each microbenchmark of libfa.so on torch's current stream, times it with
 events on that stream, and reports rates: dense bf16 MFMA FLOP/s, v_exp_f32
 and fp32 FMA instructions per second, MFMA/VALU overlap on one SIMD, and
-device-memory copy bandwidth. `python -m exact_attention_91_amd.roofs --write`
+device-memory copy and read bandwidth. `python -m exact_attention_91_amd.roofs --write`
 stores the result as JSON under profiles/, which bench.py reads to state the
 attention kernels' speed against measured as well as published peaks.
 """
