@@ -39,8 +39,8 @@
 //    memory into LDS (buffer loads to LDS) with XOR-permuted 16-byte chunks;
 //    the fp32 kernel stages through registers into padded rows. Either way
 //    the MFMA operand reads are bank-conflict free.
-//  * The plain forward (one key group, one head per work-group, unsplit)
-//    moves q and O through LDS: the work-group's 128 q rows arrive with the
+//  * The plain and window forwards (one key group, one head per work-group,
+//    unsplit) move q and O through LDS: the work-group's 128 q rows arrive with the
 //    first K/V tile as whole-row buffer loads into the idle second buffer and
 //    are read out as MFMA operands; each wave writes its O rows into the
 //    buffer the last tile did not use and stores them as whole rows, 16 bytes
@@ -259,12 +259,13 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
 
     // Q fragment = B operand of S^T = K Q^T: lane (col, half) holds
     // q[qrow, 16*ks + 8*half + 0..7].
-    // The plain forward (one head, one key group, unsplit) moves q and O
-    // through LDS: q rows arrive with the first K/V tile as whole-row buffer
-    // loads into the second K/V buffer and are read from there as MFMA operands;
-    // O rows leave from the buffer the last tile did not use as whole-row
-    // 16-byte stores. The other variants load q and store O from registers.
-    constexpr bool QO = !G2 && !HP && !SPLIT && !WINDOW && !DECODE;
+    // The plain and window forwards (one head, one key group, unsplit) move q
+    // and O through LDS: q rows arrive with the first K/V tile as whole-row
+    // buffer loads into the second K/V buffer and are read from there as MFMA
+    // operands; O rows leave from the buffer the last tile did not use as
+    // whole-row 16-byte stores. The other variants load q and store O from
+    // registers.
+    constexpr bool QO = !G2 && !HP && !SPLIT && !DECODE;
     e8_t qf[KS];
     if (!QO) {
         const unsigned short *qr = (const unsigned short *)p.q + u.b * p.qs[0] +
@@ -482,19 +483,54 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         }
         if (active) tile(need_mask, j, kt, vt, gb);
     };
+    // QO: issue the copies of the work-group's q rows into the second buffer
+    // pair (rows q0..q0+63 in k_lds1, q0+64..q0+127 in v_lds1, K tile layout;
+    // rows past T arrive as zeros) ...
+    auto qo_stage = [&]() __attribute__((always_inline)) {
+        const unsigned short *qb = (const unsigned short *)p.q + u.b * p.qs[0] + u.h * p.qs[2];
+        const long long qs1 = p.qs[1];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const int r0 = u.q0 + 64 * hb;
+            if (r0 < T)
+                stage_rows<D, NW>(qb + (long long)r0 * qs1, qs1, min(T - r0, 64), swave,
+                                  hb ? v_lds1 : k_lds1);
+        }
+    };
+    // ... and, after the first K/V tile's copies were issued too, wait for all
+    // of them: every wave's q rows have landed after the barrier. The first
+    // step's wait and barrier then order these reads before the next K/V tile
+    // is copied over them.
+    auto qo_read = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const unsigned char *qt = (wave < 2 ? k_lds1 : v_lds1) + (wave & 1) * 32 * L::ROWB;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4_t x = __builtin_bit_cast(u32x4_t, *(const lds_bf16x8_t *)(qt + kaddr[ks]));
+            x ^= p.qsign;
+            qf[ks] = __builtin_bit_cast(e8_t, x);
+        }
+    };
+    // Buffer pair (0 or 1) of the last step: the other one is free at the end.
+    bool last0 = true;
     if (WINDOW) {
         int j = next_tile(-1);
         unsigned long long gj = tile_bits(j);
+        if (QO) qo_stage();
         if (j < jend)
             stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, j * BK, swave, koff, voff, k_lds0, v_lds0);
+        if (QO) qo_read();
         while (j < jend) {
             const int jn = next_tile(j);
             const unsigned long long gn = tile_bits(jn);
             step(j, gj, jn, k_lds0, v_lds0, k_lds1, v_lds1);
+            last0 = true;
             if (jn >= jend) break;
             const int jnn = next_tile(jn);
             const unsigned long long gnn = tile_bits(jnn);
             step(jn, gn, jnn, k_lds1, v_lds1, k_lds0, v_lds0);
+            last0 = false;
             j = jnn;
             gj = gnn;
         }
@@ -509,36 +545,11 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
                 step(jbeg + i + 1, 0ull, jbeg + i + 2, k_lds1, v_lds1, k_lds0, v_lds0);
         }
     } else {
-        if (QO) {
-            // q rows q0..q0+63 into k_lds1, q0+64..q0+127 into v_lds1, in the K
-            // tile layout (rows past T arrive as zeros)
-            const unsigned short *qb =
-                (const unsigned short *)p.q + u.b * p.qs[0] + u.h * p.qs[2];
-            const long long qs1 = p.qs[1];
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                const int r0 = u.q0 + 64 * hb;
-                if (r0 < T)
-                    stage_rows<D, NW>(qb + (long long)r0 * qs1, qs1, min(T - r0, 64), swave,
-                                      hb ? v_lds1 : k_lds1);
-            }
-        }
+        if (QO) qo_stage();
         if (jbeg < jend)
             stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jbeg * BK, swave, koff, voff, k_lds0, v_lds0);
-        if (QO) {
-            // Every wave's q rows have landed after this barrier. The first step's
-            // wait and barrier then order these reads before tile jbeg + 1 is
-            // copied over them.
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            const unsigned char *qt = (wave < 2 ? k_lds1 : v_lds1) + (wave & 1) * 32 * L::ROWB;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4_t x = __builtin_bit_cast(u32x4_t, *(const lds_bf16x8_t *)(qt + kaddr[ks]));
-                x ^= p.qsign;
-                qf[ks] = __builtin_bit_cast(e8_t, x);
-            }
-        }
+        if (QO) qo_read();
+        last0 = ((jend - 1 - jbeg) & 1) == 0;
         for (int j = jbeg; j < jend; j += 2) {
             step(j, 0ull, j + 1, k_lds0, v_lds0, k_lds1, v_lds1);
             if (j + 1 < jend) step(j + 1, 0ull, j + 2, k_lds1, v_lds1, k_lds0, v_lds0);
@@ -610,13 +621,14 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     }
     if (QO) {
         // The buffer pair that did not hold the last tile is free: its last reads
-        // (tile jend - 2) and copies ended before the last step's barrier. Wave w
+        // (the tile before) and copies ended before the last step's barrier (with
+        // no step at all it still holds q, each wave's rows where that wave's O
+        // rows go, read by the wave itself before it writes there). Wave w
         // writes its 32 rows (row = col) there, 16-byte chunk c of a row at
         // c ^ oswz(row), then reads them back a row-contiguous 16 bytes per lane.
         constexpr int C = L::C;
         auto oswz = [](int r) { return (r >> 1) & (C - 1); };
-        const bool last_in0 = ((jend - 1 - jbeg) & 1) == 0;
-        unsigned char *ob = (last_in0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
+        unsigned char *ob = (last0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
                             (wave & 1) * 32 * L::ROWB;
 #ifdef FA_LDS_POISON
         for (int i = lane; i < 2 * L::ROWB; i += 64)   // 32 rows: NaN until written
