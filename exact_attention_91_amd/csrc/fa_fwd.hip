@@ -266,6 +266,9 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     // whole-row 16-byte stores. The other variants load q and store O from
     // registers.
     constexpr bool QO = !G2 && !HP && !SPLIT && !DECODE;
+    // O through LDS: also the head-pair kernel, each of its 8 waves using a
+    // quarter of one of the four buffers after a barrier past the last tile.
+    constexpr bool OO = QO || HP;
     e8_t qf[KS];
     if (!QO) {
         const unsigned short *qr = (const unsigned short *)p.q + u.b * p.qs[0] +
@@ -594,9 +597,12 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         }
     }
 
+    // HP: every wave of both heads has finished reading the K/V tiles before
+    // any wave reuses their buffers for O.
+    if (HP) __syncthreads();
     if (!wave_live) return;
     const float lt = half_swap_sum(lsum);
-    if (!QO && !row_live) return;   // QO: every lane takes part in the LDS transpose
+    if (!OO && !row_live) return;   // OO: every lane takes part in the LDS transpose
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
     const float lse_row = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
     if (SPLIT) {
@@ -619,8 +625,8 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         if (half == 0) p.lpart[row] = lse_row;
         return;
     }
-    if (QO) {
-        // The buffer pair that did not hold the last tile is free: its last reads
+    if (OO) {
+        // QO: the buffer pair that did not hold the last tile is free: its last reads
         // (the tile before) and copies ended before the last step's barrier (with
         // no step at all it still holds q, each wave's rows where that wave's O
         // rows go, read by the wave itself before it writes there). Wave w
@@ -628,8 +634,14 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         // c ^ oswz(row), then reads them back a row-contiguous 16 bytes per lane.
         constexpr int C = L::C;
         auto oswz = [](int r) { return (r >> 1) & (C - 1); };
-        unsigned char *ob = (last0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
-                            (wave & 1) * 32 * L::ROWB;
+        // HP: wave8 takes half of buffer wave8 / 2 (all four are free after the
+        // barrier above).
+        const int hb = wave8 >> 1;
+        unsigned char *ob =
+            HP ? (hb == 0 ? k_lds0 : hb == 1 ? v_lds0 : hb == 2 ? k_lds1 : v_lds1) +
+                     (wave8 & 1) * 32 * L::ROWB
+               : (last0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
+                     (wave & 1) * 32 * L::ROWB;
 #ifdef FA_LDS_POISON
         for (int i = lane; i < 2 * L::ROWB; i += 64)   // 32 rows: NaN until written
             *(lds_u32x4_t *)(ob + 16 * i) = u32x4_t{~0u, ~0u, ~0u, ~0u};
