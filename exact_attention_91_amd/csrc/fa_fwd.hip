@@ -39,8 +39,8 @@
 //    memory into LDS (buffer loads to LDS) with XOR-permuted 16-byte chunks;
 //    the fp32 kernel stages through registers into padded rows. Either way
 //    the MFMA operand reads are bank-conflict free.
-//  * The plain and window forwards (one key group, one head per work-group,
-//    unsplit) move q and O through LDS: the work-group's 128 q rows arrive with the
+//  * The plain, window and two-group forwards (one head per work-group,
+//    unsplit) move q and O through LDS (the head-pair kernel O only): the work-group's 128 q rows arrive with the
 //    first K/V tile as whole-row buffer loads into the idle second buffer and
 //    are read out as MFMA operands; each wave writes its O rows into the
 //    buffer the last tile did not use and stores them as whole rows, 16 bytes
@@ -265,7 +265,9 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     // operands; O rows leave from the buffer the last tile did not use as
     // whole-row 16-byte stores. The other variants load q and store O from
     // registers.
-    constexpr bool QO = !G2 && !HP && !SPLIT && !DECODE;
+    // (G2: group 0 copies the q rows into its second buffer pair and both groups
+    // read them there; O leaves from each group-0 wave's merge area.)
+    constexpr bool QO = !HP && !SPLIT && !DECODE;
     // O through LDS: also the head-pair kernel, each of its 8 waves using a
     // quarter of one of the four buffers after a barrier past the last tile.
     constexpr bool OO = QO || HP;
@@ -490,6 +492,7 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     // pair (rows q0..q0+63 in k_lds1, q0+64..q0+127 in v_lds1, K tile layout;
     // rows past T arrive as zeros) ...
     auto qo_stage = [&]() __attribute__((always_inline)) {
+        if (G2 && grp != 0) return;
         const unsigned short *qb = (const unsigned short *)p.q + u.b * p.qs[0] + u.h * p.qs[2];
         const long long qs1 = p.qs[1];
 #pragma unroll
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
             const int r0 = u.q0 + 64 * hb;
             if (r0 < T)
                 stage_rows<D, NW>(qb + (long long)r0 * qs1, qs1, min(T - r0, 64), swave,
-                                  hb ? v_lds1 : k_lds1);
+                                  hb ? v_lds1_ : k_lds1_);
         }
     };
     // ... and, after the first K/V tile's copies were issued too, wait for all
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     auto qo_read = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        const unsigned char *qt = (wave < 2 ? k_lds1 : v_lds1) + (wave & 1) * 32 * L::ROWB;
+        const unsigned char *qt = (wave < 2 ? k_lds1_ : v_lds1_) + (wave & 1) * 32 * L::ROWB;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4_t x = __builtin_bit_cast(u32x4_t, *(const lds_bf16x8_t *)(qt + kaddr[ks]));
@@ -540,8 +543,10 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     } else if (G2) {
         // Both groups take ghalf steps, one barrier each; group 1's last step is
         // idle when nkt is odd (no staging, no math).
+        if (QO) qo_stage();
         if (jbeg < jend)
             stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jbeg * BK, swave, koff, voff, k_lds0, v_lds0);
+        if (QO) qo_read();
         for (int i = 0; i < ghalf; i += 2) {
             step(jbeg + i, 0ull, jbeg + i + 1, k_lds0, v_lds0, k_lds1, v_lds1);
             if (i + 1 < ghalf)
@@ -636,12 +641,14 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         auto oswz = [](int r) { return (r >> 1) & (C - 1); };
         // HP: wave8 takes half of buffer wave8 / 2 (all four are free after the
         // barrier above).
+        // G2: group-0 wave w's merge area (it has read its partner's values).
         const int hb = wave8 >> 1;
         unsigned char *ob =
-            HP ? (hb == 0 ? k_lds0 : hb == 1 ? v_lds0 : hb == 2 ? k_lds1 : v_lds1) +
-                     (wave8 & 1) * 32 * L::ROWB
-               : (last0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
-                     (wave & 1) * 32 * L::ROWB;
+            HP   ? (hb == 0 ? k_lds0 : hb == 1 ? v_lds0 : hb == 2 ? k_lds1 : v_lds1) +
+                       (wave8 & 1) * 32 * L::ROWB
+            : G2 ? (wave == 0 ? k_lds0_ : wave == 1 ? v_lds0_ : wave == 2 ? k_lds1_ : v_lds1_)
+                 : (last0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
+                       (wave & 1) * 32 * L::ROWB;
 #ifdef FA_LDS_POISON
         for (int i = lane; i < 2 * L::ROWB; i += 64)   // 32 rows: NaN until written
             *(lds_u32x4_t *)(ob + 16 * i) = u32x4_t{~0u, ~0u, ~0u, ~0u};
