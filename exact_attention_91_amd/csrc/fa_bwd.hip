@@ -52,7 +52,6 @@
 namespace {
 
 constexpr int kBlk = 128;   // query rows (dQ) or keys (dK/dV) per work-group
-typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 
 struct BwdParams {
     const void *q, *k, *v, *o, *dout;

@@ -98,6 +98,7 @@ struct Bf16Layout {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8_t;
 typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));   // the builtin's type

@@ -259,18 +259,13 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
 
     // Q fragment = B operand of S^T = K Q^T: lane (col, half) holds
     // q[qrow, 16*ks + 8*half + 0..7].
-    // The plain and window forwards (one head, one key group, unsplit) move q
-    // and O through LDS: q rows arrive with the first K/V tile as whole-row
-    // buffer loads into the second K/V buffer and are read from there as MFMA
-    // operands; O rows leave from the buffer the last tile did not use as
-    // whole-row 16-byte stores. The other variants load q and store O from
-    // registers.
-    // (G2: group 0 copies the q rows into its second buffer pair and both groups
-    // read them there; O leaves from each group-0 wave's merge area.)
-    constexpr bool QO = !HP && !SPLIT && !DECODE;
-    // O through LDS: also the head-pair kernel, each of its 8 waves using a
-    // quarter of one of the four buffers after a barrier past the last tile.
-    constexpr bool OO = QO || HP;
+    // QO (every variant but head pairs and decode, whose q rows are not one
+    // head's consecutive rows): the work-group's q rows arrive with the first
+    // K/V tile as whole-row buffer loads into the second K/V buffer pair (G2:
+    // group 0's, read by both groups) and are read from there as MFMA operands.
+    // The others load their q fragments straight into registers. (Every
+    // variant writes its output rows through LDS; see the epilogue.)
+    constexpr bool QO = !HP && !DECODE;
     e8_t qf[KS];
     if (!QO) {
         const unsigned short *qr = (const unsigned short *)p.q + u.b * p.qs[0] +
@@ -602,19 +597,19 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         }
     }
 
-    // HP: every wave of both heads has finished reading the K/V tiles before
-    // any wave reuses their buffers for O.
-    if (HP) __syncthreads();
+    // HP and the key split: every wave has finished reading the K/V tiles
+    // before any wave reuses their buffers for its output rows.
+    if (HP || (SPLIT && !DECODE)) __syncthreads();
     if (!wave_live) return;
     const float lt = half_swap_sum(lsum);
-    if (!OO && !row_live) return;   // OO: every lane takes part in the LDS transpose
+    if (DECODE && !row_live) return;   // (others: every lane takes part in the LDS transposes)
     const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
     const float lse_row = lt > 0.f ? (mref + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
-    if (SPLIT) {
-        // Partial result over this split's keys, normalised by its own l.
-        const long long row = DECODE ? (((long long)u.s * p.B + u.b) * p.H + dh) * p.Tq + di
-                                     : (((long long)u.s * p.B + u.b) * p.H + u.h) * T + qrow;
-        float *orow = p.opart + row * D;
+    if (DECODE) {
+        // Partial result over this split's keys, normalised by its own l, fp32,
+        // stored from registers: a decode step writes few rows, which do not pay
+        // for the barrier and the transpose.
+        float *orow = p.opart + ((((long long)u.s * p.B + u.b) * p.H + dh) * p.Tq + di) * D;
 #pragma unroll
         for (int n = 0; n < ND; ++n)
 #pragma unroll
@@ -627,30 +622,24 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
                     *(f32x4_t *)(orow + d) = o4;
                 }
             }
-        if (half == 0) p.lpart[row] = lse_row;
+        if (half == 0) p.lpart[(((long long)u.s * p.B + u.b) * p.H + dh) * p.Tq + di] = lse_row;
         return;
     }
-    if (OO) {
-        // QO: the buffer pair that did not hold the last tile is free: its last reads
-        // (the tile before) and copies ended before the last step's barrier (with
-        // no step at all it still holds q, each wave's rows where that wave's O
-        // rows go, read by the wave itself before it writes there). Wave w
-        // writes its 32 rows (row = col) there, 16-byte chunk c of a row at
-        // c ^ oswz(row), then reads them back a row-contiguous 16 bytes per lane.
-        constexpr int C = L::C;
-        auto oswz = [](int r) { return (r >> 1) & (C - 1); };
-        // HP: wave8 takes half of buffer wave8 / 2 (all four are free after the
-        // barrier above).
-        // G2: group-0 wave w's merge area (it has read its partner's values).
-        const int hb = wave8 >> 1;
-        unsigned char *ob =
-            HP   ? (hb == 0 ? k_lds0 : hb == 1 ? v_lds0 : hb == 2 ? k_lds1 : v_lds1) +
-                       (wave8 & 1) * 32 * L::ROWB
-            : G2 ? (wave == 0 ? k_lds0_ : wave == 1 ? v_lds0_ : wave == 2 ? k_lds1_ : v_lds1_)
-                 : (last0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
-                       (wave & 1) * 32 * L::ROWB;
+    // O^T register r of block n is dim 32n + 8(r/4) + 4half + r%4 of this lane's
+    // row (col). The rows go out through LDS: each wave writes its 32 rows into
+    // a region of its own, 16-byte chunk c of a row at c XOR a function of the
+    // row, and reads them back a row-contiguous 16 bytes per lane, so the global
+    // stores cover whole rows (non-temporal: written once).
+    if (SPLIT) {
+        // Partial result over this split's keys, normalised by its own l, fp32:
+        // 32 rows x 4D bytes = one K/V buffer per wave (all free after the
+        // barrier above); a wave's rows are consecutive query rows.
+        constexpr int C = D / 4;                   // 16-byte chunks of an fp32 row
+        constexpr int RB = 4 * D;                  // bytes of an fp32 row
+        static_assert(32 * RB <= L::TILEB, "fp32 rows of a wave fit one buffer");
+        unsigned char *ob = wave == 0 ? k_lds0 : wave == 1 ? v_lds0 : wave == 2 ? k_lds1 : v_lds1;
 #ifdef FA_LDS_POISON
-        for (int i = lane; i < 2 * L::ROWB; i += 64)   // 32 rows: NaN until written
+        for (int i = lane; i < 2 * RB; i += 64)    // 32 rows: NaN until written
             *(lds_u32x4_t *)(ob + 16 * i) = u32x4_t{~0u, ~0u, ~0u, ~0u};
 #endif
 #pragma unroll
@@ -659,30 +648,49 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
             for (int rg = 0; rg < 4; ++rg) {
                 const int d = 32 * n + 8 * rg + 4 * half;
                 if (D >= 32 || d < D) {
-                    e4_t o4;
+                    f32x4_t o4;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[n][4 * rg + e] * inv);
-                    *(lds_u32x2_t *)(ob + col * L::ROWB + 16 * ((d >> 3) ^ oswz(col)) + 8 * half) =
-                        __builtin_bit_cast(u32x2_t, o4);
+                    for (int e = 0; e < 4; ++e) o4[e] = oacc[n][4 * rg + e] * inv;
+                    *(lds_f32x4_t *)(ob + col * RB + 16 * ((d >> 2) ^ (col & (C - 1)))) = o4;
                 }
             }
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_wave_barrier();
-        unsigned short *obase = (unsigned short *)p.o + u.b * p.os[0] + u.h * p.os[2];
+        // partial row index of the wave's row r (-1: past T)
+        auto prow = [&](int r) -> long long {
+            const int pr = wq0 + r;
+            return pr < T ? (((long long)u.s * p.B + u.b) * p.H + u.h) * T + pr : -1;
+        };
 #pragma unroll
         for (int i = 0; i < C / 2; ++i) {
             const int r = i * (64 / C) + lane / C;
             const int c = lane % C;
-            const u32x4_t x = *(const lds_u32x4_t *)(ob + r * L::ROWB + 16 * (c ^ oswz(r)));
-            if (wq0 + r < T)   // written once: non-temporal, like the q loads
-                __builtin_nontemporal_store(x, (u32x4_t *)(obase + (long long)(wq0 + r) * p.os[1] + 8 * c));
+            const f32x4_t x = *(const lds_f32x4_t *)(ob + r * RB + 16 * (c ^ (r & (C - 1))));
+            const long long row = prow(r);
+            if (row >= 0) __builtin_nontemporal_store(x, (f32x4_t *)(p.opart + row * D + 4 * c));
         }
-        if (half == 0 && row_live) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
+        if (half == 0 && row_live) p.lpart[prow(col)] = lse_row;
         return;
     }
-    unsigned short *orow = (unsigned short *)p.o + u.b * p.os[0] + (long long)qrow * p.os[1] +
-                           u.h * p.os[2];
-    // O^T register r of block n is dim 32n + 8(r/4) + 4half + r%4 of this row.
+    // QO: the buffer pair that did not hold the last tile is free: its last reads
+    // (the tile before) and copies ended before the last step's barrier (with
+    // no step at all it still holds q, each wave's rows where that wave's O rows
+    // go, read by the wave itself before it writes there). HP: wave8 takes half
+    // of buffer wave8 / 2 (all four are free after the barrier above). G2:
+    // group-0 wave w's merge area (it has read its partner's values).
+    constexpr int C = L::C;
+    auto oswz = [](int r) { return (r >> 1) & (C - 1); };
+    const int hb = wave8 >> 1;
+    unsigned char *ob =
+        HP   ? (hb == 0 ? k_lds0 : hb == 1 ? v_lds0 : hb == 2 ? k_lds1 : v_lds1) +
+                   (wave8 & 1) * 32 * L::ROWB
+        : G2 ? (wave == 0 ? k_lds0_ : wave == 1 ? v_lds0_ : wave == 2 ? k_lds1_ : v_lds1_)
+             : (last0 ? (wave < 2 ? k_lds1 : v_lds1) : (wave < 2 ? k_lds0 : v_lds0)) +
+                   (wave & 1) * 32 * L::ROWB;
+#ifdef FA_LDS_POISON
+    for (int i = lane; i < 2 * L::ROWB; i += 64)   // 32 rows: NaN until written
+        *(lds_u32x4_t *)(ob + 16 * i) = u32x4_t{~0u, ~0u, ~0u, ~0u};
+#endif
 #pragma unroll
     for (int n = 0; n < ND; ++n)
 #pragma unroll
@@ -692,10 +700,23 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
                 e4_t o4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o4[e] = (E)(oacc[n][4 * rg + e] * inv);
-                *(u32x2_t *)(orow + d) = __builtin_bit_cast(u32x2_t, o4);
+                *(lds_u32x2_t *)(ob + col * L::ROWB + 16 * ((d >> 3) ^ oswz(col)) + 8 * half) =
+                    __builtin_bit_cast(u32x2_t, o4);
             }
         }
-    if (half == 0) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    unsigned short *obase = (unsigned short *)p.o + u.b * p.os[0] + u.h * p.os[2];
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i) {
+        const int r = i * (64 / C) + lane / C;
+        const int c = lane % C;
+        const u32x4_t x = *(const lds_u32x4_t *)(ob + r * L::ROWB + 16 * (c ^ oswz(r)));
+        if (wq0 + r < T)
+            __builtin_nontemporal_store(x,
+                                        (u32x4_t *)(obase + (long long)(wq0 + r) * p.os[1] + 8 * c));
+    }
+    if (half == 0 && row_live) p.lse[((long long)u.b * p.H + u.h) * T + qrow] = lse_row;
 }
 // ---------------------------------------------------------------------------
 // fp32 kernel: fp32 operands on fp32 MFMA (32x32x2), 32-key tiles. Weights stay
