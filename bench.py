@@ -370,12 +370,12 @@ def main():
                  "kernel": (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
                             f"{str(a.nsplit > 1).lower()}, false, "
                             f"{str(a.nsplit == 1 and groups == 2).lower()}, "
-                            f"{str(a.nsplit == 1 and pairs).lower()}>"
+                            f"{str(a.nsplit == 1 and pairs).lower()}, false>"
                             if w.dtype in _ELEM else
                             f"fa_fwd_f32_kernel<{w.D}, {str(causal).lower()}>")})
     if w.window >= 0 and a.which == "fwd":
         roof["kernel"] = (f"fa_fwd_half_kernel<{_ELEM[w.dtype]}, {w.D}, {str(causal).lower()}, "
-                          f"false, true, false> (window)")
+                          f"false, true, false, false, false> (window)")
         roof["traffic"] = None
     if a.which == "bwd":
         roof["kernel"] = (f"fa_bwd_dq_kernel + fa_bwd_dkdv_kernel<{_ELEM[w.dtype]}, {w.D}, "
