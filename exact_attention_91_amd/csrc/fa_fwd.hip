@@ -419,9 +419,13 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         mref = mnew;
         const float mr = mref;
 
-        float ps0 = 0.f, ps1 = 0.f;
+        // (the sums start from the first weights: adding them to 0.f would cost
+        // two instructions the compiler may not drop, -0.f + 0.f being +0.f)
+        s0[0] = fast_exp2(fmaf(s0[0], c, -mr));
+        s1[0] = fast_exp2(fmaf(s1[0], c, -mr));
+        float ps0 = s0[0], ps1 = s1[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 1; r < 16; ++r) {
             s0[r] = fast_exp2(fmaf(s0[r], c, -mr));
             s1[r] = fast_exp2(fmaf(s1[r], c, -mr));
             ps0 += s0[r];
