@@ -19,7 +19,10 @@
 //    head of the group through double-buffered LDS. Scores are computed as
 //    S = Q K^T, so a lane owns one key column: P and dS feed the B operand of
 //    dV^T += dO^T P and dK^T += Q^T dS straight from registers, with dO^T and
-//    Q^T read from the same LDS tiles by transposing reads.
+//    Q^T read from the same LDS tiles by transposing reads. At D = 128 two
+//    variants fit two waves per SIMD: V rows in LDS with 32-row tiles (VL), or
+//    K rows in LDS with 8-wave work-groups whose two wave groups share each
+//    64-row tile's staging and take one 32-row block each (KL).
 //  * fa_bwd_dq_kernel (first): the forward's decomposition (one work-group
 //    per 128-row query tile, heaviest causal tiles first); each wave keeps
 //    its 32 query rows of Q and dO in registers, forms Delta = rowsum(dO o O)
@@ -83,6 +86,8 @@ struct BwdParams {
     // 1: the D = 128 dK/dV kernel keeps V rows in LDS and walks 32-row query
     // tiles (two work-groups per CU); 0: V in registers, 64-row tiles.
     int vlds;
+    // 1: the D = 128 dK/dV kernel with K rows in LDS and 8-wave work-groups
+    int klds;
     // Window mode (as the window forward): key j visible to query i iff
     // |i - j| <= window (clamped to T) or bit j%64 of gbits[j/64] is set
     // (gbits NULL: no global tokens); causal still applies.
@@ -197,14 +202,23 @@ __device__ void scan_global_tiles(const BwdParams &p, int tk, SplitLds &sl) {
 // registers 8 s2 .. 8 s2 + 7, whose queries 16 s2 + 8(e/4) + 4half + e%4 are
 // exactly the rows the transposing reads of dO^T / Q^T hand lane (d, half).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool CAUSAL, bool WINDOW, bool VL = false>
-__global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
+template <typename E, int D, bool CAUSAL, bool WINDOW, bool VL = false, bool KL = false>
+__global__ __launch_bounds__(KL ? 2 * kThreads : kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     // VL (D = 128 only): the V rows of the work-group's 128 keys live in LDS
     // (read as MFMA operands) instead of 32 registers per lane, and query tiles
     // are 32 rows, so that the kernel fits 256 registers and two work-groups
     // share a CU (two waves per SIMD). Otherwise V stays in registers and query
     // tiles are 64 rows (D = 128: one work-group per CU).
+    // KL (D = 128 only): 8 waves per work-group, the K rows of its 128 keys in
+    // LDS (read as MFMA operands, like VL's V rows), V in registers, 64-row
+    // query tiles staged once for all 8 waves; waves w and w + 4 own the same 32
+    // keys and take the first and second 32-row block of each tile, and wave
+    // w + 4 adds its dK/dV sums into wave w's at the end. Two waves per SIMD
+    // with 64-row tiles and no spilled registers.
     static_assert(!VL || (D == 128 && !WINDOW), "VL: plain masks, D = 128");
+    static_assert(!KL || (D == 128 && !WINDOW && !VL), "KL: plain masks, D = 128");
+    constexpr int NW = KL ? 8 : 4;            // waves per work-group
+    constexpr int NT = NW * 64;
     using L = Bf16Layout<D, VL ? 32 : 64>;
     using H16 = Half16<E>;
     typedef typename H16::v8 e8_t;
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int KS = D / 16;              // k-steps over the head dim
     constexpr int ND = (D + 31) / 32;       // 32-row blocks of dK^T / dV^T
     constexpr int NV = D >= 32 ? D / 32 : 1;
-    constexpr int NI = (L::NLOAD + 3) / 4;
+    constexpr int NI = (L::NLOAD + NW - 1) / NW;
 
     __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[L::TILEB];
     __shared__ __attribute__((aligned(1024))) unsigned char o_lds0[L::TILEB];
@@ -223,11 +237,15 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float st_lds0[2 * BQ];   // L2 then Delta
     __shared__ __attribute__((aligned(16))) float st_lds1[2 * BQ];
     __shared__ __attribute__((aligned(1024))) unsigned char v_rows[VL ? kBlk * L::ROWB : 16];
+    __shared__ __attribute__((aligned(1024))) unsigned char k_rows[KL ? kBlk * L::ROWB : 16];
     __shared__ SplitLds sl;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = KL ? (wave8 >> 2) : 0;       // KL: 32-row block of each query tile
+    const int wave = KL ? (wave8 & 3) : wave8;   // 32-key block
+    const int swave = KL ? wave8 : wave;          // share of the tile copies
     const int col = lane & 31, half = lane >> 5;
     const int T = p.T;
     const int nbg = p.B * p.H_kv;
@@ -255,7 +273,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
     int qoff[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int idx = wave + 4 * i;
+        const int idx = swave + NW * i;
         const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
         qoff[i] = row * (int)qrs * 2 + 16 * ((lane % L::C) ^ L::dswz(row));
     }
@@ -325,7 +343,8 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
         // K and V rows of this lane's key as B operands: lane (col, half) holds
         // dims 16 ks + 8 half + 0..7. VL: the V rows of keys k0..k0+127 are
         // copied into v_rows instead (row r at r * ROWB, chunk c at
-        // c ^ dswz(r), rows past T zero) and read with the row-read offsets.
+        // c ^ dswz(r), rows past T zero) and read with the row-read offsets;
+        // KL: the K rows likewise into k_rows.
         e8_t kf[KS], vf[KS];
         {
             const long long off = ((long long)b * T + key) * krs + (long long)g * D + 8 * half;
@@ -333,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             for (int ks = 0; ks < KS; ++ks) {
                 u32x4_t x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
                 if (key < T) {
-                    x = *(const u32x4_t *)((const unsigned short *)p.k + off + 16 * ks);
+                    if (!KL) x = *(const u32x4_t *)((const unsigned short *)p.k + off + 16 * ks);
                     if (!VL) y = *(const u32x4_t *)((const unsigned short *)p.v + off + 16 * ks);
                 }
                 kf[ks] = __builtin_bit_cast(e8_t, x);
@@ -363,6 +382,32 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
                             rv, (lds_void_t *)(v_rows + (64 * hb) * L::ROWB + idx * 1024), 16,
                             voff, 0, 0, 0);
+                    }
+                }
+            }
+        }
+
+        if (KL) {
+            // (one job: KL is not used with the window masks)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int r0 = k0 + 64 * hb;
+                if (r0 < T) {
+                    const int rows = min(T - r0, 64);
+                    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                        const_cast<unsigned short *>((const unsigned short *)p.k +
+                                                     ((long long)b * T + r0) * krs +
+                                                     (long long)g * D),
+                        (short)0, ((rows - 1) * (int)krs + D) * 2, kRsrcWord3);
+                    constexpr int NL = 64 * L::ROWB / 1024;   // 1 KB loads per half
+#pragma unroll
+                    for (int i = 0; i < NL / NW; ++i) {
+                        const int idx = swave + NW * i;
+                        const int row = idx * L::ROWS_PER_LOAD + lane / L::C;
+                        const int koff = row * (int)krs * 2 + 16 * ((lane % L::C) ^ L::dswz(row));
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            rk, (lds_void_t *)(k_rows + (64 * hb) * L::ROWB + idx * 1024), 16,
+                            koff, 0, 0, 0);
                     }
                 }
             }
@@ -436,15 +481,15 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             int h;
             const int q0 = qtile0(it, h);
             const long long hoff = (long long)b * T * qrs + (long long)h * D;
-            stage_tile<D, 4, BQ>((const unsigned short *)p.q + hoff,
-                                 (const unsigned short *)p.dout + hoff, qrs, qrs, T, q0, wave, qoff,
+            stage_tile<D, NW, BQ>((const unsigned short *)p.q + hoff,
+                                 (const unsigned short *)p.dout + hoff, qrs, qrs, T, q0, swave, qoff,
                                  qoff, qd, od);
-            if (wave < 2 && (BQ == 64 || lane < BQ)) {   // one float per lane
+            if (swave < 2 && (BQ == 64 || lane < BQ)) {   // one float per lane
                 const long long r = ((long long)b * p.H + h) * T + q0;
-                const float *src = (wave == 0 ? p.l2 : p.delta) + r;
+                const float *src = (swave == 0 ? p.l2 : p.delta) + r;
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     const_cast<float *>(src), (short)0, min(T - q0, BQ) * 4, kRsrcWord3);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sd + BQ * wave), 4,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(sd + BQ * swave), 4,
                                                          lane * 4, 0, 0, 0);
             }
         };
@@ -455,6 +500,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             const int q0 = qtile0(it, h);
 #pragma unroll
             for (int sub = 0; sub < NSUB; ++sub) {
+                if (KL && sub != grp) continue;   // KL: the other group's block
                 const int n0 = q0 + 32 * sub;
                 if (n0 >= T || (CAUSAL && n0 + 31 < wk0)) continue;   // wave-uniform
                 bool need_mask = (CAUSAL && n0 < wk0 + 31) || (wk0 + 31 >= T);
@@ -477,7 +523,11 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
                                              e8_t, *(const lds_bf16x8_t *)(
                                                        v_rows + 32 * wave * L::ROWB + ra))
                                        : vf[ks];
-                    s = H16::mfma(a, kf[ks], s);
+                    const e8_t bk = KL ? __builtin_bit_cast(
+                                             e8_t, *(const lds_bf16x8_t *)(
+                                                       k_rows + 32 * wave * L::ROWB + ra))
+                                       : kf[ks];
+                    s = H16::mfma(a, bk, s);
                     dp = H16::mfma(a2v, bv, dp);
                 }
                 // P and dS; register r is query n0 + 8(r/4) + 4half + r%4.
@@ -547,20 +597,47 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_dkdv_kernel(BwdParams p) {
             __builtin_amdgcn_s_waitcnt(0);   // this lane's copies of tile `it` have landed
             __syncthreads();
             // (debug builds: the buffers about to be refilled read as NaN until then)
-            lds_poison2(it + 1 < ite, qn, on, L::TILEB, tid, kThreads);
-            lds_poison(it + 1 < ite, sn, 2 * BQ * 4, tid, kThreads);
+            lds_poison2(it + 1 < ite, qn, on, L::TILEB, tid, NT);
+            lds_poison(it + 1 < ite, sn, 2 * BQ * 4, tid, NT);
             if (it + 1 < ite) stage(it + 1, qn, on, sn);
             if (wave_live) compute(it, qt, ot, st);
         };
-        lds_poison2(job > 0 && itb < ite, q_lds0, o_lds0, L::TILEB, tid, kThreads);
-        lds_poison(job > 0 && itb < ite, st_lds0, 2 * BQ * 4, tid, kThreads);
+        lds_poison2(job > 0 && itb < ite, q_lds0, o_lds0, L::TILEB, tid, NT);
+        lds_poison(job > 0 && itb < ite, st_lds0, 2 * BQ * 4, tid, NT);
         if (itb < ite) stage(itb, q_lds0, o_lds0, st_lds0);
         for (int it = itb; it < ite; it += 2) {
             step(it, q_lds0, o_lds0, st_lds0, q_lds1, o_lds1, st_lds1);
             if (it + 1 < ite) step(it + 1, q_lds1, o_lds1, st_lds1, q_lds0, o_lds0, st_lds0);
         }
 
-        if (wave_live && key < T) {
+        if (KL) {
+            // wave w + 4 (the second 32-row blocks) hands its sums to wave w (the
+            // same keys) through the free tile buffers, dK then dV; every wave
+            // takes every barrier (no tile copy is in flight after the last step)
+            __syncthreads();
+            float *mb = (float *)(wave == 0 ? q_lds0 : wave == 1 ? o_lds0
+                                  : wave == 2 ? q_lds1 : o_lds1);
+            static_assert(!KL || ND * 16 * 64 * 4 <= L::TILEB, "merge area");
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                f32x16_t *acc = pass == 0 ? dkacc : dvacc;
+                if (grp == 1 && wave_live) {
+#pragma unroll
+                    for (int n = 0; n < ND; ++n)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mb[(n * 16 + r) * 64 + lane] = acc[n][r];
+                }
+                __syncthreads();
+                if (grp == 0 && wave_live) {
+#pragma unroll
+                    for (int n = 0; n < ND; ++n)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[n][r] += mb[(n * 16 + r) * 64 + lane];
+                }
+                __syncthreads();
+            }
+        }
+        if (wave_live && key < T && grp == 0) {
             // dK^T / dV^T register r of block n is dim 32n + 8(r/4) + 4half + r%4.
             const long long off = ((long long)b * T + key) * krs + (long long)g * D;
             if (far) {
@@ -1085,6 +1162,17 @@ bool dkdv_vlds(int B, int H_kv, int T, int D, bool window) {
     return !(T >= 4096 && units >= 2 * kNumCUB);
 }
 
+// The D = 128 dK/dV variant with K rows in LDS and 8-wave work-groups (one per
+// CU, two waves per SIMD, 64-row query tiles) for plain masks when the launch
+// has at most two work-groups per CU (measured on MI355X, bf16 causal backward,
+// against the choice above: B=8 T=8192 498 -> 458 us, B=4 T=8192 465 -> 372,
+// B=16 T=2048 129 -> 107, B=1 T=8192 120 -> 116, B=64 T=1024 91 -> 90; with
+// 1024 work-groups it lost: B=2 T=8192 in 8 query-tile runs 197 -> 212, B=16
+// H=16 H_kv=4 T=2048 1004 -> 1026).
+bool dkdv_klds(long long workgroups, int D, bool window) {
+    return D == 128 && !window && workgroups <= 2 * kNumCUB;
+}
+
 int head_parts(int B, int H, int H_kv, int T, int requested, bool window) {
     const int group = H / H_kv;
     if (requested > 0) return requested < group ? requested : group;
@@ -1192,7 +1280,10 @@ hipError_t launch_bwd(const BwdParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     constexpr bool CAN_VL = D == 128 && !WINDOW;
     const dim3 grid((unsigned)((long long)p.B * p.H_kv * p.nblk * p.hsplit + p.nfar));
-    if (CAN_VL && p.vlds)
+    if (CAN_VL && p.klds)
+        e = launch_kernel((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW, false, CAN_VL>), grid,
+                          dim3(2 * kThreads), s, p);
+    else if (CAN_VL && p.vlds)
         e = launch_kernel((fa_bwd_dkdv_kernel<E, D, CAUSAL, WINDOW, CAN_VL>), grid, dim3(kThreads),
                           s, p);
     else
@@ -1316,6 +1407,7 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     p.scale = scale;
     p.hsplit = hs;
     p.vlds = dkdv_vlds(B, H_kv, T, D, window >= 0) ? 1 : 0;
+    p.klds = dkdv_klds((long long)B * H_kv * nblk * hs, D, window >= 0) ? 1 : 0;
     p.dkpart = p.dvpart = nullptr;
     if (hs > 1) {
         p.dkpart = (float *)((char *)workspace + stat_bytes);

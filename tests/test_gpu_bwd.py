@@ -186,6 +186,24 @@ def test_bwd_long_rows_d128():
     check_grads(x, do64, "bf16", True, default_scale(128), got, "long-shape")
 
 
+@pytest.mark.parametrize("B,H,T,causal,variant", [
+    (2, 2, 1000, True, "K rows in LDS, 8 waves"),
+    (2, 2, 1000, False, "K rows in LDS, 8 waves"),
+    (16, 9, 500, True, "V rows in LDS, 32-row tiles"),
+    (16, 9, 500, False, "V rows in LDS, 32-row tiles"),
+    (1, 17, 4096, True, "K and V in registers, 64-row tiles"),
+])
+def test_bwd_dkdv_variants_d128(B, H, T, causal, variant):
+    """The three D = 128 dK/dV kernels, each on a shape the library picks it
+    for: at most 512 key-tile work-groups take the 8-wave kernel with K rows in
+    LDS; more take V rows in LDS, or, with rows of at least 4096 keys and at
+    least 512 key tiles, K and V in registers. Compared in full."""
+    say(f"case bwd D=128 B={B} H={H} T={T} causal={causal}: {variant}")
+    x, do, do64 = case(B, H, H, T, 128, "bf16", 7100 + B + H + T)
+    got = run_bwd(x, do, causal, default_scale(128))
+    check_grads(x, do64, "bf16", causal, default_scale(128), got, variant)
+
+
 @pytest.mark.parametrize("H,H_kv", [(6, 2), (8, 1), (12, 1)])
 @pytest.mark.parametrize("head_split", [1, 2, 3, 0, 12])
 def test_bwd_head_split(H, H_kv, head_split):

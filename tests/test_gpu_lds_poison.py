@@ -107,16 +107,21 @@ def test_backward(D, causal):
     same(a, b, f"bwd D={D} causal={causal}")
 
 
-def test_backward_long_rows_d128():
-    """D = 128 with long rows and many key tiles: the dK/dV kernel that keeps V
-    in registers and walks 64-row query tiles (the other D = 128 cases above
-    take the V-in-LDS variant)."""
-    B, H, T, D = 16, 1, 4096, 128
-    x, q, k, v = inputs(B, H, H, T, D, "bf16", 20)
-    do = generate_dout(B, H, T, D, "bf16", 21)[0].cuda()
+@pytest.mark.parametrize("B,H,T,variant", [
+    (16, 1, 4096, "K rows in LDS, 8 waves (512 key tiles)"),
+    (16, 9, 500, "V rows in LDS, 32-row tiles"),
+    (1, 17, 4096, "K and V in registers, 64-row tiles"),
+])
+def test_backward_d128_variants(B, H, T, variant):
+    """The three D = 128 dK/dV kernels (the small cases above take the 8-wave
+    one with K rows in LDS): more than 512 key-tile work-groups pick V rows in
+    LDS, or with rows of at least 4096 keys K and V in registers."""
+    D = 128
+    x, q, k, v = inputs(B, H, H, T, D, "bf16", 20 + H)
+    do = generate_dout(B, H, T, D, "bf16", 21 + H)[0].cuda()
     o, lse = fa.fwd(q, k, v, causal=True, scale=default_scale(D))
     a, b = both(lambda: fa.bwd(q, k, v, o, lse, do, causal=True, scale=default_scale(D)))
-    same(a, b, "bwd long rows D=128")
+    same(a, b, f"bwd D=128 {variant}")
 
 
 def test_backward_head_split_and_window():
