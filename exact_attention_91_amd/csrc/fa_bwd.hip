@@ -1149,7 +1149,8 @@ constexpr long long kMaxQueryParts = 8; // query-tile runs per key tile (library
 // or, for 0, enough parts to bring the launch to kTargetWG work-groups --
 // runs of query heads, or, with one query head per kv head, key tiles for at
 // most half the CUs and T >= 4096, runs of each key tile's query tiles (not
-// for the window masks, whose key tiles see only their band's query tiles).
+// for the window masks, whose key tiles see only their band's query tiles);
+// at D = 128 no more than keep the launch within two work-groups per CU.
 // The D = 128 dK/dV variant with V rows in LDS and 32-row query tiles (two
 // work-groups per CU) for plain masks, except for long rows with two or more
 // work-groups of whole key tiles per CU already, where 64-row tiles' lower
@@ -1173,7 +1174,7 @@ bool dkdv_klds(long long workgroups, int D, bool window) {
     return D == 128 && !window && workgroups <= 2 * kNumCUB;
 }
 
-int head_parts(int B, int H, int H_kv, int T, int requested, bool window) {
+int head_parts(int B, int H, int H_kv, int T, int D, int requested, bool window) {
     const int group = H / H_kv;
     if (requested > 0) return requested < group ? requested : group;
     const long long nwg = mul_sat(mul_sat(B, H_kv), ((long long)T + kBlk - 1) / kBlk);
@@ -1183,9 +1184,19 @@ int head_parts(int B, int H, int H_kv, int T, int requested, bool window) {
     // rows: split each key tile's query tiles instead (at most kMaxQueryParts
     // runs; shorter rows or more key tiles lose more to the parts' fp32
     // traffic than they gain)
+    // D = 128, plain masks: no more parts than keep the launch within two
+    // work-groups per CU, where the 8-wave dK/dV kernel runs (dkdv_klds; measured
+    // on MI355X, bf16 causal backward: B=2 T=8192 in 4 query-tile runs instead
+    // of 8 195 -> 178 us, B=4 H=16 H_kv=1 T=4096 with 4 head parts instead of 8
+    // 938 -> 916 us)
+    long long cap = want;
+    if (D == 128 && !window && nwg <= 2 * kNumCUB) {
+        const long long fit = (2 * kNumCUB) / nwg;
+        cap = fit < want ? fit : want;
+    }
     if (!window && group == 1 && nwg <= kNumCUB / 2 && T >= 4096)
-        return (int)(want < kMaxQueryParts ? want : kMaxQueryParts);
-    return (int)(want < group ? want : group);
+        return (int)(cap < kMaxQueryParts ? cap : kMaxQueryParts);
+    return (int)(cap < group ? cap : group);
 }
 
 // Workspace: Delta and L2 (B*H*T floats each, padded to 16 bytes), then, with
@@ -1331,7 +1342,7 @@ extern "C" long long fa_bwd_workspace_bytes(int B, int H, int H_kv, int T, int D
     if (B < 0 || H < 1 || H_kv < 1 || T < 0 || H % H_kv != 0 || head_split < 0 ||
         (D != 16 && D != 32 && D != 64 && D != 128))
         return -1;
-    return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split, false),
+    return bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, D, head_split, false),
                         dq_parts_for(B, H, T, D, false), nullptr, nullptr);
 }
 
@@ -1340,7 +1351,7 @@ extern "C" long long fa_bwd_window_workspace_bytes(int B, int H, int H_kv, int T
     const long long base = fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split);
     if (base < 0 || window < 0 || n_global < 0) return -1;
     if (n_global == 0 || T == 0 || B == 0) return base;
-    const int hs = head_parts(B, H, H_kv, T, head_split, true);
+    const int hs = head_parts(B, H, H_kv, T, D, head_split, true);
     const int w = window < T ? window : T;
     const long long slots = n_global < T ? n_global : T;
     const long long extra =
@@ -1372,12 +1383,12 @@ int bwd_impl(const void *q, const void *k, const void *v, const void *o, const f
     for (const void *ptr : ptrs)
         if (!aligned16(ptr)) return FA_ERR_ALIGN;
     if (((uintptr_t)lse % 4) != 0 || ((uintptr_t)global_bits % 8) != 0) return FA_ERR_ALIGN;
-    const int hs = head_parts(B, H, H_kv, T, head_split, window >= 0);
+    const int hs = head_parts(B, H, H_kv, T, D, head_split, window >= 0);
     // The workspace starts with fa_bwd's layout for these arguments (the
     // window's split sums follow it); the window may use fewer parts of it.
     long long stat_bytes = 0, dq_offset = 0;
     const long long need =
-        bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, head_split, false),
+        bwd_ws_bytes(B, H, H_kv, T, D, head_parts(B, H, H_kv, T, D, head_split, false),
                      dq_parts_for(B, H, T, D, false), &stat_bytes, &dq_offset);
     if (need < 0) return FA_ERR_OVERFLOW;
     if (workspace_bytes < need) return FA_ERR_WORKSPACE;

@@ -308,8 +308,10 @@ long long fa_window_bitmap_bytes(int T);
  * a fixed order (still deterministic). A value > 0 is capped at H / H_kv.
  * 0 lets the library choose: enough parts to occupy the GPU, up to H / H_kv,
  * or, with H == H_kv, T >= 4096 and at most 128 (batch, kv head, 128-key
- * tile) work-groups, up to 8 parts of each key tile's query tiles. 1 means
- * no split; < 0 is FA_ERR_BAD_SHAPE.
+ * tile) work-groups, up to 8 parts of each key tile's query tiles; at D = 128
+ * without a window, no more parts than keep the dK/dV launch within 512
+ * work-groups when the key tiles alone fit in 512. 1 means no split; < 0 is
+ * FA_ERR_BAD_SHAPE.
  * workspace: caller-owned device memory, 16-byte aligned, at least
  * fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split) bytes: float32 Delta
  * [B][H][T], float32 lse * log2(e) [B][H][T] (padded to 16 bytes), then with

@@ -279,8 +279,13 @@ def test_bwd_workspace_bytes(lib):
     st = lambda B, H, T: (B * H * T * 8 + 15) // 16 * 16
     assert f(1, 1, 1, 8192, 128, 0) == st(1, 1, 8192) + 8 * 1 * 8192 * 1 * 128 * 8 + \
         4 * 1 * 8192 * 1 * 128 * 4                              # 64 tiles: 8 + 4 parts
-    assert f(2, 1, 1, 8192, 128, 0) == st(2, 1, 8192) + 8 * 2 * 8192 * 1 * 128 * 8 + \
-        2 * 2 * 8192 * 1 * 128 * 4                              # 128 tiles: 8 + 2 parts
+    # (at D = 128 the runs also stop at 512 dK/dV work-groups: 128 tiles take 4)
+    assert f(2, 1, 1, 8192, 128, 0) == st(2, 1, 8192) + 4 * 2 * 8192 * 1 * 128 * 8 + \
+        2 * 2 * 8192 * 1 * 128 * 4                              # 128 tiles: 4 + 2 parts
+    assert f(2, 1, 1, 8192, 64, 0) == st(2, 1, 8192) + 8 * 2 * 8192 * 1 * 64 * 8 + \
+        2 * 2 * 8192 * 1 * 64 * 4                               # D = 64: 8 + 2 parts
+    # query heads at D = 128: 128 key-tile work-groups take 4 head parts, not 8
+    assert f(4, 16, 1, 4096, 128, 0) == st(4, 16, 4096) + 4 * 4 * 4096 * 1 * 128 * 8
     assert f(1, 2, 2, 4096, 64, 0) == st(1, 2, 4096) + 8 * 1 * 4096 * 2 * 64 * 8 + \
         4 * 1 * 4096 * 2 * 64 * 4                               # D = 64, 64 tiles: 8 + 4 parts
     assert f(3, 1, 1, 8192, 128, 0) == st(3, 1, 8192)        # 192 tiles: no split
