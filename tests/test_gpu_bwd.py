@@ -204,17 +204,18 @@ def test_bwd_dkdv_variants_d128(B, H, T, causal, variant):
     check_grads(x, do64, "bf16", causal, default_scale(128), got, variant)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("H,H_kv", [(6, 2), (8, 1), (12, 1)])
 @pytest.mark.parametrize("head_split", [1, 2, 3, 0, 12])
-def test_bwd_head_split(H, H_kv, head_split):
+def test_bwd_head_split(H, H_kv, head_split, D):
     """The dK/dV kernel's query heads split into parts (fp32 sums added by the
     reduce kernel in part order): every split count matches the oracle and is
-    bitwise repeatable."""
+    bitwise repeatable (D = 128: the 8-wave kernel with K rows in LDS)."""
     from exact_attention_91_amd import fa
-    x, do, do64 = case(2, H, H_kv, 333, 64, "bf16", 9800 + 10 * H + head_split)
+    x, do, do64 = case(2, H, H_kv, 333, D, "bf16", 9800 + 10 * H + head_split + D)
     q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
     for causal in (False, True):
-        say(f"case bwd head_split={head_split} H={H} H_kv={H_kv} causal={causal}")
+        say(f"case bwd head_split={head_split} H={H} H_kv={H_kv} D={D} causal={causal}")
         o, lse = fa.fwd(q, k, v, causal=causal, scale=0.125)
         g1 = fa.bwd(q, k, v, o, lse, do.cuda(), causal=causal, scale=0.125,
                     head_split=head_split)
