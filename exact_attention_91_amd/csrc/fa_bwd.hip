@@ -511,7 +511,16 @@ __global__ __launch_bounds__(KL ? 2 * kThreads : kThreads) void fa_bwd_dkdv_kern
                     const bool inside = n0 + 31 - wk0 <= p.window && wk0 + 31 - n0 <= p.window;
                     need_mask = need_mask || !inside;
                 }
-                f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+                // dP - Delta accumulates from C = -Delta of each row (the workspace
+                // holds -Delta), so dS = P (dP - Delta) is one multiply
+                f32x16_t s = f32x16_t{}, dp;
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4_t nd4 =
+                        *(const lds_f32x4_t *)(st + BQ + 32 * sub + 8 * gq + 4 * half);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dp[4 * gq + e] = nd4[e];
+                }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ra = roff(ks);
@@ -534,14 +543,12 @@ __global__ __launch_bounds__(KL ? 2 * kThreads : kThreads) void fa_bwd_dkdv_kern
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const f32x4_t l4 = *(const lds_f32x4_t *)(st + 32 * sub + 8 * gq + 4 * half);
-                    const f32x4_t d4 =
-                        *(const lds_f32x4_t *)(st + BQ + 32 * sub + 8 * gq + 4 * half);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 4 * gq + e;
                         const float pr = fast_exp2(fmaf(s[r], c, -l4[e]));
                         s[r] = pr;
-                        dp[r] = pr * (dp[r] - d4[e]);
+                        dp[r] = pr * dp[r];
                     }
                 }
                 if (need_mask) {
@@ -807,7 +814,7 @@ __global__ __launch_bounds__(G2 ? 2 * kThreads : kThreads) void fa_bwd_dq_kernel
             const long long r = ((long long)b * p.H + h) * T + qrow;
             l2 = p.lse[r] * kLog2e;
             if (half == 0 && grp == 0 && kpart == 0) {
-                p.delta[r] = dl;
+                p.delta[r] = -dl;   // the dK/dV kernel starts its dP sums from it
                 p.l2[r] = l2;
             }
         }

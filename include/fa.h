@@ -313,7 +313,7 @@ long long fa_window_bitmap_bytes(int T);
  * work-groups when the key tiles alone fit in 512. 1 means no split; < 0 is
  * FA_ERR_BAD_SHAPE.
  * workspace: caller-owned device memory, 16-byte aligned, at least
- * fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split) bytes: float32 Delta
+ * fa_bwd_workspace_bytes(B, H, H_kv, T, D, head_split) bytes: float32 -Delta
  * [B][H][T], float32 lse * log2(e) [B][H][T] (padded to 16 bytes), then with
  * dK/dV parts the fp32 dK and dV parts, then with dQ parts the fp32 dQ parts;
  * overwritten (calls sharing a workspace must be ordered on one stream);
