@@ -15,7 +15,7 @@
 //  * fa_bwd_dkdv_kernel: one work-group per 128-key tile of one (batch, kv
 //    head); each wave keeps its 32 keys' K and V rows in registers as MFMA
 //    operands and its dK, dV accumulators in registers for the whole loop,
-//    and streams 64-row tiles of Q, dO (and their L2, Delta) of every query
+//    and streams 64-row tiles of Q, dO (and their L2, -Delta) of every query
 //    head of the group through double-buffered LDS. Scores are computed as
 //    S = Q K^T, so a lane owns one key column: P and dS feed the B operand of
 //    dV^T += dO^T P and dK^T += Q^T dS straight from registers, with dO^T and
@@ -26,8 +26,8 @@
 //  * fa_bwd_dq_kernel (first): the forward's decomposition (one work-group
 //    per 128-row query tile, heaviest causal tiles first); each wave keeps
 //    its 32 query rows of Q and dO in registers, forms Delta = rowsum(dO o O)
-//    and L2 = L log2(e) for them (stored in the workspace for the dK/dV
-//    kernel), streams K and V tiles, computes S^T = K Q^T and dP^T = V dO^T,
+//    and L2 = L log2(e) for them (-Delta and L2 stored in the workspace for
+//    the dK/dV kernel), streams K and V tiles, computes S^T = K Q^T and dP^T = V dO^T,
 //    and accumulates dQ^T += K^T dS^T with K^T from transposing reads of the
 //    K tile. At D = 64 and 128 on small grids its 8-wave G2 instantiation
 //    splits each query tile's key tiles between two groups of 4 waves and adds
@@ -195,7 +195,7 @@ __device__ void scan_global_tiles(const BwdParams &p, int tk, SplitLds &sl) {
 // dK, dV. Work-group: keys [k0, k0 + 128) of kv head g of batch b, wave w
 // owns keys wk0 = k0 + 32w .. wk0 + 31 (lane col = key wk0 + col).
 // Query tiles: 64 rows; LDS holds Q and dO tiles (dual swizzle) and the
-// tile's L2 and Delta (64 floats each), two buffers alternating.
+// tile's L2 and -Delta (64 floats each), two buffers alternating.
 // In the 32x32 accumulator layout of S = Q K^T (a 32-query block x 32 keys),
 // lane (col, half) register r is query 8(r/4) + 4half + r%4 of the block and
 // key col: the B operand of the 32-query reduction for k-step s2 is
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(KL ? 2 * kThreads : kThreads) void fa_bwd_dkdv_kern
     __shared__ __attribute__((aligned(1024))) unsigned char o_lds0[L::TILEB];
     __shared__ __attribute__((aligned(1024))) unsigned char q_lds1[L::TILEB];
     __shared__ __attribute__((aligned(1024))) unsigned char o_lds1[L::TILEB];
-    __shared__ __attribute__((aligned(16))) float st_lds0[2 * BQ];   // L2 then Delta
+    __shared__ __attribute__((aligned(16))) float st_lds0[2 * BQ];   // L2 then -Delta
     __shared__ __attribute__((aligned(16))) float st_lds1[2 * BQ];
     __shared__ __attribute__((aligned(1024))) unsigned char v_rows[VL ? kBlk * L::ROWB : 16];
     __shared__ __attribute__((aligned(1024))) unsigned char k_rows[KL ? kBlk * L::ROWB : 16];
@@ -1206,7 +1206,7 @@ int head_parts(int B, int H, int H_kv, int T, int D, int requested, bool window)
     return (int)(cap < group ? cap : group);
 }
 
-// Workspace: Delta and L2 (B*H*T floats each, padded to 16 bytes), then, with
+// Workspace: -Delta and L2 (B*H*T floats each, padded to 16 bytes), then, with
 // hs > 1 head parts, the fp32 dK and dV parts (hs * B*T*H_kv*D floats each).
 // Sets *stat_bytes to the size of the first region; -1 on overflow.
 long long bwd_ws_bytes(int B, int H, int H_kv, int T, int D, int hs, int dqp,
@@ -1282,7 +1282,7 @@ long long split_bytes(long long slots, int nparts, int B, int H_kv, int D) {
     return total;
 }
 
-// dQ first: it also writes Delta and L2, which the dK/dV kernel reads. The
+// dQ first: it also writes -Delta and L2, which the dK/dV kernel reads. The
 // global-key sums go last, over the rows the dK/dV (or reduce) kernel wrote.
 template <typename E, int D, bool CAUSAL, bool WINDOW>
 hipError_t launch_bwd(const BwdParams &p, hipStream_t s) {
