@@ -205,6 +205,28 @@ def test_bwd_dkdv_variants_d128(B, H, T, causal, variant):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def _d128_sweep_cases():
+    rng = np.random.default_rng(20261203)
+    out = []
+    for i in range(12):
+        H_kv = int(rng.integers(1, 4))
+        group = int(rng.choice([1, 2, 4]))
+        out.append((int(rng.integers(1, 4)), H_kv * group, H_kv, int(rng.integers(1, 1500)),
+                    bool(rng.integers(0, 2)), "bf16" if i % 3 else "f16", 7300 + i))
+    return out
+
+
+@pytest.mark.parametrize("B,H,H_kv,T,causal,dtype,seed", _d128_sweep_cases())
+def test_bwd_d128_seeded_shapes(B, H, H_kv, T, causal, dtype, seed):
+    """Seeded shapes at D = 128 (batch 1-3, 1-3 kv heads of 1, 2 or 4 query
+    heads, T from 1 to 1499, both masks, bf16 and fp16): the 8-wave dK/dV kernel
+    with K rows in LDS, with and without head parts, against the oracle."""
+    say(f"case bwd D=128 B={B} H={H} H_kv={H_kv} T={T} causal={causal} {dtype} seed={seed}")
+    x, do, do64 = case(B, H, H_kv, T, 128, dtype, seed)
+    got = run_bwd(x, do, causal, default_scale(128))
+    check_grads(x, do64, dtype, causal, default_scale(128), got, "d128 sweep")
+
+
 @pytest.mark.parametrize("H,H_kv", [(6, 2), (8, 1), (12, 1)])
 @pytest.mark.parametrize("head_split", [1, 2, 3, 0, 12])
 def test_bwd_head_split(H, H_kv, head_split, D):
