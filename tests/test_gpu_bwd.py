@@ -229,6 +229,7 @@ def test_bwd_d128_seeded_shapes(B, H, H_kv, T, causal, dtype, seed):
 
 @pytest.mark.parametrize("H,H_kv", [(6, 2), (8, 1), (12, 1)])
 @pytest.mark.parametrize("head_split", [1, 2, 3, 0, 12])
+@pytest.mark.parametrize("D", [64, 128])
 def test_bwd_head_split(H, H_kv, head_split, D):
     """The dK/dV kernel's query heads split into parts (fp32 sums added by the
     reduce kernel in part order): every split count matches the oracle and is
