@@ -227,7 +227,6 @@ __global__ __launch_bounds__(KL ? 2 * kThreads : kThreads) void fa_bwd_dkdv_kern
     constexpr int NSUB = BQ / 32;           // 32-row blocks per tile
     constexpr int KS = D / 16;              // k-steps over the head dim
     constexpr int ND = (D + 31) / 32;       // 32-row blocks of dK^T / dV^T
-    constexpr int NV = D >= 32 ? D / 32 : 1;
     constexpr int NI = (L::NLOAD + NW - 1) / NW;
 
     __shared__ __attribute__((aligned(1024))) unsigned char q_lds0[L::TILEB];
@@ -283,7 +282,7 @@ __global__ __launch_bounds__(KL ? 2 * kThreads : kThreads) void fa_bwd_dkdv_kern
     // transposing read of block n is tbase ^ 64 n (^ T8 for its +8-row half):
     // the chunk index of a row is XOR-permuted and the row base shares no bit
     // with it. The XOR is issued at each use (lane_xor) instead of holding
-    // 2 KS + 2 NV offsets in registers for the whole loop.
+    // 2 KS + 2 ND offsets in registers for the whole loop.
     const int rbase = col * L::ROWB + 16 * (half ^ L::dswz(col));
     // Transposing reads (A operand dO^T / Q^T): rows r0 and r0 + 8 of each
     // 16-row step, dims 32 n + dl .. + 3.

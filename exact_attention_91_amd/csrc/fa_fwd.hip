@@ -92,6 +92,7 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 namespace {
 
 constexpr int kBQ = 128;        // query rows per work-group (32 per wave)
+constexpr int kCUs = 256;       // MI355X compute units
 // Starting value of the running max: below every finite fp32 score, so only
 // rows with no visible key (all scores -inf) keep it. exp2(kMaxFloor - m) is 0
 // for any finite m above it, and exp2(-inf - kMaxFloor) is 0 for masked keys,
@@ -133,6 +134,12 @@ struct FwdParams {
     // (head h = g * group + hh), R = group * Tq of them per (batch, kv head);
     // nq counts 128-row tiles of those packed rows.
     int Tq, R;
+    // Work-group order: the first `snake` rounds of kCUs work-groups are
+    // resident from the start, the i-th work-group of every round on the same
+    // CU; odd rounds take their units in reverse, so the CU that starts the
+    // heaviest query tile of round 0 gets the lightest one of round 1
+    // (0: heaviest first throughout).
+    int snake;
 };
 
 template <bool B>
@@ -145,8 +152,14 @@ struct BoolC {
 struct Unit {
     int b, h, g, q0, s;
 };
+__device__ __forceinline__ int snake_id(const FwdParams &p) {
+    const int id = blockIdx.x;
+    const int k = id / kCUs;
+    return k < p.snake && (k & 1) ? k * kCUs + kCUs - 1 - (id - k * kCUs) : id;
+}
+
 __device__ __forceinline__ Unit unit_of(const FwdParams &p) {
-    int id = blockIdx.x;
+    int id = snake_id(p);
     Unit u;
     u.s = 0;
     if (p.nsplit > 1) {
@@ -216,8 +229,9 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         // (both heads read the same kv head: the group size is even)
         const int npair = p.H / 2;
         const int nbp = p.B * npair;
-        const int t = blockIdx.x / nbp;
-        const int bp = blockIdx.x - t * nbp;
+        const int id = snake_id(p);
+        const int t = id / nbp;
+        const int bp = id - t * nbp;
         u.b = bp / npair;
         u.h = 2 * (bp - u.b * npair) + grp;
         u.g = u.h / p.group;
@@ -990,7 +1004,7 @@ __global__ __launch_bounds__(256) void fa_global_bits_kernel(const int *idx, int
 // ---------------------------------------------------------------------------
 constexpr long long kMaxOffset = 1LL << 62;
 constexpr int kMaxT = (1 << 30);    // longest sequence accepted (32-bit row arithmetic)
-constexpr long long kNumCU = 256;   // MI355X compute units
+constexpr long long kNumCU = kCUs;
 constexpr long long kMaxGrid = (1LL << 24) - 1;
 
 // Largest element offset + 1 of a [B, T, heads, D] view; -1 on overflow.
@@ -1006,33 +1020,60 @@ long long extent(const long long s[3], int B, int T, int heads, int D) {
 
 bool aligned(const void *ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+// Work-groups of kernel K resident on one CU when it runs alone (asked of the
+// runtime once per kernel; 0 if the query fails).
+template <void (*K)(FwdParams)>
+int resident_per_cu(int threads) {
+    static const int n = [threads] {
+        int b = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, (const void *)K, threads, 0) ==
+                       hipSuccess
+                   ? b
+                   : 0;
+    }();
+    return n;
+}
+
+// Launch K with the causal work-group order balanced per CU when the whole
+// grid is resident at once (work-group i + r kCUs then shares CU i with
+// i, one per round): its full rounds are snaked. A larger grid keeps the
+// heaviest-first order, which the hardware's dynamic dispatch balances;
+// uniform (non-causal) work has nothing to balance.
+template <void (*K)(FwdParams)>
+hipError_t launch_fwd(dim3 grid, dim3 block, hipStream_t stream, FwdParams p, bool causal) {
+    if (causal) {
+        const long long resident = (long long)kCUs * resident_per_cu<K>((int)block.x);
+        p.snake = (long long)grid.x <= resident ? (int)(grid.x / kCUs) : 0;
+    }
+    return launch_kernel(K, grid, block, stream, p);
+}
+
 template <int D, bool CAUSAL, bool SPLIT, bool WINDOW>
 hipError_t launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) {
     constexpr bool CAN_G2 = D >= 64 && !SPLIT && !WINDOW;
     constexpr bool CAN_HP = !SPLIT && !WINDOW;
     const dim3 b4(kThreads), b8(2 * kThreads);
     if (CAN_HP && p.hpair && dtype == FA_DTYPE_BF16)
-        return launch_kernel(
-            (fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, b8,
-            stream, p);
+        return launch_fwd<fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>>(
+            grid, b8, stream, p, CAUSAL);
     else if (CAN_HP && p.hpair && dtype == FA_DTYPE_F16)
-        return launch_kernel(
-            (fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>), grid, b8,
-            stream, p);
+        return launch_fwd<fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false, CAN_HP>>(
+            grid, b8, stream, p, CAUSAL);
     else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_BF16)
-        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>), grid,
-                             b8, stream, p);
+        return launch_fwd<fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>>(
+            grid, b8, stream, p, CAUSAL);
     else if (CAN_G2 && p.groups == 2 && dtype == FA_DTYPE_F16)
-        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>),
-                             grid, b8, stream, p);
+        return launch_fwd<fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, CAN_G2>>(
+            grid, b8, stream, p, CAUSAL);
     else if (dtype == FA_DTYPE_BF16)
-        return launch_kernel((fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>), grid,
-                             b4, stream, p);
+        return launch_fwd<fa_fwd_half_kernel<__bf16, D, CAUSAL, SPLIT, WINDOW, false>>(
+            grid, b4, stream, p, CAUSAL);
     else if (dtype == FA_DTYPE_F16)
-        return launch_kernel((fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>),
-                             grid, b4, stream, p);
+        return launch_fwd<fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>>(
+            grid, b4, stream, p, CAUSAL);
     else if (!SPLIT && !WINDOW)
-        return launch_kernel((fa_fwd_f32_kernel<D, CAUSAL>), grid, b4, stream, p);
+        return launch_fwd<fa_fwd_f32_kernel<D, CAUSAL>>(
+            grid, b4, stream, p, CAUSAL);
     return hipErrorInvalidValue;   // callers validate dtype first; not reached
 }
 
@@ -1133,6 +1174,7 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
     p.hpair = 0;
     p.Tq = T;
     p.R = 0;
+    p.snake = 0;
     return FA_OK;
 }
 

@@ -202,3 +202,38 @@ def test_one_group_ragged(dtype, D, causal, T):
     scale = default_scale(D)
     o, lse = run_gpu(x, causal, scale)
     check_full(x, dtype, causal, scale, o, lse, "one group")
+
+
+def _fwd_into_nan(q, k, v, causal, scale):
+    """fa_fwd through the C ABI into outputs filled with NaN first, so a query
+    tile that no work-group visits shows up in the comparison."""
+    from exact_attention_91_amd import fa
+    B, T, H, D = q.shape
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, T), float("nan"), dtype=torch.float32, device=q.device)
+    rc = fa._lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), B, H, k.shape[2], T, D, int(causal), float(scale),
+                          fa._dtype_code(q), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, fa.status_str(rc)
+    torch.cuda.synchronize()
+    return o.to(torch.float64).cpu().numpy(), lse.to(torch.float64).cpu().numpy()
+
+
+# Causal grids that are resident on the chip all at once, where the work-group
+# order alternates direction per round of 256 (one work-group per CU per
+# round): 550 one-group work-groups at D = 64, 512 head-pair work-groups
+# (8 query heads per 2 kv heads), 512 one-group work-groups at D = 128 (fp16)
+# and 512 fp32 work-groups. Outputs start as NaN, so a unit the permuted order
+# skipped or visited twice in place of another fails.
+@pytest.mark.parametrize("dtype,B,H,H_kv,T,D", [("bf16", 11, 5, 5, 1200, 64),
+                                                ("bf16", 16, 8, 2, 1024, 64),
+                                                ("f16", 64, 1, 1, 1024, 128),
+                                                ("f32", 8, 8, 8, 1000, 32)])
+def test_resident_grid_order(dtype, B, H, H_kv, T, D):
+    seed = 9900 + B + H + T + D
+    say(f"case resident order dtype={dtype} B={B} H={H} H_kv={H_kv} T={T} D={D} seed={seed}")
+    x = generate(B, H, H_kv, T, D, dtype, seed)
+    scale = default_scale(D)
+    q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+    o, lse = _fwd_into_nan(q, k, v, True, scale)
+    check_full(x, dtype, True, scale, o, lse, "resident order")

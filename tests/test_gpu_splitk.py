@@ -244,3 +244,20 @@ def test_workload_long_b1_sampled_rows(nsplit):
                        fixed=(0, 1, 63, 64, 127, 128, 1023, 1024, 4095, 4096, 8190, 8191))
     check_rows(x, w.dtype, True, w.scale, o, lse, rows, f"{w.name} nsplit={nsplit}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("B,H,T,D,nsplit", [(2, 4, 2000, 64, 4), (1, 1, 8192, 128, 8)])
+def test_splitk_resident_grid_order(B, H, T, D, nsplit):
+    """Key-split grids of 512 work-groups, all resident at once, whose order
+    alternates direction per round of 256: with the workspace filled with NaN
+    first, a (query tile, part) that no work-group visits would reach the
+    output. Compared in full."""
+    say(f"case splitk resident order B={B} H={H} T={T} D={D} nsplit={nsplit}")
+    x = generate(B, H, H, T, D, "bf16", 7600 + T + D)
+    from exact_attention_91_amd import fa
+    need = fa.splitk_workspace_bytes(B, H, T, D, nsplit)
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32,
+                    device="cuda").view(torch.uint8)
+    scale = default_scale(D)
+    o, lse = run_splitk(x, True, scale, nsplit, workspace=ws)
+    check_full(x, "bf16", True, scale, o, lse, f"resident order nsplit={nsplit}")
