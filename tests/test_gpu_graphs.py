@@ -91,3 +91,41 @@ def test_bwd_and_splitk_and_window_graph_replays():
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outs, eager)):
             assert torch.equal(a, b), f"replay {rep} output {i}"
+
+
+_FIRST_CALL_CAPTURED = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from exact_attention_91_amd import fa
+from exact_attention_91_amd.inputs import generate
+x = generate(4, 8, 8, 1024, 64, "bf16", 12077)
+q, k, v = x.q.cuda(), x.k.cuda(), x.v.cuda()
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    o, lse = fa.fwd(q, k, v, causal=True, scale=0.125)   # the library's first call
+torch.cuda.synchronize()
+for rep in range(3):
+    g.replay()
+    torch.cuda.synchronize()
+    eo, el = fa.fwd(q, k, v, causal=True, scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o, eo) and torch.equal(lse, el), rep
+print("first call captured: ok", flush=True)
+"""
+
+
+def test_fwd_first_call_under_capture():
+    """A process whose first library call is made under graph capture (a
+    causal grid: the launch then also asks the runtime, once per kernel, how
+    many of its work-groups a CU holds): the capture succeeds and its replays
+    equal eager calls. Runs in a child process, so no earlier call has done
+    that query already."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED, root], capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "first call captured: ok" in r.stdout
