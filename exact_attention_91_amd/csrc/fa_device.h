@@ -137,8 +137,9 @@ constexpr int kCachePolicyNT = 2;              // buffer instruction cache polic
 // Issue this wave's share (of NW waves) of the global->LDS copies of two
 // ROWS-row tiles (64 unless stated), e.g. a K tile and a V tile (buffer loads straight into LDS;
 // rows past T read as zeros): loads wave, wave + NW, ... koff/voff: per-lane
-// byte offsets of the global chunk each lane fetches for its LDS slot.
-template <int D, int NW = 4, int ROWS = 64>
+// byte offsets of the global chunk each lane fetches for its LDS slot. AUX:
+// the loads' cache policy (0, or kCachePolicyNT for tiles read only once).
+template <int D, int NW = 4, int ROWS = 64, int AUX = 0>
 __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const unsigned short *vbase,
                                            long long ks1, long long vs1, int T, int key0,
                                            int wave, const int *koff, const int *voff,
@@ -159,9 +160,9 @@ __device__ __forceinline__ void stage_tile(const unsigned short *kbase, const un
         const int idx = wave + NW * i;
         if (L::NLOAD % NW == 0 || idx < L::NLOAD) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kdst + idx * 1024), 16,
-                                                     koff[i], 0, 0, 0);
+                                                     koff[i], 0, 0, AUX);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + idx * 1024), 16,
-                                                     voff[i], 0, 0, 0);
+                                                     voff[i], 0, 0, AUX);
         }
     }
 }

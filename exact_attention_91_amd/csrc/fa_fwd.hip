@@ -293,6 +293,10 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         }
     }
 
+    // Decode reads every K/V tile once (no other work-group shares it): its
+    // copies carry the non-temporal policy. Elsewhere the query tiles of a
+    // head re-read each tile and keep the default policy.
+    constexpr int KV_POL = DECODE ? kCachePolicyNT : 0;
     const int kend = CAUSAL && !DECODE ? min(T, u.q0 + kBQ) : T;
     const int nkt = (kend + BK - 1) / BK;
     // Key tiles of this work-group: all of them, or split u.s's share; with G2,
@@ -484,7 +488,8 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         lds_poison2(jn < jend, kn, vn, L::TILEB, G2 ? (tid & (kThreads - 1)) : tid,
                     HP ? 2 * kThreads : kThreads);
         if (jn < jend)
-            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jn * BK, swave, koff, voff, kn, vn);
+            stage_tile<D, NW, 64, KV_POL>(kbase, vbase, ks1, vs1, T, jn * BK,
+                                           swave, koff, voff, kn, vn);
         const int key0 = j * BK;
         // (decode: every row sees keys up to at least T - Tq, and some row up to T - 1)
         bool active = wave_live && (!CAUSAL || DECODE || key0 <= wq0 + 31) && (!G2 || j < jend);
@@ -538,7 +543,8 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         unsigned long long gj = tile_bits(j);
         if (QO) qo_stage();
         if (j < jend)
-            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, j * BK, swave, koff, voff, k_lds0, v_lds0);
+            stage_tile<D, NW, 64, KV_POL>(kbase, vbase, ks1, vs1, T, j * BK,
+                                           swave, koff, voff, k_lds0, v_lds0);
         if (QO) qo_read();
         while (j < jend) {
             const int jn = next_tile(j);
@@ -558,7 +564,8 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
         // idle when nkt is odd (no staging, no math).
         if (QO) qo_stage();
         if (jbeg < jend)
-            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jbeg * BK, swave, koff, voff, k_lds0, v_lds0);
+            stage_tile<D, NW, 64, KV_POL>(kbase, vbase, ks1, vs1, T, jbeg * BK,
+                                           swave, koff, voff, k_lds0, v_lds0);
         if (QO) qo_read();
         for (int i = 0; i < ghalf; i += 2) {
             step(jbeg + i, 0ull, jbeg + i + 1, k_lds0, v_lds0, k_lds1, v_lds1);
@@ -568,7 +575,8 @@ __global__ __launch_bounds__(G2 || HP ? 2 * kThreads : kThreads) void fa_fwd_hal
     } else {
         if (QO) qo_stage();
         if (jbeg < jend)
-            stage_tile<D, NW>(kbase, vbase, ks1, vs1, T, jbeg * BK, swave, koff, voff, k_lds0, v_lds0);
+            stage_tile<D, NW, 64, KV_POL>(kbase, vbase, ks1, vs1, T, jbeg * BK,
+                                           swave, koff, voff, k_lds0, v_lds0);
         if (QO) qo_read();
         last0 = ((jend - 1 - jbeg) & 1) == 0;
         for (int j = jbeg; j < jend; j += 2) {
