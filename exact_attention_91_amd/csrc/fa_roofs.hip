@@ -79,47 +79,58 @@ __global__ __launch_bounds__(512) void roof_overlap_kernel(int n_mfma, int n_val
     }
 }
 
+// Work-group g of G streams its own contiguous share [n16 g / G, n16 (g+1) / G)
+// of the buffer, 256 threads reading consecutive 16-byte vectors. On this
+// chip per-work-group streams reach a higher rate than one grid-wide stride
+// over the whole buffer (reads about 7.0 against 5.4 TB/s).
+__device__ __forceinline__ void my_chunk(long long n16, long long &lo, long long &hi) {
+    lo = n16 * blockIdx.x / gridDim.x;
+    hi = n16 * (blockIdx.x + 1) / gridDim.x;
+}
+
 // Four 16-byte vectors in flight per thread: all loads of a step are issued
 // before its stores. n16: 16-byte vectors in the buffer.
 __global__ __launch_bounds__(256) void roof_copy_kernel(const u32x4_t *src, u32x4_t *dst,
                                                         long long n16) {
-    const long long nthreads = (long long)gridDim.x * blockDim.x;
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    long long i = t;
-    for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
+    long long lo, hi;
+    my_chunk(n16, lo, hi);
+    long long i = lo + threadIdx.x;
+    for (; i + 3 * 256 < hi; i += 4 * 256) {
         const u32x4_t a = __builtin_nontemporal_load(src + i);
-        const u32x4_t b = __builtin_nontemporal_load(src + i + nthreads);
-        const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * nthreads);
-        const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * nthreads);
+        const u32x4_t b = __builtin_nontemporal_load(src + i + 256);
+        const u32x4_t c = __builtin_nontemporal_load(src + i + 2 * 256);
+        const u32x4_t d = __builtin_nontemporal_load(src + i + 3 * 256);
         __builtin_nontemporal_store(a, dst + i);
-        __builtin_nontemporal_store(b, dst + i + nthreads);
-        __builtin_nontemporal_store(c, dst + i + 2 * nthreads);
-        __builtin_nontemporal_store(d, dst + i + 3 * nthreads);
+        __builtin_nontemporal_store(b, dst + i + 256);
+        __builtin_nontemporal_store(c, dst + i + 2 * 256);
+        __builtin_nontemporal_store(d, dst + i + 3 * 256);
     }
-    for (; i < n16; i += nthreads) dst[i] = src[i];
+    for (; i < hi; i += 256) dst[i] = src[i];
 }
 
 // Reads n16 16-byte vectors, eight in flight per thread, and folds them into
 // one word per thread (stored only if it matches an impossible pattern).
 __global__ __launch_bounds__(256) void roof_read_kernel(const u32x4_t *src, long long n16,
                                                         float *sink) {
-    const long long nthreads = (long long)gridDim.x * blockDim.x;
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    long long lo, hi;
+    my_chunk(n16, lo, hi);
     u32x4_t acc = {0u, 0u, 0u, 0u};
-    long long i = t;
-    for (; i + 7 * nthreads < n16; i += 8 * nthreads) {
+    long long i = lo + threadIdx.x;
+    for (; i + 7 * 256 < hi; i += 8 * 256) {
         u32x4_t x[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(src + i + r * nthreads);
+        for (int r = 0; r < 8; ++r) x[r] = __builtin_nontemporal_load(src + i + r * 256);
 #pragma unroll
         for (int r = 0; r < 8; ++r) acc ^= x[r];
     }
-    for (; i < n16; i += nthreads) acc ^= src[i];
+    for (; i < hi; i += 256) acc ^= src[i];
     const unsigned w = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-    if (w == 0x9e3779b9u && t == 0) sink[blockIdx.x] = 1.f;
+    if (w == 0x9e3779b9u && threadIdx.x == 0) sink[blockIdx.x] = 1.f;
 }
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : 9; }
+
+constexpr unsigned kStreamBlocks = 256 * 32;   // work-groups of the copy and read roofs
 
 }  // namespace
 
@@ -159,15 +170,17 @@ extern "C" int fa_roof_read(const void *src, long long bytes, float *sink, void 
     if (bytes < 16) return 2;
     if (!src || !sink) return 1;
     if (bytes % 16 != 0 || (uintptr_t)src % 16 != 0) return 7;
-    return status(launch_kernel(roof_read_kernel, dim3(256 * 8), dim3(256), (hipStream_t)stream,
-                                (const u32x4_t *)src, bytes / 16, sink));
+    // 32 work-groups of 256 threads per compute unit, each streaming its own chunk
+    return status(launch_kernel(roof_read_kernel, dim3(kStreamBlocks), dim3(256),
+                                (hipStream_t)stream, (const u32x4_t *)src, bytes / 16, sink));
 }
 
 extern "C" int fa_roof_copy(const void *src, void *dst, long long bytes, void *stream) {
     if (bytes < 16) return 2;
     if (!src || !dst) return 1;
     if (bytes % 16 != 0 || (uintptr_t)src % 16 != 0 || (uintptr_t)dst % 16 != 0) return 7;
-    // 8 work-groups of 256 threads per compute unit, each thread striding
-    return status(launch_kernel(roof_copy_kernel, dim3(256 * 8), dim3(256), (hipStream_t)stream,
-                                (const u32x4_t *)src, (u32x4_t *)dst, bytes / 16));
+    // 32 work-groups of 256 threads per compute unit, each copying its own chunk
+    return status(launch_kernel(roof_copy_kernel, dim3(kStreamBlocks), dim3(256),
+                                (hipStream_t)stream, (const u32x4_t *)src, (u32x4_t *)dst,
+                                bytes / 16));
 }

@@ -114,7 +114,7 @@ def measure(copy_mib: int = 1024):
     out["copy_gbps"] = 2 * nbytes / (ms * 1e-3) / 1e9   # read + write
     out["copy_ms"] = ms
     del dst
-    big = torch.zeros(2048, dtype=torch.float32, device="cuda")
+    big = torch.zeros(8192, dtype=torch.float32, device="cuda")   # one per work-group
     ms = _time(lambda: _check(lib.fa_roof_read(src.data_ptr(), nbytes, big.data_ptr(), sp),
                               "fa_roof_read"))
     out["read_gbps"] = nbytes / (ms * 1e-3) / 1e9

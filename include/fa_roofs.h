@@ -23,9 +23,11 @@
  *                  4-7 (sharing those SIMDs) run n_valu * 16 instructions of
  *                  kind `op` when mask bit 1 is set. Comparing the time with
  *                  both bits against each alone shows the overlap.
- *   fa_roof_copy:  reads and writes `bytes` bytes (16-byte vectors).
+ *   fa_roof_copy:  reads and writes `bytes` bytes (16-byte vectors), each of
+ *                  8192 work-groups streaming its own contiguous chunk.
  *   fa_roof_read:  reads `bytes` bytes (16-byte vectors, eight in flight per
- *                  thread); sink needs 2048 elements (one per work-group).
+ *                  thread, 8192 work-groups each streaming its own contiguous
+ *                  chunk); sink needs 8192 elements (one per work-group).
  * sink: device float array of at least grid_blocks elements (written, holds
  * nothing useful; it keeps the arithmetic from being optimised away).
  * Returns 0 on success, 9 (FA_ERR_LAUNCH) if the runtime rejects a launch,
