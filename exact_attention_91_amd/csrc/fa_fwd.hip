@@ -940,7 +940,8 @@ __global__ __launch_bounds__(256) void fa_lse_combine_kernel(CombineParams p) {
     if (row >= rows) return;
     // One pass, merging part by part with a running max (the online-softmax
     // update): every load is independent of the arithmetic, so the loads of
-    // an unrolled group are all in flight together.
+    // an unrolled group are all in flight together. Each partial is read once
+    // (non-temporal loads).
     const float *lp = p.lpart + row;
     const float *op = p.opart + row * D + d;
     float m = -INFINITY, l = 0.f;
@@ -962,12 +963,13 @@ __global__ __launch_bounds__(256) void fa_lse_combine_kernel(CombineParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             ls[i] = lp[(s + i) * rows];
-            os[i] = *(const f32x4_t *)(op + (s + i) * rows * D);
+            os[i] = __builtin_nontemporal_load((const f32x4_t *)(op + (s + i) * rows * D));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) merge(ls[i], os[i]);
     }
-    for (; s < p.n; ++s) merge(lp[s * rows], *(const f32x4_t *)(op + s * rows * D));
+    for (; s < p.n; ++s)
+        merge(lp[s * rows], __builtin_nontemporal_load((const f32x4_t *)(op + s * rows * D)));
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float L = l > 0.f ? m + logf(l) : -INFINITY;
     const int t = (int)(row % p.T);
