@@ -53,7 +53,9 @@
 //  * Causal: key tiles past the query tile are never loaded; a wave skips the
 //    math of tiles wholly in its future; only tiles that touch the diagonal or
 //    the ragged end T are masked element-wise. Query tiles are issued
-//    heaviest-first.
+//    heaviest-first; when the whole grid is resident at once, each round of
+//    256 work-groups (one per CU) alternates direction, so a CU's heavy tile
+//    of one round is paired with a light one of the next.
 //  * Small grids (few query tiles per CU, or long rows with every work-group
 //    resident): the G2 instantiation runs 8 waves per work-group in two groups
 //    of 4 that take the first and second half of the query tile's key tiles,
@@ -71,7 +73,9 @@
 //    of "Softmax 的在線計算" applied across ranges); WINDOW visits only the key
 //    tiles that meet the query tile's band or hold a global token (the
 //    sparse-attention variants of the same article) and masks by band, token
-//    bitmap and causality.
+//    bitmap and causality; DECODE (a SPLIT form) packs the few query rows of
+//    the heads that share a kv head into one row tile and copies its K/V tiles,
+//    which no other work-group reads, with the non-temporal cache policy.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -1045,8 +1049,8 @@ int resident_per_cu(int threads) {
 }
 
 // Launch K with the causal work-group order balanced per CU when the whole
-// grid is resident at once (work-group i + r kCUs then shares CU i with
-// i, one per round): its full rounds are snaked. A larger grid keeps the
+// grid is resident at once (work-groups i, i + kCUs, i + 2 kCUs, ... then all
+// run on one CU): its full rounds are snaked. A larger grid keeps the
 // heaviest-first order, which the hardware's dynamic dispatch balances;
 // uniform (non-causal) work has nothing to balance.
 template <void (*K)(FwdParams)>
@@ -1082,8 +1086,7 @@ hipError_t launch(const FwdParams &p, int dtype, dim3 grid, hipStream_t stream) 
         return launch_fwd<fa_fwd_half_kernel<_Float16, D, CAUSAL, SPLIT, WINDOW, false>>(
             grid, b4, stream, p, CAUSAL);
     else if (!SPLIT && !WINDOW)
-        return launch_fwd<fa_fwd_f32_kernel<D, CAUSAL>>(
-            grid, b4, stream, p, CAUSAL);
+        return launch_fwd<fa_fwd_f32_kernel<D, CAUSAL>>(grid, b4, stream, p, CAUSAL);
     return hipErrorInvalidValue;   // callers validate dtype first; not reached
 }
 
